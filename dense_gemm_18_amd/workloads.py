@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the fp16 NT GEMM workloads.
+
+This module only draws numbers: it holds none of the GEMM's arithmetic and
+is shared, unchanged, by the oracle-side tests and the GPU-side tests and
+benchmark.  Every array is IEEE binary16 (numpy ``float16``) in the layouts
+the GEMM takes: A row-major M x K, B row-major N x K.
+
+Shapes follow the pages' workloads: the 128 x 128 x 64 single output tile
+and the multi-tile / K-loop steps of page "构建 Tiled GEMM" ("Building a
+Tiled GEMM", mlc.ai, sections "第 1 步" .. "第 3 步"), and the 8192^3 fp16
+problem that page "如何用 Croqtile 一步步优化矩阵乘法内核" measures
+throughout (header and section "性能一览").  The ragged 3000 x 5000 x 2050
+shape and the skinny 64 x 16384 x 8192 linear-layer shape extend those
+with tails and an HBM-bound case.  The pages fix no value distribution
+(page 2's harness draws ``torch.randn``); the distributions below are stated
+per workload.
+
+Draws use numpy's PCG64 (``default_rng(seed)``) in float64 and are rounded to
+fp16 by numpy's ``astype`` (round to nearest, ties to even).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    a_dist: str          # "uniform" | "normal_scaled" | "normal_0.02"
+    b_dist: str
+    seeds: tuple         # (seed_A, seed_B) for the random variant
+    int_seeds: tuple     # (seed_A, seed_B) for the integer {-2..2} variant
+    sample_seed: int | None = None   # seed of the sampled-entry check, if any
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tile_128x128x64", 128, 128, 64, "uniform", "uniform",
+                 (1001, 1002), (1011, 1012)),
+        Workload("square_1024", 1024, 1024, 1024, "uniform", "uniform",
+                 (2001, 2002), (2011, 2012)),
+        Workload("ragged_3000x5000x2050", 3000, 5000, 2050, "normal_scaled", "normal_scaled",
+                 (3001, 3002), (3011, 3012)),
+        Workload("skinny_64x16384x8192", 64, 16384, 8192, "uniform", "normal_0.02",
+                 (4001, 4002), (4011, 4012)),
+        Workload("square_8192", 8192, 8192, 8192, "uniform", "uniform",
+                 (5001, 5002), (5011, 5012), sample_seed=5003),
+    )
+}
+
+HEADLINE = "square_8192"
+
+
+def _draw(rng: np.random.Generator, dist: str, rows: int, K: int) -> np.ndarray:
+    shape = (rows, K)
+    if dist == "uniform":
+        x = rng.uniform(-1.0, 1.0, size=shape)
+    elif dist == "normal_scaled":
+        x = rng.standard_normal(size=shape) / np.sqrt(K)
+    elif dist == "normal_0.02":
+        x = 0.02 * rng.standard_normal(size=shape)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return x.astype(np.float16)
+
+
+def random_inputs(w: Workload, M: int | None = None, N: int | None = None,
+                  K: int | None = None):
+    """The random variant of workload ``w`` (optionally at another shape)."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    A = _draw(np.random.default_rng(w.seeds[0]), w.a_dist, M, K)
+    B = _draw(np.random.default_rng(w.seeds[1]), w.b_dist, N, K)
+    return A, B
+
+
+def integer_inputs(w: Workload, M: int | None = None, N: int | None = None,
+                   K: int | None = None):
+    """Integer-valued entries, uniform over {-2, -1, 0, 1, 2}."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    A = np.random.default_rng(w.int_seeds[0]).integers(-2, 3, size=(M, K), dtype=np.int8)
+    B = np.random.default_rng(w.int_seeds[1]).integers(-2, 3, size=(N, K), dtype=np.int8)
+    return A.astype(np.float16), B.astype(np.float16)
+
+
+def uniform_inputs(seed: int, M: int, N: int, K: int, lo: float = -1.0, hi: float = 1.0):
+    """Free-shape uniform[lo, hi] inputs (edge-case sweeps)."""
+    rng = np.random.default_rng(seed)
+    A = rng.uniform(lo, hi, size=(M, K)).astype(np.float16)
+    B = rng.uniform(lo, hi, size=(N, K)).astype(np.float16)
+    return A, B
+
+
+def integer_free(seed: int, M: int, N: int, K: int, lo: int = -2, hi: int = 2):
+    """Free-shape integer inputs uniform over {lo..hi}."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(lo, hi + 1, size=(M, K), dtype=np.int16).astype(np.float16)
+    B = rng.integers(lo, hi + 1, size=(N, K), dtype=np.int16).astype(np.float16)
+    return A, B
+
+
+def random_bits(seed: int, shape, finite_max: float | None = None) -> np.ndarray:
+    """Uniformly random fp16 bit patterns over all finite values (subnormals,
+    zeros and +-65504 included); optionally restricted to |x| <= finite_max."""
+    rng = np.random.default_rng(seed)
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    filled = 0
+    while filled < out.size:
+        cand = rng.integers(0, 65536, size=2 * (out.size - filled) + 16, dtype=np.uint32)
+        cand = cand.astype(np.uint16)
+        v = cand.view(np.float16)
+        ok = np.isfinite(v)
+        if finite_max is not None:
+            ok &= np.abs(v.astype(np.float64)) <= finite_max
+        cand = cand[ok][: out.size - filled]
+        out[filled: filled + cand.size] = cand
+        filled += cand.size
+    return out.reshape(shape).view(np.float16)
+
+
+def sample_indices(w: Workload, count: int = 4096):
+    """``count`` distinct (row, col) positions of D drawn without replacement
+    from the workload's sample seed."""
+    seed = w.sample_seed if w.sample_seed is not None else w.seeds[0] + 2
+    flat = np.random.default_rng(seed).choice(w.M * w.N, size=count, replace=False)
+    return (flat // w.N).astype(np.int64), (flat % w.N).astype(np.int64)
+
+
+def edge_lines(extent: int, tile: int) -> np.ndarray:
+    """Rows (or columns) of D at tile edges: the first, second, last and
+    first-of-next of the first two tiles and of the last full tile, the last
+    two of the extent, and the fixed probes 63/64/127/128/255/256."""
+    full = (extent // tile) * tile
+    cand = {0, 1, tile - 1, tile, 2 * tile - 1, 2 * tile, full - 1, full,
+            extent - 2, extent - 1, 63, 64, 127, 128, 255, 256}
+    return np.array(sorted(c for c in cand if 0 <= c < extent), dtype=np.int64)

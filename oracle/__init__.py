@@ -1,0 +1,130 @@
+"""CPU oracle for the dense fp16 NT GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package.  The product path (the HIP
+library and its Python binding) never imports, calls or loads it, and the
+oracle shares no code with that path.
+
+The arithmetic lives in ``gemm_oracle.c`` (plain C, built with gcc, fp64):
+``D[m,n] = sum_k A[m,k] * B[n,k]`` with A stored M x K and B stored N x K,
+as defined on page "构建 Tiled GEMM" ("Building a Tiled GEMM", mlc.ai
+modern-gpu-programming-for-mlsys, chapter gemm_basics), section "GEMM".
+Each fp16 input is widened to fp64 exactly, the sum runs over ascending k in
+fp64 from +0.0 and is rounded once to fp16 (round to nearest, ties to even).
+This module only marshals numpy arrays of raw fp16 bit patterns (uint16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "gemm_oracle.c"
+_LIB_PATH = _HERE / "liboracle.so"
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra"]
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile ``gemm_oracle.c`` into ``liboracle.so`` with gcc."""
+    if force or not _LIB_PATH.exists():
+        tmp = _LIB_PATH.with_suffix(f".so.tmp{os.getpid()}")
+        subprocess.check_call(["gcc", *_CFLAGS, str(_SRC), "-o", str(tmp), "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
+        build(force=True)
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_f16_decode.argtypes = [p, p, i64]
+    lib.oracle_f16_decode.restype = None
+    lib.oracle_f16_encode.argtypes = [p, p, i64]
+    lib.oracle_f16_encode.restype = None
+    lib.oracle_gemm_nt_f16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_f16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_entries.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    """Return a C-contiguous uint16 view of fp16 data (float16 or uint16 in)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16)
+    if x.dtype != np.uint16:
+        raise TypeError(f"expected float16 or uint16 bit patterns, got {x.dtype}")
+    return x
+
+
+def _ptr(x: np.ndarray) -> int:
+    return x.ctypes.data
+
+
+def decode(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns -> exact fp64 values (binary16 definition)."""
+    b = _bits(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_f16_decode(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def encode(values: np.ndarray) -> np.ndarray:
+    """fp64 values -> fp16 bit patterns, round to nearest, ties to even."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_f16_encode(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def gemm_nt_f16(A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
+    """Full D = A * B^T as fp16 bit patterns (uint16, shape M x N)."""
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_f16(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(threads))
+    return d
+
+
+def gemm_nt_f16_entries(A: np.ndarray, B: np.ndarray, rows, cols,
+                        threads: int = 0) -> np.ndarray:
+    """Entries D[rows[i], cols[i]] as fp16 bit patterns (uint16, 1-D)."""
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    r = np.ascontiguousarray(rows, dtype=np.int64).ravel()
+    c = np.ascontiguousarray(cols, dtype=np.int64).ravel()
+    if r.shape != c.shape:
+        raise ValueError("rows and cols differ in length")
+    M, K = a.shape
+    N = b.shape[0]
+    if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+        raise IndexError("entry index outside D")
+    out = np.empty(r.shape, dtype=np.uint16)
+    _load().oracle_gemm_nt_f16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c),
+                                       r.size, _ptr(out), int(threads))
+    return out
+
+
+def threads_available() -> int:
+    """Host threads OpenMP would use by default (the CPU-baseline core count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1

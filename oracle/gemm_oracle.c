@@ -1,0 +1,182 @@
+/*
+ * gemm_oracle.c -- CPU oracle for the dense fp16 "NT" GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it: only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg use it.  It shares no code,
+ * header or table with the HIP library.
+ *
+ * What it computes (page "构建 Tiled GEMM" / "Building a Tiled GEMM",
+ * mlc.ai modern-gpu-programming-for-mlsys, chapter gemm_basics, section
+ * "GEMM"):
+ *
+ *     D[m,n] = sum_{k<K} A[m,k] * B[n,k]
+ *
+ * A is M x K, B is stored N x K (the linear-layer weight layout; the product
+ * equals A * B^T and B is never transposed), D is M x N.  All three are
+ * dense row-major IEEE binary16 arrays.  The same page stores A, B and D in
+ * fp16 and accumulates in a wider type; the oracle widens every fp16 input to
+ * fp64 exactly, sums in fp64 in ascending k starting from +0.0, and rounds the
+ * final sum once, directly from fp64 to fp16, round-to-nearest-ties-to-even.
+ * The same index formula (row * K + k for the operands, row * N + col for
+ * the output) is the one the naive kernel of page "如何用 Croqtile 一步步优化
+ * 矩阵乘法内核" (section "内核 0：朴素版", Kernel 0: naive) evaluates.
+ *
+ * Readings taken where the pages are silent:
+ *  - rounding of the final cast: IEEE round-to-nearest, ties-to-even;
+ *  - magnitudes >= 65520 round to +-inf; subnormal fp16 inputs are honoured;
+ *  - an exact-zero sum is +0 (the sum starts from +0.0);
+ *  - K = 0 gives D = +0 everywhere (the empty sum);
+ *  - NaN results are returned as the canonical quiet NaN 0x7E00.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
+ * the sum must be evaluated exactly in the written order).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- binary16 decode, from the IEEE 754 binary16 definition ------------
+ * Layout: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-24
+ *   exponent 1..30  : normal,    value = (1024 + fraction) * 2^(exponent-25)
+ *   exponent 31     : infinity (fraction 0) or NaN (fraction != 0)        */
+static double f16_decode(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* ---- fp64 -> binary16, round to nearest, ties to even ------------------
+ * Take |x| in binade [2^E, 2^(E+1)).  Normal fp16 numbers in that binade are
+ * integer multiples of the quantum 2^(E-10); below 2^-14 the quantum is fixed
+ * at 2^-24 (subnormals).  Scale |x| by the inverse quantum (a power of two,
+ * so exact), round the scaled value to an integer with ties to even, then
+ * re-assemble.  A carry to 2048 moves to the next binade; a binade above 15
+ * is infinity.                                                            */
+static uint16_t f16_encode_rne(double x)
+{
+    if (isnan(x))
+        return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a))
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    (void)frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1)     */
+    int E = e2 - 1;               /* a in [2^E, 2^(E+1))               */
+    if (E > 15)
+        return sign | 0x7c00;     /* >= 65536: beyond every rounding   */
+    if (E < -14)
+        E = -14;                  /* subnormal quantum 2^-24           */
+    double scaled = ldexp(a, 10 - E);   /* exact power-of-two scaling  */
+    double lo = floor(scaled);
+    double rem = scaled - lo;           /* exact: scaled < 2^11        */
+    long n = (long)lo;
+    if (rem > 0.5 || (rem == 0.5 && (n & 1)))
+        n += 1;
+    if (n == 2048) {              /* rounded up into the next binade   */
+        n = 1024;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    if (n < 1024)                 /* only possible when E == -14       */
+        return sign | (uint16_t)n;
+    return sign | (uint16_t)(((E + 15) << 10) | (n - 1024));
+}
+
+/* Decoded value of every binary16 pattern, filled once from f16_decode. */
+static double g_lut[65536];
+static int g_lut_ready = 0;
+
+static void lut_init(void)
+{
+    if (g_lut_ready)
+        return;
+    for (int h = 0; h < 65536; ++h)
+        g_lut[h] = f16_decode((uint16_t)h);
+    g_lut_ready = 1;
+}
+
+static int pick_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* One output entry: fp64 sum over ascending k, rounded once. */
+static uint16_t entry(const uint16_t *arow, const uint16_t *brow, int64_t K)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += g_lut[arow[k]] * g_lut[brow[k]];
+    return f16_encode_rne(acc);
+}
+
+/* ---- exported API ------------------------------------------------------ */
+
+void oracle_f16_decode(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f16_decode(in[i]);
+}
+
+void oracle_f16_encode(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f16_encode_rne(in[i]);
+}
+
+/* Full D = A * B^T.  Rows of D are spread over threads; every entry's sum is
+ * sequential.  Returns the number of threads used. */
+int oracle_gemm_nt_f16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                       int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    lut_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            D[m * N + n] = entry(A + m * K, B + n * K, K);
+    return nt;
+}
+
+/* Selected entries D[rows[i], cols[i]], i < count.  Indices must lie in
+ * [0, M) x [0, N); entries with an index outside get 0x7E00 (NaN) so that a
+ * caller's mistake cannot pass silently.  Returns the number of threads. */
+int oracle_gemm_nt_f16_entries(const uint16_t *A, const uint16_t *B,
+                               int64_t M, int64_t N, int64_t K,
+                               const int64_t *rows, const int64_t *cols,
+                               int64_t count, uint16_t *out, int nthreads)
+{
+    lut_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = rows[i], n = cols[i];
+        if (m < 0 || m >= M || n < 0 || n >= N)
+            out[i] = 0x7e00;
+        else
+            out[i] = entry(A + m * K, B + n * K, K);
+    }
+    return nt;
+}

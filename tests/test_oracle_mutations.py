@@ -1,0 +1,101 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies ``oracle/gemm_oracle.c`` to a temporary directory, plants one
+mistake by a textual edit (a dropped term, a wrong sign, a transposed index,
+a detour through fp32, flushed subnormals, ties rounded away, a wrong zero
+sign, saturation instead of infinity), compiles the copy with gcc, points the oracle wrapper at it and runs
+the pin battery.  At least one pin must fail for every planted mistake.  All
+of this runs on the CPU; the real oracle is not modified.
+"""
+from __future__ import annotations
+
+import ctypes
+import shutil
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = Path(oracle.__file__).resolve().parent / "gemm_oracle.c"
+
+MUTATIONS = {
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)"),
+    "wrong_sign": ("acc += g_lut[arow[k]] * g_lut[brow[k]];", "acc -= g_lut[arow[k]] * g_lut[brow[k]];"),
+    "transposed_output": ("D[m * N + n] = entry(", "D[n * M + m] = entry("),
+    "b_row_index": ("D[m * N + n] = entry(A + m * K, B + n * K, K);",
+                    "D[m * N + n] = entry(A + m * K, B + ((n + 1) % N) * K, K);"),
+    "round_via_fp32": ("return f16_encode_rne(acc);", "return f16_encode_rne((double)(float)acc);"),
+    "flush_subnormals": ("v = ldexp((double)frac, -24);", "v = 0.0 * frac;"),
+    "ties_away": ("if (rem > 0.5 || (rem == 0.5 && (n & 1)))", "if (rem >= 0.5)"),
+    "negative_zero_start": ("double acc = 0.0;", "double acc = -0.0;"),
+    "saturating_overflow": ("if (E > 15)\n        return sign | 0x7c00;\n    if (n < 1024)",
+                            "if (E > 15)\n        return sign | 0x7bff;\n    if (n < 1024)"),
+}
+
+
+def _battery():
+    """The pin checks, each as a zero-argument callable."""
+    return [
+        pins.test_p1_decode_exhaustive,
+        pins.test_p1_encode_roundtrip_exhaustive,
+        pins.test_p1_encode_midpoints_and_neighbours,
+        pins.test_p1_encode_overflow_and_random,
+        lambda: pins.test_p2a_brute_force_any_finite(K=7, seed=11),
+        lambda: pins.test_p2a_brute_force_any_finite(K=17, seed=12),
+        lambda: pins.test_p2b_exact_rational(K=33, seed=21),
+        pins.test_p3_identity_and_permutation,
+        lambda: pins.test_p4_integer_exact((33, 65, 129)),
+        lambda: pins.test_p5_all_ones(64),
+        pins.test_p5_rank_one,
+        pins.test_p6_transpose_symmetry,
+        pins.test_p7_ties_and_double_rounding,
+        lambda: pins.test_p8_subnormal_inputs(64),
+        pins.test_p8_overflow_and_signed_zero_and_empty,
+    ]
+
+
+def _build_mutant(tmp: Path, old: str, new: str) -> Path:
+    text = SRC.read_text()
+    assert text.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    src = tmp / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+                           "-std=c11", str(src), "-o", str(lib), "-lm"])
+    return lib
+
+
+def _wrap(path: Path):
+    lib = ctypes.CDLL(str(path))
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_f16_decode.argtypes = [p, p, i64]
+    lib.oracle_f16_encode.argtypes = [p, p, i64]
+    lib.oracle_gemm_nt_f16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_f16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_entries.restype = ctypes.c_int
+    return lib
+
+
+def test_unmutated_battery_passes():
+    for check in _battery():
+        check()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    lib = _wrap(_build_mutant(tmp_path, old, new))
+    oracle._load()                      # make sure the real library is not loaded later
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = 0
+    for check in _battery():
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin catches the planted mistake {name!r}"

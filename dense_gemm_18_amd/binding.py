@@ -1,0 +1,119 @@
+"""Python binding of the C ABI in ``include/gemm_nt_f16.h``.
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels of
+``libgemm18.so``.  PyTorch supplies device memory and the current stream.
+A missing library raises; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_LIB_PATH = Path(__file__).resolve().parent / "libgemm18.so"
+_lib = None
+
+GEMM_OK = 0
+GEMM_EINVAL = 1
+GEMM_ELAUNCH = 2
+GEMM_MAX_K = 4194303
+
+# Every symbol the header declares.
+EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {gemm_nt_f16_strerror(code)} (code {code})")
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def lib():
+    """Load ``libgemm18.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it first with "
+            "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(str(_LIB_PATH))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.gemm_nt_f16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_nt_f16.restype = ctypes.c_int
+    L.gemm_nt_f16_strerror.argtypes = [ctypes.c_int]
+    L.gemm_nt_f16_strerror.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    L.gemm_nt_f16_tile.argtypes = [i64, i64, i64, ip, ip, ip, lp]
+    L.gemm_nt_f16_tile.restype = ctypes.c_int
+    L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
+    L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ---- the C entry points, same names ---------------------------------------
+
+def gemm_nt_f16(A: int, B: int, D: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Raw call: device addresses as integers; returns the C return code."""
+    return lib().gemm_nt_f16(A or None, B or None, D or None, M, N, K, stream or None)
+
+
+def gemm_nt_f16_strerror(code: int) -> str:
+    return lib().gemm_nt_f16_strerror(code).decode()
+
+
+def gemm_nt_f16_tile(M: int, N: int, K: int):
+    """(BM, BN, BK, workgroups) the library uses for an M x N x K problem."""
+    bm, bn, bk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    wg = ctypes.c_int64()
+    rc = lib().gemm_nt_f16_tile(M, N, K, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(bk),
+                                ctypes.byref(wg))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_tile")
+    return bm.value, bn.value, bk.value, wg.value
+
+
+def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):
+    """(tile_m, tile_n) computed by workgroup ``wg``."""
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().gemm_nt_f16_tile_coord(wg, tiles_m, tiles_n, ctypes.byref(tm), ctypes.byref(tn))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_tile_coord")
+    return tm.value, tn.value
+
+
+# ---- tensor-level convenience ----------------------------------------------
+
+def gemm_nt(A, B, out=None, stream=None):
+    """D = A @ B.T for fp16 CUDA (HIP) tensors A [M, K] and B [N, K].
+
+    ``out`` (optional) is a contiguous fp16 [M, N] tensor on the same device.
+    The call is enqueued on ``stream`` (default: the current stream).
+    """
+    import torch
+
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError(f"shapes {tuple(A.shape)} and {tuple(B.shape)} are not [M,K] and [N,K]")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("A and B must be on the same GPU")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous row-major")
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
+          or out.device != A.device):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor on A's device")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    rc = gemm_nt_f16(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, s.cuda_stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16")
+    return out

@@ -1,0 +1,122 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare with the oracle.
+
+Tolerance for random inputs, evaluated in fp64 on the widened fp16 values:
+    |D_gpu - D_ref| <= 2^-10 * |D_ref| + 1e-3 * sqrt(K)
+where D_ref is the oracle's fp16 result.  The first term is one fp16
+rounding step (half an ulp is 2^-11 relative; the fp32-accumulated sum may
+land on the other side of a rounding boundary); the second bounds the fp32
+accumulation drift, which grows like sqrt(K) for random signs.  Integer
+inputs must match bit for bit: fp32 sums of small integers are exact and
+both sides round the same exact value once.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+CANARY = 0x7E5A          # a NaN pattern the kernel never writes
+GUARD = 256              # guard elements on each side of D (512 B keeps alignment)
+
+
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    return torch.device("cuda:0")
+
+
+def note(msg: str) -> None:
+    """Name the case before a GPU step, flushed, so a fault still shows it."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, misalign_elems: int = 0):
+    """Copy fp16 numpy data to the GPU; optionally start it `misalign_elems`
+    fp16 elements past a 256-byte boundary (to exercise the general path)."""
+    import torch
+    dev = device()
+    flat = np.ascontiguousarray(x, dtype=np.float16).ravel()
+    if misalign_elems == 0:
+        return torch.from_numpy(flat.copy()).to(dev).view(x.shape), None
+    buf = torch.empty(flat.size + misalign_elems + 8, dtype=torch.float16, device=dev)
+    view = buf[misalign_elems: misalign_elems + flat.size]
+    view.copy_(torch.from_numpy(flat.copy()).to(dev))
+    return view.view(x.shape), buf
+
+
+def run_gemm(A: np.ndarray, B: np.ndarray, *, a_off: int = 0, b_off: int = 0, d_off: int = 0,
+             check_canary: bool = True, repeat: int = 1) -> np.ndarray:
+    """D = A B^T on the GPU through the C ABI; returns fp16 bit patterns.
+
+    D lives inside a buffer with GUARD canary elements on both sides; the
+    canaries must survive.  `*_off` shift operands by whole fp16 elements."""
+    import torch
+    from dense_gemm_18_amd import binding
+
+    M, K = A.shape
+    N = B.shape[0]
+    dev = device()
+    dA, _ka = to_dev(A, a_off)
+    dB, _kb = to_dev(B, b_off)
+    total = M * N + 2 * GUARD + d_off
+    dbuf = torch.full((total,), int(np.uint16(CANARY).view(np.int16)), dtype=torch.int16,
+                      device=dev)
+    dptr = dbuf.data_ptr() + 2 * (GUARD + d_off)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for _ in range(repeat):
+        rc = binding.gemm_nt_f16(dA.data_ptr(), dB.data_ptr(), dptr, M, N, K, stream)
+        assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
+    torch.cuda.synchronize(dev)
+    host = dbuf.cpu().numpy().view(np.uint16)
+    if check_canary:
+        lo = host[: GUARD + d_off]
+        hi = host[GUARD + d_off + M * N:]
+        assert np.all(lo == CANARY), "write before D"
+        assert np.all(hi == CANARY), "write after D"
+    return host[GUARD + d_off: GUARD + d_off + M * N].reshape(M, N).copy()
+
+
+def f16val(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def tolerance_report(d_gpu: np.ndarray, d_ref: np.ndarray, K: int) -> dict:
+    """Elementwise tolerance check; returns a summary (ok, counts, worst)."""
+    g = f16val(d_gpu)
+    r = f16val(d_ref)
+    inf_ref = np.isinf(r)
+    bound = 2.0 ** -10 * np.abs(r) + 1e-3 * math.sqrt(max(K, 0))
+    with np.errstate(invalid="ignore"):
+        err = np.abs(g - r)
+    ok_fin = (~inf_ref) & np.isfinite(g) & (err <= bound)
+    ok_inf = inf_ref & (g == r)
+    ok = ok_fin | ok_inf
+    same = d_gpu == d_ref
+    bad = np.flatnonzero(~ok.ravel())
+    return {
+        "ok": bool(ok.all()),
+        "n": int(ok.size),
+        "bad": int(bad.size),
+        "first_bad": [int(i) for i in bad[:5]],
+        "bitwise_equal_frac": float(same.mean()) if same.size else 1.0,
+        "max_err": float(np.nanmax(np.where(inf_ref, 0, err))) if err.size else 0.0,
+    }
+
+
+def assert_tolerance(d_gpu, d_ref, K, what=""):
+    rep = tolerance_report(d_gpu, d_ref, K)
+    note(f"{what}: {rep}")
+    assert rep["ok"], f"{what}: {rep['bad']} of {rep['n']} entries outside tolerance {rep}"
+    return rep
+
+
+def assert_bitexact(d_gpu, d_ref, what=""):
+    diff = np.flatnonzero(d_gpu.ravel() != d_ref.ravel())
+    if diff.size:
+        i = diff[0]
+        raise AssertionError(f"{what}: {diff.size} entries differ; first flat index {i}: "
+                             f"gpu 0x{int(d_gpu.ravel()[i]):04x} ref 0x{int(d_ref.ravel()[i]):04x}")

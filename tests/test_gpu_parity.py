@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Integer-valued inputs must match bit for bit; random inputs must satisfy
+|D_gpu - D_ref| <= 2^-10 |D_ref| + 1e-3 sqrt(K) elementwise.  Full outputs
+are compared wherever the oracle finishes in seconds; the 8192^3 workload is
+compared on 4096 seeded entries plus full rows and columns at tile edges,
+through the same entry point and launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_18_amd import binding
+from dense_gemm_18_amd import workloads as wl
+from tests.gpu_util import assert_bitexact, assert_tolerance, note, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tile_128x128x64", "square_1024", "ragged_3000x5000x2050", "skinny_64x16384x8192"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library_present():
+    # The product path must be the native library; a missing build is a failure.
+    assert binding.library_path().exists(), "libgemm18.so not built"
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_random_full(name):
+    w = wl.WORKLOADS[name]
+    A, B = wl.random_inputs(w)
+    note(f"{name} random M={w.M} N={w.N} K={w.K}")
+    d = run_gemm(A, B)
+    ref = oracle.gemm_nt_f16(A, B)
+    assert_tolerance(d, ref, w.K, f"{name} random")
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_integer_full(name):
+    w = wl.WORKLOADS[name]
+    A, B = wl.integer_inputs(w)
+    note(f"{name} integer M={w.M} N={w.N} K={w.K}")
+    d = run_gemm(A, B)
+    ref = oracle.gemm_nt_f16(A, B)
+    assert np.abs(oracle.decode(ref)).max() <= 2048
+    assert_bitexact(d, ref, f"{name} integer")
+
+
+def _headline_positions(w):
+    rows, cols = wl.sample_indices(w, 4096)
+    bm, bn, _, _ = binding.gemm_nt_f16_tile(w.M, w.N, w.K)
+    er = wl.edge_lines(w.M, bm)
+    ec = wl.edge_lines(w.N, bn)
+    return rows, cols, er, ec
+
+
+@pytest.mark.parametrize("variant", ["random", "integer"])
+def test_headline_8192_sampled(variant):
+    w = wl.WORKLOADS[wl.HEADLINE]
+    A, B = wl.random_inputs(w) if variant == "random" else wl.integer_inputs(w)
+    note(f"{w.name} {variant} (sampled + tile-edge rows/cols)")
+    d = run_gemm(A, B, check_canary=True)
+    rows, cols, er, ec = _headline_positions(w)
+    # 4096 sampled entries
+    ref_s = oracle.gemm_nt_f16_entries(A, B, rows, cols)
+    got_s = d[rows, cols]
+    # full rows and full columns at tile edges
+    rr = np.repeat(er, w.N)
+    rc = np.tile(np.arange(w.N), er.size)
+    cr = np.tile(np.arange(w.M), ec.size)
+    cc = np.repeat(ec, w.M)
+    ref_r = oracle.gemm_nt_f16_entries(A, B, rr, rc)
+    ref_c = oracle.gemm_nt_f16_entries(A, B, cr, cc)
+    got_r = d[rr, rc]
+    got_c = d[cr, cc]
+    ref = np.concatenate([ref_s, ref_r, ref_c])
+    got = np.concatenate([got_s, got_r, got_c])
+    if variant == "integer":
+        assert np.abs(oracle.decode(ref)).max() <= 2048
+        assert_bitexact(got, ref, f"{w.name} integer sampled")
+    else:
+        assert_tolerance(got, ref, w.K, f"{w.name} random sampled")
+
+
+def test_permutation_lane_maps():
+    # Permutation operands make any row/column mis-map of the MFMA lanes or
+    # the epilogue visible bit for bit (128 x 128 x 64, one tile).
+    rng = np.random.default_rng(91)
+    M = N = 128
+    K = 64
+    A = np.zeros((M, K), np.float16)
+    A[np.arange(M), rng.integers(0, K, M)] = 1
+    B = (rng.integers(1, 9, (N, K)) * rng.choice([-1, 1], (N, K))).astype(np.float16)
+    note("permutation 128x128x64")
+    assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), "A one-hot rows")
+    Bp = np.zeros((N, K), np.float16)
+    Bp[np.arange(N), rng.integers(0, K, N)] = 1
+    A2 = (rng.integers(1, 9, (M, K)) * rng.choice([-1, 1], (M, K))).astype(np.float16)
+    assert_bitexact(run_gemm(A2, Bp), oracle.gemm_nt_f16(A2, Bp), "B one-hot rows")
+    # identity: D = B^T for A = I_K
+    I = np.eye(K, dtype=np.float16)
+    Bq = (rng.integers(1, 9, (300, K))).astype(np.float16)
+    assert_bitexact(run_gemm(I, Bq), oracle.gemm_nt_f16(I, Bq), "A = I")
+
+
+@pytest.mark.parametrize("K", list(range(1, 131)))
+def test_every_k_tail(K):
+    A, B = wl.integer_free(1000 + K, 67, 45, K)
+    note(f"K tail K={K}")
+    assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), f"K={K}")
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (1, 300), (300, 1), (2, 3), (31, 33), (63, 65),
+                                 (64, 64), (65, 63), (127, 129), (128, 128), (129, 257),
+                                 (255, 256), (256, 255), (257, 257), (300, 299), (513, 1031)])
+def test_mn_sweep(M, N):
+    A, B = wl.integer_free(2000 + M * 7 + N, M, N, 40)
+    note(f"MN sweep {M}x{N}x40")
+    assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), f"{M}x{N}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1100, 1100, 96), (800, 2300, 72), (2000, 700, 136)])
+def test_big_tile_tails(M, N, K):
+    # shapes large enough for the 256 x 256 tile, with ragged M, N and K
+    A, B = wl.integer_free(3000 + K, M, N, K)
+    bm, bn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
+    note(f"big-tile tails {M}x{N}x{K} tile {bm}x{bn}")
+    assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("a_off,b_off,d_off,K", [(1, 0, 0, 64), (0, 1, 0, 64), (0, 0, 1, 64),
+                                                 (2, 2, 2, 64), (1, 3, 5, 37), (0, 0, 0, 66),
+                                                 (0, 0, 0, 67), (4, 4, 3, 130)])
+def test_misaligned_pointers_and_k(a_off, b_off, d_off, K):
+    A, B = wl.integer_free(4000 + K + a_off, 150, 97, K)
+    note(f"misaligned a+{a_off} b+{b_off} d+{d_off} K={K}")
+    assert_bitexact(run_gemm(A, B, a_off=a_off, b_off=b_off, d_off=d_off),
+                    oracle.gemm_nt_f16(A, B), "misaligned")
+
+
+def test_random_small_general_path():
+    A, B = wl.uniform_inputs(77, 333, 222, 1001)     # K odd: element loads
+    note("random 333x222x1001")
+    assert_tolerance(run_gemm(A, B), oracle.gemm_nt_f16(A, B), 1001, "odd K random")
+
+
+def test_k_zero_writes_positive_zero():
+    A = np.zeros((70, 0), np.float16)
+    B = np.zeros((90, 0), np.float16)
+    note("K=0")
+    d = run_gemm(A, B)
+    assert np.all(d == 0)
+
+
+def test_subnormal_and_overflow():
+    K = 512
+    A = np.full((64, K), 2.0 ** -24, np.float16)           # smallest subnormal
+    B = np.full((64, K), 1024.0, np.float16)
+    note("subnormal inputs")
+    assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), "subnormal")
+    A2 = np.full((64, 256), 16.0, np.float16)
+    note("overflow to inf")
+    d = run_gemm(A2, A2)
+    assert np.all(d == 0x7C00)
+    d = run_gemm(A2, -A2)
+    assert np.all(d == 0xFC00)
+
+
+def test_deterministic_repeat():
+    w = wl.WORKLOADS["square_1024"]
+    A, B = wl.random_inputs(w)
+    note("determinism 1024^3 x3")
+    d0 = run_gemm(A, B)
+    d1 = run_gemm(A, B)
+    d2 = run_gemm(A, B, repeat=3)
+    assert np.array_equal(d0, d1) and np.array_equal(d0, d2)
+
+
+def test_rejects_bad_arguments_without_launch():
+    import torch
+    x = torch.zeros(16, dtype=torch.float16, device="cuda:0")
+    p = x.data_ptr()
+    assert binding.gemm_nt_f16(p, p + 32, p, 4, 4, 2, 0) == binding.GEMM_EINVAL   # D overlaps A
+    assert binding.gemm_nt_f16(p, p, p + 1, 1, 1, 1, 0) == binding.GEMM_EINVAL    # misaligned D
+    assert binding.gemm_nt_f16(p, p, p, -1, 1, 1, 0) == binding.GEMM_EINVAL
+    assert binding.gemm_nt_f16(p, p, p, 0, 3, 3, 0) == binding.GEMM_OK             # M = 0: no-op

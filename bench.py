@@ -82,6 +82,18 @@ def cpu_baseline(A, B, M, N, K, budget_s: float = 12.0) -> dict:
     }
 
 
+def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> int:
+    """A plain copy of known size: each launch reads and writes `nbytes`."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_calibration_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +101,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8192^3 GEMM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     ap.add_argument("--torch-context", action="store_true",
                     help="also time torch.nn.functional.linear on the same inputs (context only)")
     args = ap.parse_args()
@@ -98,8 +113,10 @@ def main() -> int:
               "single-GPU and has no multi-GPU mode.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     from dense_gemm_18_amd import binding
     from dense_gemm_18_amd import build as hip_build

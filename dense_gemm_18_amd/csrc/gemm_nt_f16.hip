@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_nt_f16.h"
 
 namespace {
@@ -126,6 +128,47 @@ __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t 
         }
     }
     return v;
+}
+
+// Epilogue shared by the kernels.  With B as the MFMA's first operand,
+// accumulator r of MFMA block (i, j) holds D[m][n] for
+//   m = mbase + 32 i + lane % 32,  n = nbase + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4,
+// so each group of four accumulators is four consecutive columns of one row.
+// fp32 -> fp16 uses v_cvt_f16_f32 (round to nearest even); stores are masked
+// at the M and N edges.  vec_store: D is 8-byte aligned and N % 4 == 0.
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 *__restrict__ D,
+                                          int M, int N, int mbase, int nbase, int lane,
+                                          int vec_store)
+{
+    const int frow = lane & 31, fhi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = mbase + 32 * i + frow;
+        if (m >= M)
+            continue;
+        _Float16 *drow = D + (int64_t)m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = nbase + 32 * j + 8 * g + 4 * fhi;
+                f16x4 h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = (_Float16)acc[i][j][4 * g + r];
+                if (vec_store) {
+                    if (n < N)
+                        *(f16x4 *)(drow + n) = h;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            drow[n + r] = h[r];
+                }
+            }
+        }
+    }
 }
 
 template <class C, int LOADB>
@@ -233,36 +276,245 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
         __syncthreads();
     }
 
-    // Epilogue.  With B as the MFMA's first operand, accumulator r of block
-    // (i, j) holds D[m][n] for m = row base + lane % 32 and
-    // n = column base + 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+    store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel (fast path: K % 8 == 0, A and B 16-byte aligned).
+//
+// gfx950's buffer_load_dwordx4 ... lds writes each lane's 16 bytes straight
+// into LDS, at M0 + 16 * lane: one instruction fills 1024 contiguous bytes
+// and needs no staging registers and no ds_write.  That leaves room for a
+// ring of NSTAGE LDS stages of BK = 32, so the loads for K-step u + NSTAGE - 1
+// are in flight while step u is multiplied (page 1, "内核 3：Warp 特化" and
+// "内核 4", overlaps loads with MMAs through a STAGES-deep ring; here one
+// wavefront both loads and multiplies, and the ring is tracked with vmcnt
+// and one workgroup barrier per K-step instead of full/empty events).
+//
+// LDS rows are BK fp16 (64 or 128 bytes, four or eight 16-byte chunks).  The
+// swizzle is applied on the global side: LDS slot (row, chunk) receives
+// global chunk chunk ^ swz_row(row) of that row.  Both swizzles were chosen
+// by measuring SQ_LDS_BANK_CONFLICT for the MFMA fragment read pattern
+// (32 rows x 16 bytes per half wave) on gfx950: zero conflicts.
+#ifndef GEMM_DMA_BK
+#define GEMM_DMA_BK 64
+#endif
+#ifndef GEMM_DMA_NSTAGE
+#define GEMM_DMA_NSTAGE 2
+#endif
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// Chunk swizzle of an LDS row of BK fp16.
+template <int BK>
+__device__ __forceinline__ int swz_row(int row) { return BK == 64 ? swz(row) : swz64(row); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt
+// left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// outstanding direct-to-LDS load, prefetches included).  This wave's LDS
+// reads complete first (lgkmcnt 0, issued as the builtin so the compiler's
+// own wait tracking sees it); the empty asm with a "memory" clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
+    static constexpr int BK = BK_;
+    static constexpr int SLICES = BK / 16;                   // 16-wide K slices per step
+    static constexpr int CPR = BK / 8;                       // 16-byte chunks per LDS row
+    static constexpr int NWAVES = WM * WN, THREADS = NWAVES * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int ROW_BYTES = BK * 2;                 // 64
+    static constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;   // 16 rows per load instruction
+    static constexpr int A_LOADS = BM / ROWS_PER_INST / NWAVES;   // per wave per stage
+    static constexpr int B_LOADS = BN / ROWS_PER_INST / NWAVES;
+    static constexpr int LPS = A_LOADS + B_LOADS;            // vmcnt units per stage
+    static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+    static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
+    static_assert(BM % (ROWS_PER_INST * NWAVES) == 0 && BN % (ROWS_PER_INST * NWAVES) == 0,
+                  "load instructions must split evenly over the waves");
+    static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
+    static_assert(NSTAGE >= 2 && LPS * (NSTAGE - 1) < 64, "vmcnt budget");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, 1)
+gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+                       _Float16 *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n,
+                       int vec_store)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
+    const int wm = wave % C::WM, wn = wave / C::WM;
+
+    int64_t tm64, tn64;
+    tile_coord(blockIdx.x, tiles_m, tiles_n, tm64, tn64);
+    const int m0 = (int)tm64 * C::BM, n0 = (int)tn64 * C::BN;
+    const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * K), (short)0, rows_a * K * 2, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcFlags);
+
+    // This lane's part of each load instruction: LDS slot `lane` of a
+    // 16-row block is row lane / 4, chunk lane % 4; it fetches the global
+    // chunk that the swizzle places there.  Instruction i of this wave covers
+    // rows 16 * (wave + NWAVES * i) ...
+    const int slot_row = lane / C::CPR;
+    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+    int a_k[C::A_LOADS], b_k[C::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-        const int m = m0 + wm * C::WTM + 32 * i + frow;
-        if (m >= M)
-            continue;
-        _Float16 *drow = D + (int64_t)m * N;
+    for (int i = 0; i < C::A_LOADS; ++i) {
+        const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
+        const int gch = (lane % C::CPR) ^ swz_row<C::BK>(row);
+        a_k[i] = gch * 8;
+        a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
+    }
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
+    for (int i = 0; i < C::B_LOADS; ++i) {
+        const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
+        const int gch = (lane % C::CPR) ^ swz_row<C::BK>(row);
+        b_k[i] = gch * 8;
+        b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
+    }
+
+    // One global->LDS load of step `step`: q < A_LOADS moves A rows, the
+    // rest B rows.  Instruction q covers 1024 contiguous LDS bytes.
+    auto issue_one = [&](int step, int q) {
+        const int k0 = step * C::BK;
+        char *stage = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
+        if (q < C::A_LOADS) {
+            const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOob;
+            char *dst = stage + (wave + C::NWAVES * q) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 16, off, 0, 0, 0);
+        } else {
+            const int i = q - C::A_LOADS;
+            const uint32_t off = (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : kOob;
+            char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[C::TM][C::TN];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * C::WTN + 32 * j + 8 * g + 4 * fhi;
-                f16x4 h;
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][4 * g + r];
-                if (vec_store) {
-                    if (n < N)
-                        *(f16x4 *)(drow + n) = h;
-                } else {
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = f32x16{};
+
+    const int frow = lane & 31, fhi = lane >> 5;
+    const int a_row0 = wm * C::WTM + frow;
+    const int b_row0 = wn * C::WTN + frow;
+    const int fsw = swz_row<C::BK>(frow);   // fragment rows differ from frow by multiples of 32
+
+    // Fragments of one 16-wide K slice: lane l holds row l % 32 of each
+    // 32-row block and K chunk 2t + l / 32 of slice t (the same pattern for A
+    // and B, which are both K-contiguous).  Fragment q < TM is A block q, the
+    // rest B blocks.
+    f16x8 fr[2][C::TM + C::TN];
+    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], int step, int t, int q) {
+        const char *sa = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
+        const int ch = ((2 * t + fhi) ^ fsw) * 16;
+        if (q < C::TM)
+            f[q] = *(const f16x8 *)(sa + (a_row0 + 32 * q) * C::ROW_BYTES + ch);
+        else
+            f[q] = *(const f16x8 *)(sa + C::BM * C::ROW_BYTES +
+                                    (b_row0 + 32 * (q - C::TM)) * C::ROW_BYTES + ch);
+    };
+
+    // One slice: MFMA q of TM x TN, each followed by at most one global->LDS
+    // load and at most one fragment read for the next slice; the scheduling
+    // fences keep exactly this issue order, so neither kind of issue stalls
+    // the MFMA pipe for long (one wavefront per SIMD: nothing else can fill
+    // an issue gap).
+    auto slice = [&](const f16x8 (&cur)[C::TM + C::TN], f16x8 (&nxt)[C::TM + C::TN],
+                     int rstep, int rt, bool do_read, int lstep, bool do_load) {
+        constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            drow[n + r] = h[r];
-                }
+        for (int q = 0; q < NM; ++q) {
+            const int i = q / C::TN, j = q % C::TN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[C::TM + j], cur[i], acc[i][j],
+                                                                0, 0, 0);
+            if (do_load && q < C::LPS)
+                issue_one(lstep, q);
+            if (do_read && q < NR)
+                read_one(nxt, rstep, rt, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Software pipeline over K-steps of BK (SLICES 16-wide slices each).
+    // Fragments are double-buffered: slice t + 1 is read while slice t is
+    // multiplied.  Before the last slice of step u, the workgroup barrier
+    // makes step u + 1 readable and frees step u's stage, which is refilled
+    // with step u + NSTAGE while the last slice is multiplied; step u + 1's
+    // first slice loads under the same MFMAs.  The prefetch is
+    // unconditional: steps past the end have every offset out of range and
+    // only write zeros into a stage no one reads again, which keeps the
+    // vmcnt accounting the same in every iteration.
+    const int nk = (K + C::BK - 1) / C::BK;
+#pragma unroll
+    for (int st = 0; st < C::NSTAGE; ++st)
+#pragma unroll
+        for (int q = 0; q < C::LPS; ++q)
+            issue_one(st, q);
+    wait_vmcnt<C::LPS * (C::NSTAGE - 1)>();
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < C::TM + C::TN; ++q)
+        read_one(fr[0], 0, 0, q);
+
+    static_assert(C::SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
+    auto step_body = [&](int u, bool last) {
+#pragma unroll
+        for (int t = 0; t < C::SLICES; ++t) {
+            const int c = t & 1;
+            if (t + 1 < C::SLICES) {
+                slice(fr[c], fr[c ^ 1], u, t + 1, true, 0, false);
+            } else if (!last) {
+                // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
+                // be outstanding.  The fence keeps the previous slice's MFMAs
+                // ahead of the barrier, where they run while the wave waits.
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                slice(fr[c], fr[c ^ 1], u + 1, 0, true, u + C::NSTAGE, true);
+            } else {
+                slice(fr[c], fr[c ^ 1], 0, 0, false, 0, false);
             }
         }
-    }
+    };
+    for (int u = 0; u + 1 < nk; ++u)
+        step_body(u, false);
+    step_body(nk - 1, true);
+    wait_vmcnt<0>();      // drain the zero-filling prefetches before exit
+
+    store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
 }
 
 // D = +0 everywhere (K == 0).
@@ -278,6 +530,7 @@ __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
 using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
 using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
+using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE>;
 
 enum class Tile { kBig, kMid, kThin };
 
@@ -332,10 +585,25 @@ void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int 
 }
 
 template <class C>
+void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s)
+{
+    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
+    hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C>), dim3((unsigned)(tm * tn)), dim3(C::THREADS),
+                       0, s, (const _Float16 *)A, (const _Float16 *)B, (_Float16 *)D, M, N, K,
+                       tm, tn, vec);
+}
+
+template <class C, class CDma = void>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    if constexpr (!std::is_void<CDma>::value) {
+        if (K % 8 == 0 && (ab & 15u) == 0) {
+            launch_dma<CDma>(A, B, D, M, N, K, vec, s);
+            return;
+        }
+    }
     if (K % 8 == 0 && (ab & 15u) == 0)
         launch_cfg<C, 16>(A, B, D, M, N, K, vec, s);
     else if (K % 2 == 0 && (ab & 3u) == 0)
@@ -363,7 +631,7 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                            (uint16_t *)D, count);
     } else {
         switch (choose_tile(M, N)) {
-        case Tile::kBig: launch_tile<Big>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kBig: launch_tile<Big, BigDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         case Tile::kMid: launch_tile<Mid>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         default: launch_tile<Thin>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         }

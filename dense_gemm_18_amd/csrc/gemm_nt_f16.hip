@@ -321,6 +321,21 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Kernel-local lambdas must always inline: an out-of-line call would keep
+// every array they capture by reference in scratch memory.
+#define G18_INLINE __attribute__((always_inline))
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1, so that
+// register arrays are only ever indexed by constants.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Workgroup barrier without a memory fence (a fence would wait for every
 // outstanding direct-to-LDS load, prefetches included).  This wave's LDS
 // reads complete first (lgkmcnt 0, issued as the builtin so the compiler's
@@ -404,15 +419,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
 
     // One global->LDS load of step `step`: q < A_LOADS moves A rows, the
     // rest B rows.  Instruction q covers 1024 contiguous LDS bytes.
-    auto issue_one = [&](int step, int q) {
+    auto issue_one = [&](int step, auto qc) G18_INLINE {
+        constexpr int q = decltype(qc)::value;
         const int k0 = step * C::BK;
         char *stage = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
-        if (q < C::A_LOADS) {
+        if constexpr (q < C::A_LOADS) {
             const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOob;
             char *dst = stage + (wave + C::NWAVES * q) * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 16, off, 0, 0, 0);
         } else {
-            const int i = q - C::A_LOADS;
+            constexpr int i = q - C::A_LOADS;
             const uint32_t off = (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : kOob;
             char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 16, off, 0, 0, 0);
@@ -436,65 +452,79 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // and B, which are both K-contiguous).  Fragment q < TM is A block q, the
     // rest B blocks.
     f16x8 fr[2][C::TM + C::TN];
-    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], int step, int t, int q) {
+    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], int step, int t, auto qc) G18_INLINE {
+        constexpr int q = decltype(qc)::value;
         const char *sa = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
         const int ch = ((2 * t + fhi) ^ fsw) * 16;
-        if (q < C::TM)
+        if constexpr (q < C::TM)
             f[q] = *(const f16x8 *)(sa + (a_row0 + 32 * q) * C::ROW_BYTES + ch);
         else
             f[q] = *(const f16x8 *)(sa + C::BM * C::ROW_BYTES +
                                     (b_row0 + 32 * (q - C::TM)) * C::ROW_BYTES + ch);
     };
 
-    // One slice: MFMA q of TM x TN, each followed by at most one global->LDS
-    // load and at most one fragment read for the next slice; the scheduling
-    // fences keep exactly this issue order, so neither kind of issue stalls
-    // the MFMA pipe for long (one wavefront per SIMD: nothing else can fill
-    // an issue gap).
+    // One slice: MFMA q of TM x TN, each followed by at most one fragment
+    // read for the next slice and, every LSPACE MFMAs, one global->LDS load
+    // (loads l0, l0+1, ... of step lstep).  The scheduling fences keep
+    // exactly this issue order.  With one wavefront per SIMD nothing else
+    // fills an issue gap, and the loads of all four waves share the CU's
+    // load pipe (about 25 cycles per 1 KB load), so the loads are spread
+    // evenly over two slices instead of issued in a burst.
+    constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
+    constexpr int LHALF = C::LPS / 2;
+    constexpr int LSPACE = NM / LHALF;
+    static_assert(C::LPS % 2 == 0 && NM % LHALF == 0, "loads split evenly over two slices");
+    // DO_READ / L0 / DO_LOAD arrive as integral_constants.
     auto slice = [&](const f16x8 (&cur)[C::TM + C::TN], f16x8 (&nxt)[C::TM + C::TN],
-                     int rstep, int rt, bool do_read, int lstep, bool do_load) {
-        constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-            const int i = q / C::TN, j = q % C::TN;
+                     int rstep, int rt, auto do_read, int lstep, auto l0, bool do_load) G18_INLINE {
+        static_for<0, NM>([&](auto qc) G18_INLINE {
+            constexpr int q = decltype(qc)::value;
+            constexpr int i = q / C::TN, j = q % C::TN;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[C::TM + j], cur[i], acc[i][j],
                                                                 0, 0, 0);
-            if (do_load && q < C::LPS)
-                issue_one(lstep, q);
-            if (do_read && q < NR)
-                read_one(nxt, rstep, rt, q);
+            if constexpr (decltype(do_read)::value && q < NR)
+                read_one(nxt, rstep, rt, qc);
+            if constexpr (q % LSPACE == 0) {
+                if (do_load)
+                    issue_one(lstep, std::integral_constant<int, decltype(l0)::value + q / LSPACE>{});
+            }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
 
     // Software pipeline over K-steps of BK (SLICES 16-wide slices each).
     // Fragments are double-buffered: slice t + 1 is read while slice t is
     // multiplied.  Before the last slice of step u, the workgroup barrier
     // makes step u + 1 readable and frees step u's stage, which is refilled
-    // with step u + NSTAGE while the last slice is multiplied; step u + 1's
-    // first slice loads under the same MFMAs.  The prefetch is
-    // unconditional: steps past the end have every offset out of range and
-    // only write zeros into a stage no one reads again, which keeps the
-    // vmcnt accounting the same in every iteration.
+    // with step u + NSTAGE: the first half of its loads during the last
+    // slice of step u, the second half during the first slice of step u + 1
+    // (each step's loads stay contiguous in issue order, so "step u + 1 has
+    // landed" is "at most (NSTAGE - 2) * LPS loads outstanding").  Step
+    // u + 1's first fragments load under the last MFMAs of step u.  The
+    // prefetch is unconditional: steps past the end have every offset out of
+    // range and only write zeros into a stage no one reads again, which
+    // keeps the vmcnt accounting the same in every iteration.
     const int nk = (K + C::BK - 1) / C::BK;
-#pragma unroll
     for (int st = 0; st < C::NSTAGE; ++st)
-#pragma unroll
-        for (int q = 0; q < C::LPS; ++q)
-            issue_one(st, q);
+        static_for<0, C::LPS>([&](auto qc) G18_INLINE { issue_one(st, qc); });
     wait_vmcnt<C::LPS * (C::NSTAGE - 1)>();
     lds_barrier();
-#pragma unroll
-    for (int q = 0; q < C::TM + C::TN; ++q)
-        read_one(fr[0], 0, 0, q);
+    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], 0, 0, qc); });
 
     static_assert(C::SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
-    auto step_body = [&](int u, bool last) {
-#pragma unroll
-        for (int t = 0; t < C::SLICES; ++t) {
-            const int c = t & 1;
-            if (t + 1 < C::SLICES) {
-                slice(fr[c], fr[c ^ 1], u, t + 1, true, 0, false);
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using Z_ = std::integral_constant<int, 0>;
+    using H_ = std::integral_constant<int, LHALF>;
+    auto step_body = [&](int u, bool last) G18_INLINE {
+        static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
+            constexpr int t = decltype(tc)::value;
+            constexpr int c = t & 1;
+            if constexpr (t == 0) {
+                // second half of step u - 1 + NSTAGE (issued in the prologue for u = 0)
+                slice(fr[c], fr[c ^ 1], u, t + 1, T_{}, u - 1 + C::NSTAGE, H_{}, u > 0);
+            } else if constexpr (t + 1 < C::SLICES) {
+                slice(fr[c], fr[c ^ 1], u, t + 1, T_{}, 0, Z_{}, false);
             } else if (!last) {
                 // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
                 // be outstanding.  The fence keeps the previous slice's MFMAs
@@ -503,11 +533,11 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                 wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
                 lds_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                slice(fr[c], fr[c ^ 1], u + 1, 0, true, u + C::NSTAGE, true);
+                slice(fr[c], fr[c ^ 1], u + 1, 0, T_{}, u + C::NSTAGE, Z_{}, true);
             } else {
-                slice(fr[c], fr[c ^ 1], 0, 0, false, 0, false);
+                slice(fr[c], fr[c ^ 1], 0, 0, F_{}, 0, Z_{}, false);
             }
-        }
+        });
     };
     for (int u = 0; u + 1 < nk; ++u)
         step_body(u, false);

@@ -47,11 +47,18 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
-constexpr int kGroupM = 4;         // tile rows per rasterisation group
+#ifndef GEMM_GROUP_M
+#define GEMM_GROUP_M 4
+#endif
+#ifndef GEMM_TILE_ORDER
+#define GEMM_TILE_ORDER 0
+#endif
+constexpr int kGroupM = GEMM_GROUP_M;   // tile rows per rasterisation group
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range
 constexpr int kRsrcFlags = 0x00020000;   // gfx9 buffer descriptor word 3
@@ -66,7 +73,11 @@ __host__ __device__ inline void tile_coord(int64_t wg, int64_t tiles_m, int64_t 
     // a contiguous range of logical ids.
     const int64_t q = total / kXcds, r = total % kXcds;
     const int64_t x = wg % kXcds, i = wg / kXcds;
+#if GEMM_TILE_ORDER == 1
+    const int64_t logical = wg;
+#else
     const int64_t logical = x * q + (x < r ? x : r) + i;
+#endif
     // Grouped rasterisation: kGroupM tile rows at a time, rows fastest.
     const int64_t per_group = (int64_t)kGroupM * tiles_n;
     const int64_t g = logical / per_group;
@@ -166,6 +177,41 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 
                         if (n + r < N)
                             drow[n + r] = h[r];
                 }
+            }
+        }
+    }
+}
+
+// Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
+// accumulator r of block (i, j) holds D[m][n] for
+//   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16 *__restrict__ D,
+                                            int M, int N, int mbase, int nbase, int lane,
+                                            int vec_store)
+{
+    const int frow = lane & 15, fq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = mbase + 16 * i + frow;
+        if (m >= M)
+            continue;
+        _Float16 *drow = D + (int64_t)m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = nbase + 16 * j + 4 * fq;
+            f16x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                h[r] = (_Float16)acc[i][j][r];
+            if (vec_store) {
+                if (n < N)
+                    *(f16x4 *)(drow + n) = h;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        drow[n + r] = h[r];
             }
         }
     }
@@ -302,14 +348,27 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
 #ifndef GEMM_DMA_NSTAGE
 #define GEMM_DMA_NSTAGE 2
 #endif
+#ifndef GEMM_LOAD_AUX
+#define GEMM_LOAD_AUX 0
+#endif
+#ifndef GEMM_DMA_MF
+#define GEMM_DMA_MF 32
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
-// Chunk swizzle of an LDS row of BK fp16.
-template <int BK>
-__device__ __forceinline__ int swz_row(int row) { return BK == 64 ? swz(row) : swz64(row); }
+// 128-byte rows read by 16x16x32 fragments (16 rows x 16 bytes per quarter
+// wave): measured conflict-free, and also for the 32x32x16 pattern.
+__device__ __forceinline__ int swz128_q(int row) { return (row >> 1) & 7; }
+
+// Chunk swizzle of an LDS row of BK fp16 read by MF x MF MFMA fragments.
+template <int BK, int MF>
+__device__ __forceinline__ int swz_row(int row)
+{
+    return BK == 64 ? (MF == 32 ? swz(row) : swz128_q(row)) : swz64(row);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt
@@ -349,15 +408,20 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
     static constexpr int BK = BK_;
-    static constexpr int SLICES = BK / 16;                   // 16-wide K slices per step
+    // MF = 32: v_mfma_f32_32x32x16_f16; MF = 16: v_mfma_f32_16x16x32_f16.
+    static constexpr int MF = MF_;
+    static constexpr int KSL = MF == 32 ? 16 : 32;           // K per MFMA (one slice)
+    static constexpr int SLICES = BK / KSL;                  // slices per step
+    static constexpr int CHS = KSL / 8;                      // 16-byte chunks per slice
     static constexpr int CPR = BK / 8;                       // 16-byte chunks per LDS row
     static constexpr int NWAVES = WM * WN, THREADS = NWAVES * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int TM = WTM / MF, TN = WTN / MF;
+    using acc_t = typename std::conditional<MF == 32, f32x16, f32x4>::type;
     static constexpr int ROW_BYTES = BK * 2;                 // 64
     static constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;   // 16 rows per load instruction
     static constexpr int A_LOADS = BM / ROWS_PER_INST / NWAVES;   // per wave per stage
@@ -365,7 +429,8 @@ struct DmaCfg {
     static constexpr int LPS = A_LOADS + B_LOADS;            // vmcnt units per stage
     static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
     static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
+    static_assert(MF == 32 || MF == 16, "MFMA block of 32x32 or 16x16");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
     static_assert(BM % (ROWS_PER_INST * NWAVES) == 0 && BN % (ROWS_PER_INST * NWAVES) == 0,
                   "load instructions must split evenly over the waves");
     static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
@@ -405,14 +470,14 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
         const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (lane % C::CPR) ^ swz_row<C::BK>(row);
+        const int gch = (lane % C::CPR) ^ swz_row<C::BK, C::MF>(row);
         a_k[i] = gch * 8;
         a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
         const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (lane % C::CPR) ^ swz_row<C::BK>(row);
+        const int gch = (lane % C::CPR) ^ swz_row<C::BK, C::MF>(row);
         b_k[i] = gch * 8;
         b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
     }
@@ -426,41 +491,41 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
         if constexpr (q < C::A_LOADS) {
             const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOob;
             char *dst = stage + (wave + C::NWAVES * q) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 16, off, 0, 0, GEMM_LOAD_AUX);
         } else {
             constexpr int i = q - C::A_LOADS;
             const uint32_t off = (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : kOob;
             char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 16, off, 0, 0, GEMM_LOAD_AUX);
         }
     };
 
-    f32x16 acc[C::TM][C::TN];
+    typename C::acc_t acc[C::TM][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = f32x16{};
+            acc[i][j] = typename C::acc_t{};
 
-    const int frow = lane & 31, fhi = lane >> 5;
+    const int frow = lane % C::MF, fhi = lane / C::MF;
     const int a_row0 = wm * C::WTM + frow;
     const int b_row0 = wn * C::WTN + frow;
-    const int fsw = swz_row<C::BK>(frow);   // fragment rows differ from frow by multiples of 32
+    const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
 
-    // Fragments of one 16-wide K slice: lane l holds row l % 32 of each
-    // 32-row block and K chunk 2t + l / 32 of slice t (the same pattern for A
-    // and B, which are both K-contiguous).  Fragment q < TM is A block q, the
-    // rest B blocks.
+    // Fragments of one K slice (16 wide for 32x32x16, 32 wide for 16x16x32):
+    // lane l holds row l % MF of each MF-row block and K chunk
+    // CHS * t + l / MF of slice t (the same pattern for A and B, which are
+    // both K-contiguous).  Fragment q < TM is A block q, the rest B blocks.
     f16x8 fr[2][C::TM + C::TN];
     auto read_one = [&](f16x8 (&f)[C::TM + C::TN], int step, int t, auto qc) G18_INLINE {
         constexpr int q = decltype(qc)::value;
         const char *sa = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
-        const int ch = ((2 * t + fhi) ^ fsw) * 16;
+        const int ch = ((C::CHS * t + fhi) ^ fsw) * 16;
         if constexpr (q < C::TM)
-            f[q] = *(const f16x8 *)(sa + (a_row0 + 32 * q) * C::ROW_BYTES + ch);
+            f[q] = *(const f16x8 *)(sa + (a_row0 + C::MF * q) * C::ROW_BYTES + ch);
         else
             f[q] = *(const f16x8 *)(sa + C::BM * C::ROW_BYTES +
-                                    (b_row0 + 32 * (q - C::TM)) * C::ROW_BYTES + ch);
+                                    (b_row0 + C::MF * (q - C::TM)) * C::ROW_BYTES + ch);
     };
 
     // One slice: MFMA q of TM x TN, each followed by at most one fragment
@@ -472,21 +537,36 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // evenly over two slices instead of issued in a burst.
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
     constexpr int LHALF = C::LPS / 2;
-    constexpr int LSPACE = NM / LHALF;
-    static_assert(C::LPS % 2 == 0 && NM % LHALF == 0, "loads split evenly over two slices");
+    // Spacing of the loads over the NM MFMAs of a slice: one load every
+    // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
+    // than MFMAs (small tiles); the same for fragment reads (RPG).
+    constexpr int LSPACE = NM >= LHALF ? NM / LHALF : 1;
+    constexpr int LPG = NM >= LHALF ? 1 : LHALF / NM;
+    constexpr int RPG = (NR + NM - 1) / NM;
+    static_assert(C::LPS % 2 == 0 && (NM % LHALF == 0 || LHALF % NM == 0),
+                  "loads split evenly over two slices");
     // DO_READ / L0 / DO_LOAD arrive as integral_constants.
     auto slice = [&](const f16x8 (&cur)[C::TM + C::TN], f16x8 (&nxt)[C::TM + C::TN],
                      int rstep, int rt, auto do_read, int lstep, auto l0, bool do_load) G18_INLINE {
         static_for<0, NM>([&](auto qc) G18_INLINE {
             constexpr int q = decltype(qc)::value;
             constexpr int i = q / C::TN, j = q % C::TN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[C::TM + j], cur[i], acc[i][j],
-                                                                0, 0, 0);
-            if constexpr (decltype(do_read)::value && q < NR)
-                read_one(nxt, rstep, rt, qc);
+            if constexpr (C::MF == 32)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[C::TM + j], cur[i],
+                                                                    acc[i][j], 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[C::TM + j], cur[i],
+                                                                    acc[i][j], 0, 0, 0);
+            if constexpr (decltype(do_read)::value)
+                static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
+                    [&](auto rc) G18_INLINE { read_one(nxt, rstep, rt, rc); });
             if constexpr (q % LSPACE == 0) {
                 if (do_load)
-                    issue_one(lstep, std::integral_constant<int, decltype(l0)::value + q / LSPACE>{});
+                    static_for<0, LPG>([&](auto gc) G18_INLINE {
+                        issue_one(lstep, std::integral_constant<int, decltype(l0)::value +
+                                                                         (q / LSPACE) * LPG +
+                                                                         decltype(gc)::value>{});
+                    });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -544,7 +624,11 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     step_body(nk - 1, true);
     wait_vmcnt<0>();      // drain the zero-filling prefetches before exit
 
-    store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
+    if constexpr (C::MF == 32)
+        store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
+    else
+        store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                  vec_store);
 }
 
 // D = +0 everywhere (K == 0).
@@ -560,7 +644,12 @@ __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
 using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
 using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
-using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE>;
+using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE, GEMM_DMA_MF>;
+// 128 x 128: 4 waves of 64 x 64, four 32 KB stages.
+using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 32>;
+// 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
+// eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
+using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16>;
 
 enum class Tile { kBig, kMid, kThin };
 
@@ -662,8 +751,8 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
     } else {
         switch (choose_tile(M, N)) {
         case Tile::kBig: launch_tile<Big, BigDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        case Tile::kMid: launch_tile<Mid>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        default: launch_tile<Thin>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kMid: launch_tile<Mid, MidDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        default: launch_tile<Thin, ThinDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         }
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;

@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="only run the GEMM back to back for this many seconds (for sampling "
+                         "clock and power with amd-smi); prints the achieved TFLOPS")
     ap.add_argument("--torch-context", action="store_true",
                     help="also time torch.nn.functional.linear on the same inputs (context only)")
     args = ap.parse_args()
@@ -145,6 +148,18 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+
+    if args.sustain > 0:
+        calls, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.sustain:
+            for _ in range(50):
+                step()
+            torch.cuda.synchronize(dev)
+            calls += 50
+        dt = time.perf_counter() - t0
+        print(json.dumps({"sustain_s": round(dt, 2), "calls": calls,
+                          "tflops": round(tflops(M, N, K, dt / calls), 1)}), flush=True)
+        return 0
 
     # Timed region: exactly `steps` calls, synchronised on both sides.  Each
     # launch is bracketed by HIP events on the launch stream.

@@ -438,7 +438,9 @@ struct DmaCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
-template <class C>
+// KTAIL: K % BK != 0, so the last step is partial and every load carries a
+// per-lane K mask; otherwise loads carry no mask at all.
+template <class C, bool KTAIL>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                        _Float16 *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n,
@@ -459,11 +461,18 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
         (void *)(A + (int64_t)m0 * K), (short)0, rows_a * K * 2, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(B + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcFlags);
+    // Zero-length resource: every load through it reads zero.  Steps past the
+    // end of K use it, chosen per step in scalar registers.
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)A, (short)0, 0, kRsrcFlags);
+    const int nk = (K + C::BK - 1) / C::BK;
 
-    // This lane's part of each load instruction: LDS slot `lane` of a
-    // 16-row block is row lane / 4, chunk lane % 4; it fetches the global
-    // chunk that the swizzle places there.  Instruction i of this wave covers
-    // rows 16 * (wave + NWAVES * i) ...
+    // This lane's part of each load instruction: LDS slot `lane` of a block
+    // of ROWS_PER_INST rows is row lane / CPR, chunk lane % CPR; it fetches
+    // the global chunk that the swizzle places there.  Instruction i of this
+    // wave covers rows ROWS_PER_INST * (wave + NWAVES * i) and up.  The
+    // vector offsets carry rows and chunks only; a step's K offset travels in
+    // the scalar offset, so a full step issues its loads with no VALU work.
     const int slot_row = lane / C::CPR;
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_k[C::A_LOADS], b_k[C::B_LOADS];
@@ -482,21 +491,31 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
         b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
     }
 
-    // One global->LDS load of step `step`: q < A_LOADS moves A rows, the
-    // rest B rows.  Instruction q covers 1024 contiguous LDS bytes.
-    auto issue_one = [&](int step, auto qc) G18_INLINE {
-        constexpr int q = decltype(qc)::value;
+    // One global->LDS load q of step `step` into stage S: q < A_LOADS moves
+    // A rows, the rest B rows; each instruction fills 1024 contiguous LDS
+    // bytes.  Rows past the tile's valid rows lie past the buffer range and
+    // read as zero; steps past the end load through the zero-length
+    // resource; with KTAIL, chunks with k >= K get an out-of-range offset.
+    auto issue_one = [&](int step, auto sc, auto qc) G18_INLINE {
+        constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
         const int k0 = step * C::BK;
-        char *stage = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
+        const bool live = step < nk;
+        char *stage = smem + S * C::STAGE_BYTES;
         if constexpr (q < C::A_LOADS) {
-            const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOob;
+            uint32_t off = a_off[q];
+            if constexpr (KTAIL)
+                off = (k0 + a_k[q] < K) ? off : kOob;
             char *dst = stage + (wave + C::NWAVES * q) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)dst, 16, off, 0, 0, GEMM_LOAD_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra : rz, (lds_void *)dst, 16, off,
+                                                     k0 * 2, 0, GEMM_LOAD_AUX);
         } else {
             constexpr int i = q - C::A_LOADS;
-            const uint32_t off = (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : kOob;
+            uint32_t off = b_off[i];
+            if constexpr (KTAIL)
+                off = (k0 + b_k[i] < K) ? off : kOob;
             char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)dst, 16, off, 0, 0, GEMM_LOAD_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rz, (lds_void *)dst, 16, off,
+                                                     k0 * 2, 0, GEMM_LOAD_AUX);
         }
     };
 
@@ -507,34 +526,33 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
         for (int j = 0; j < C::TN; ++j)
             acc[i][j] = typename C::acc_t{};
 
-    const int frow = lane % C::MF, fhi = lane / C::MF;
-    const int a_row0 = wm * C::WTM + frow;
-    const int b_row0 = wn * C::WTN + frow;
-    const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
-
     // Fragments of one K slice (16 wide for 32x32x16, 32 wide for 16x16x32):
     // lane l holds row l % MF of each MF-row block and K chunk
     // CHS * t + l / MF of slice t (the same pattern for A and B, which are
     // both K-contiguous).  Fragment q < TM is A block q, the rest B blocks.
+    // The LDS address of every (stage, slice) is precomputed, so a fragment
+    // read is one ds_read_b128 with an immediate offset.
+    const int frow = lane % C::MF, fhi = lane / C::MF;
+    const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
+    uint32_t a_addr[C::NSTAGE][C::SLICES], b_addr[C::NSTAGE][C::SLICES];
+#pragma unroll
+    for (int st = 0; st < C::NSTAGE; ++st)
+#pragma unroll
+        for (int t = 0; t < C::SLICES; ++t) {
+            const uint32_t ch = (uint32_t)(((C::CHS * t + fhi) ^ fsw) * 16);
+            a_addr[st][t] = st * C::STAGE_BYTES + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
+            b_addr[st][t] = st * C::STAGE_BYTES + C::BM * C::ROW_BYTES +
+                            (wn * C::WTN + frow) * C::ROW_BYTES + ch;
+        }
     f16x8 fr[2][C::TM + C::TN];
-    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], int step, int t, auto qc) G18_INLINE {
-        constexpr int q = decltype(qc)::value;
-        const char *sa = smem + (step % C::NSTAGE) * C::STAGE_BYTES;
-        const int ch = ((C::CHS * t + fhi) ^ fsw) * 16;
+    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
+        constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
         if constexpr (q < C::TM)
-            f[q] = *(const f16x8 *)(sa + (a_row0 + C::MF * q) * C::ROW_BYTES + ch);
+            f[q] = *(const f16x8 *)(smem + a_addr[S][t] + C::MF * q * C::ROW_BYTES);
         else
-            f[q] = *(const f16x8 *)(sa + C::BM * C::ROW_BYTES +
-                                    (b_row0 + C::MF * (q - C::TM)) * C::ROW_BYTES + ch);
+            f[q] = *(const f16x8 *)(smem + b_addr[S][t] + C::MF * (q - C::TM) * C::ROW_BYTES);
     };
 
-    // One slice: MFMA q of TM x TN, each followed by at most one fragment
-    // read for the next slice and, every LSPACE MFMAs, one global->LDS load
-    // (loads l0, l0+1, ... of step lstep).  The scheduling fences keep
-    // exactly this issue order.  With one wavefront per SIMD nothing else
-    // fills an issue gap, and the loads of all four waves share the CU's
-    // load pipe (about 25 cycles per 1 KB load), so the loads are spread
-    // evenly over two slices instead of issued in a burst.
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
     constexpr int LHALF = C::LPS / 2;
     // Spacing of the loads over the NM MFMAs of a slice: one load every
@@ -545,9 +563,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     constexpr int RPG = (NR + NM - 1) / NM;
     static_assert(C::LPS % 2 == 0 && (NM % LHALF == 0 || LHALF % NM == 0),
                   "loads split evenly over two slices");
-    // DO_READ / L0 / DO_LOAD arrive as integral_constants.
+
+    // One slice: MFMA q of TM x TN, each followed by its share of fragment
+    // reads for the next slice (stage RS, slice RT) and of the loads l0, l0+1,
+    // ... of step lstep into stage LS.  The scheduling fences keep exactly
+    // this issue order: with one wavefront per SIMD nothing else fills an
+    // issue gap, and the four waves share the CU's load pipe (about 25 cycles
+    // per 1 KB load), so loads are spread evenly rather than issued in a burst.
     auto slice = [&](const f16x8 (&cur)[C::TM + C::TN], f16x8 (&nxt)[C::TM + C::TN],
-                     int rstep, int rt, auto do_read, int lstep, auto l0, bool do_load) G18_INLINE {
+                     auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
+                     auto l0) G18_INLINE {
         static_for<0, NM>([&](auto qc) G18_INLINE {
             constexpr int q = decltype(qc)::value;
             constexpr int i = q / C::TN, j = q % C::TN;
@@ -559,53 +584,50 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                                                                     acc[i][j], 0, 0, 0);
             if constexpr (decltype(do_read)::value)
                 static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
-                    [&](auto rc) G18_INLINE { read_one(nxt, rstep, rt, rc); });
-            if constexpr (q % LSPACE == 0) {
-                if (do_load)
-                    static_for<0, LPG>([&](auto gc) G18_INLINE {
-                        issue_one(lstep, std::integral_constant<int, decltype(l0)::value +
-                                                                         (q / LSPACE) * LPG +
-                                                                         decltype(gc)::value>{});
-                    });
-            }
+                    [&](auto rc) G18_INLINE { read_one(nxt, rs, rt, rc); });
+            if constexpr (decltype(do_load)::value && q % LSPACE == 0)
+                static_for<0, LPG>([&](auto gc) G18_INLINE {
+                    issue_one(lstep, ls,
+                              std::integral_constant<int, decltype(l0)::value + (q / LSPACE) * LPG +
+                                                              decltype(gc)::value>{});
+                });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
 
-    // Software pipeline over K-steps of BK (SLICES 16-wide slices each).
-    // Fragments are double-buffered: slice t + 1 is read while slice t is
-    // multiplied.  Before the last slice of step u, the workgroup barrier
-    // makes step u + 1 readable and frees step u's stage, which is refilled
-    // with step u + NSTAGE: the first half of its loads during the last
-    // slice of step u, the second half during the first slice of step u + 1
-    // (each step's loads stay contiguous in issue order, so "step u + 1 has
-    // landed" is "at most (NSTAGE - 2) * LPS loads outstanding").  Step
-    // u + 1's first fragments load under the last MFMAs of step u.  The
-    // prefetch is unconditional: steps past the end have every offset out of
-    // range and only write zeros into a stage no one reads again, which
-    // keeps the vmcnt accounting the same in every iteration.
-    const int nk = (K + C::BK - 1) / C::BK;
-    for (int st = 0; st < C::NSTAGE; ++st)
-        static_for<0, C::LPS>([&](auto qc) G18_INLINE { issue_one(st, qc); });
-    wait_vmcnt<C::LPS * (C::NSTAGE - 1)>();
-    lds_barrier();
-    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], 0, 0, qc); });
-
-    static_assert(C::SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
     using T_ = std::true_type;
     using F_ = std::false_type;
     using Z_ = std::integral_constant<int, 0>;
     using H_ = std::integral_constant<int, LHALF>;
-    auto step_body = [&](int u, bool last) G18_INLINE {
+
+    // Software pipeline over K-steps of BK (SLICES slices each).  Fragments
+    // are double-buffered: slice t + 1 is read while slice t is multiplied.
+    // Before the last slice of step u, the workgroup barrier makes step u + 1
+    // readable and frees step u's stage, which is refilled with step
+    // u + NSTAGE: the first half of its loads during the last slice of step u,
+    // the second half during the first slice of step u + 1 (each step's loads
+    // stay contiguous in issue order, so "step u + 1 has landed" is "at most
+    // (NSTAGE - 2) * LPS loads outstanding").  Step u + 1's first fragments
+    // load under the last MFMAs of step u.  Every step, the last included,
+    // runs the same code: refills of steps past the end read zeros into
+    // stages no one reads again, which keeps the vmcnt accounting the same in
+    // every iteration.  S is step u's stage, a compile-time constant: the
+    // step loop is unrolled NSTAGE times.
+    auto step_body = [&](int u, auto sc) G18_INLINE {
+        constexpr int S = decltype(sc)::value;
+        using S_ = std::integral_constant<int, S>;
+        using SP_ = std::integral_constant<int, (S + C::NSTAGE - 1) % C::NSTAGE>;   // step u-1+NSTAGE
+        using SN_ = std::integral_constant<int, (S + 1) % C::NSTAGE>;               // step u+1
         static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
             constexpr int t = decltype(tc)::value;
             constexpr int c = t & 1;
+            using TN_ = std::integral_constant<int, t + 1>;
             if constexpr (t == 0) {
-                // second half of step u - 1 + NSTAGE (issued in the prologue for u = 0)
-                slice(fr[c], fr[c ^ 1], u, t + 1, T_{}, u - 1 + C::NSTAGE, H_{}, u > 0);
+                // second half of step u - 1 + NSTAGE
+                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{});
             } else if constexpr (t + 1 < C::SLICES) {
-                slice(fr[c], fr[c ^ 1], u, t + 1, T_{}, 0, Z_{}, false);
-            } else if (!last) {
+                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{});
+            } else {
                 // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
                 // be outstanding.  The fence keeps the previous slice's MFMAs
                 // ahead of the barrier, where they run while the wave waits.
@@ -613,15 +635,33 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                 wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
                 lds_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                slice(fr[c], fr[c ^ 1], u + 1, 0, T_{}, u + C::NSTAGE, Z_{}, true);
-            } else {
-                slice(fr[c], fr[c ^ 1], 0, 0, F_{}, 0, Z_{}, false);
+                slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{});
             }
         });
     };
-    for (int u = 0; u + 1 < nk; ++u)
-        step_body(u, false);
-    step_body(nk - 1, true);
+    static_assert(C::SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
+
+    // Prologue: steps 0 .. NSTAGE-2 and the first half of step NSTAGE-1 (its
+    // second half is issued by step 0's first slice, like every later step).
+    static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
+        constexpr int st = decltype(sc)::value;
+        static_for<0, (st + 1 < C::NSTAGE ? C::LPS : LHALF)>(
+            [&](auto qc) G18_INLINE { issue_one(st, sc, qc); });
+    });
+    wait_vmcnt<C::LPS * (C::NSTAGE - 2) + LHALF>();
+    lds_barrier();
+    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], Z_{}, Z_{}, qc); });
+
+    // With two stages the step count is rounded up to even instead of
+    // guarding each step (a guard costs registers at the loop back-edge):
+    // an extra step multiplies the all-zero stage that the zero-length
+    // resource filled, and adding +0 leaves every accumulator unchanged (an
+    // fp32 sum that starts at +0 is never -0).
+    for (int u = 0; u < nk; u += C::NSTAGE)
+        static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
+            if (C::NSTAGE <= 2 || u + decltype(sc)::value < nk)
+                step_body(u + decltype(sc)::value, sc);
+        });
     wait_vmcnt<0>();      // drain the zero-filling prefetches before exit
 
     if constexpr (C::MF == 32)
@@ -707,9 +747,14 @@ template <class C>
 void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s)
 {
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C>), dim3((unsigned)(tm * tn)), dim3(C::THREADS),
-                       0, s, (const _Float16 *)A, (const _Float16 *)B, (_Float16 *)D, M, N, K,
-                       tm, tn, vec);
+    if (K % C::BK == 0)
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false>), dim3((unsigned)(tm * tn)),
+                           dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
+                           (_Float16 *)D, M, N, K, tm, tn, vec);
+    else
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true>), dim3((unsigned)(tm * tn)),
+                           dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
+                           (_Float16 *)D, M, N, K, tm, tn, vec);
 }
 
 template <class C, class CDma = void>

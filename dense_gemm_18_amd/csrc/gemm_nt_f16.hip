@@ -52,13 +52,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
-#ifndef GEMM_GROUP_M
-#define GEMM_GROUP_M 4
-#endif
-#ifndef GEMM_TILE_ORDER
-#define GEMM_TILE_ORDER 0
-#endif
-constexpr int kGroupM = GEMM_GROUP_M;   // tile rows per rasterisation group
+constexpr int kGroupM = 4;         // tile rows per rasterisation group
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range
 constexpr int kRsrcFlags = 0x00020000;   // gfx9 buffer descriptor word 3
@@ -73,11 +67,7 @@ __host__ __device__ inline void tile_coord(int64_t wg, int64_t tiles_m, int64_t 
     // a contiguous range of logical ids.
     const int64_t q = total / kXcds, r = total % kXcds;
     const int64_t x = wg % kXcds, i = wg / kXcds;
-#if GEMM_TILE_ORDER == 1
-    const int64_t logical = wg;
-#else
     const int64_t logical = x * q + (x < r ? x : r) + i;
-#endif
     // Grouped rasterisation: kGroupM tile rows at a time, rows fastest.
     const int64_t per_group = (int64_t)kGroupM * tiles_n;
     const int64_t g = logical / per_group;
@@ -348,14 +338,25 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
 #ifndef GEMM_DMA_NSTAGE
 #define GEMM_DMA_NSTAGE 2
 #endif
-#ifndef GEMM_LOAD_AUX
-#define GEMM_LOAD_AUX 0
-#endif
 #ifndef GEMM_DMA_MF
 #define GEMM_DMA_MF 32
 #endif
 
+
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS buffer load of LB bytes per lane.  The size is spelled as a
+// literal in each branch: the builtin's host-side check of a dependent size
+// argument rejects 16 (a gfx950-only width) and silently drops the kernel.
+template <int LB>
+__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, char *dst, uint32_t voff,
+                                         uint32_t soff)
+{
+    if constexpr (LB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
@@ -408,8 +409,12 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_>
 struct DmaCfg {
+    // LB: bytes one lane moves per load: 16 (buffer_load_dwordx4 ... lds,
+    // needs K % 8 == 0 and 16-byte aligned operands) or 4 (buffer_load_dword
+    // ... lds, needs K even and 4-byte aligned operands).
+    static constexpr int LB = LB_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
     static constexpr int BK = BK_;
     // MF = 32: v_mfma_f32_32x32x16_f16; MF = 16: v_mfma_f32_16x16x32_f16.
@@ -422,8 +427,10 @@ struct DmaCfg {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / MF, TN = WTN / MF;
     using acc_t = typename std::conditional<MF == 32, f32x16, f32x4>::type;
-    static constexpr int ROW_BYTES = BK * 2;                 // 64
-    static constexpr int ROWS_PER_INST = 1024 / ROW_BYTES;   // 16 rows per load instruction
+    static constexpr int ROW_BYTES = BK * 2;                 // 64 or 128
+    static constexpr int INST_BYTES = 64 * LB;               // LDS bytes one load instruction fills
+    static constexpr int ROWS_PER_INST = INST_BYTES / ROW_BYTES;
+    static constexpr int LPR = ROW_BYTES / LB;               // lanes per LDS row in one load
     static constexpr int A_LOADS = BM / ROWS_PER_INST / NWAVES;   // per wave per stage
     static constexpr int B_LOADS = BN / ROWS_PER_INST / NWAVES;
     static constexpr int LPS = A_LOADS + B_LOADS;            // vmcnt units per stage
@@ -434,7 +441,10 @@ struct DmaCfg {
     static_assert(BM % (ROWS_PER_INST * NWAVES) == 0 && BN % (ROWS_PER_INST * NWAVES) == 0,
                   "load instructions must split evenly over the waves");
     static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
-    static_assert(NSTAGE >= 2 && LPS * (NSTAGE - 1) < 64, "vmcnt budget");
+    static_assert(LB == 16 || LB == 4, "16- or 4-byte loads");
+    static_assert(ROWS_PER_INST >= 1, "a load covers whole LDS rows");
+    // The largest vmcnt the pipeline waits on (prologue) must be encodable.
+    static_assert(NSTAGE >= 2 && LPS * (NSTAGE - 2) + LPS / 2 < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
@@ -473,22 +483,26 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // wave covers rows ROWS_PER_INST * (wave + NWAVES * i) and up.  The
     // vector offsets carry rows and chunks only; a step's K offset travels in
     // the scalar offset, so a full step issues its loads with no VALU work.
-    const int slot_row = lane / C::CPR;
+    // With LB = 4 a lane moves one 4-byte quarter of a chunk (intra-chunk
+    // byte offset `sub`).
+    const int slot_row = lane / C::LPR;
+    const int slot_byte = (lane % C::LPR) * C::LB;
+    const int sub = slot_byte % 16;
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_k[C::A_LOADS], b_k[C::B_LOADS];
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
         const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (lane % C::CPR) ^ swz_row<C::BK, C::MF>(row);
-        a_k[i] = gch * 8;
-        a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
+        const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
+        a_k[i] = gch * 8 + sub / 2;
+        a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
         const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (lane % C::CPR) ^ swz_row<C::BK, C::MF>(row);
-        b_k[i] = gch * 8;
-        b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)gch * 16u;
+        const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
+        b_k[i] = gch * 8 + sub / 2;
+        b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
     }
 
     // One global->LDS load q of step `step` into stage S: q < A_LOADS moves
@@ -505,17 +519,15 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
             uint32_t off = a_off[q];
             if constexpr (KTAIL)
                 off = (k0 + a_k[q] < K) ? off : kOob;
-            char *dst = stage + (wave + C::NWAVES * q) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra : rz, (lds_void *)dst, 16, off,
-                                                     k0 * 2, 0, GEMM_LOAD_AUX);
+            char *dst = stage + (wave + C::NWAVES * q) * C::INST_BYTES;
+            load_lds<C::LB>(live ? ra : rz, dst, off, k0 * 2);
         } else {
             constexpr int i = q - C::A_LOADS;
             uint32_t off = b_off[i];
             if constexpr (KTAIL)
                 off = (k0 + b_k[i] < K) ? off : kOob;
-            char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rz, (lds_void *)dst, 16, off,
-                                                     k0 * 2, 0, GEMM_LOAD_AUX);
+            char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * C::INST_BYTES;
+            load_lds<C::LB>(live ? rb : rz, dst, off, k0 * 2);
         }
     };
 
@@ -684,12 +696,17 @@ __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
 using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
 using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
-using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE, GEMM_DMA_MF>;
+using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE, GEMM_DMA_MF, 16>;
 // 128 x 128: 4 waves of 64 x 64, four 32 KB stages.
-using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 32>;
+using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 32, 16>;
 // 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
 // eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
-using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16>;
+using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16>;
+// 4-byte loads (K even, operands 4-byte aligned): four times as many load
+// instructions per step, so fewer stages keep the waits encodable.
+using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 32, 4>;
+using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4>;
+using BigDma4 = DmaCfg<256, 256, 2, 2, 64, 2, 32, 4>;
 
 enum class Tile { kBig, kMid, kThin };
 
@@ -757,23 +774,23 @@ void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int 
                            (_Float16 *)D, M, N, K, tm, tn, vec);
 }
 
-template <class C, class CDma = void>
+// CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
+// 4-byte loads; C: the register-staged kernel for whatever remains (odd K or
+// 2-byte aligned operands).
+template <class C, class CDma, class CDma4>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if constexpr (!std::is_void<CDma>::value) {
-        if (K % 8 == 0 && (ab & 15u) == 0) {
-            launch_dma<CDma>(A, B, D, M, N, K, vec, s);
-            return;
-        }
+    if (K % 8 == 0 && (ab & 15u) == 0) {
+        launch_dma<CDma>(A, B, D, M, N, K, vec, s);
+        return;
     }
-    if (K % 8 == 0 && (ab & 15u) == 0)
-        launch_cfg<C, 16>(A, B, D, M, N, K, vec, s);
-    else if (K % 2 == 0 && (ab & 3u) == 0)
-        launch_cfg<C, 4>(A, B, D, M, N, K, vec, s);
-    else
-        launch_cfg<C, 2>(A, B, D, M, N, K, vec, s);
+    if (K % 2 == 0 && (ab & 3u) == 0) {
+        launch_dma<CDma4>(A, B, D, M, N, K, vec, s);
+        return;
+    }
+    launch_cfg<C, 2>(A, B, D, M, N, K, vec, s);
 }
 
 } // namespace
@@ -795,9 +812,9 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                            (uint16_t *)D, count);
     } else {
         switch (choose_tile(M, N)) {
-        case Tile::kBig: launch_tile<Big, BigDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        case Tile::kMid: launch_tile<Mid, MidDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        default: launch_tile<Thin, ThinDma>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kBig: launch_tile<Big, BigDma, BigDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kMid: launch_tile<Mid, MidDma, MidDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        default: launch_tile<Thin, ThinDma, ThinDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         }
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;

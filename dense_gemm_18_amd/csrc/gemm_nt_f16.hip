@@ -17,22 +17,24 @@
 //     blocks; page 1 ("内核 4：生产级调优") notes that a larger M tile
 //     improves L2 reuse of B.
 //   * Global -> LDS staging: A and B are both K-contiguous, so one loader
-//     serves both.  Each lane moves 16-byte chunks (8 fp16 along K) with
-//     buffer loads; 8 lanes cover one 128-byte row of a K-step, so the
-//     accesses are fully coalesced (page 1, "内核 1：共享内存分块", shows
+//     serves both.  Each lane moves 16-byte chunks (8 fp16 along K), or
+//     4-byte pieces of them when K is not a multiple of 8, with buffer loads
+//     that write LDS directly; 8 lanes cover one 128-byte row of a K-step, so
+//     the accesses are fully coalesced (page 1, "内核 1：共享内存分块", shows
 //     the cooperative coalesced tile copy).  The buffer resource of each
 //     workgroup spans only its valid rows, so rows past M or N read as zero
 //     in hardware; K tails are masked per load.
 //   * LDS layout: rows of 64 fp16 (128 B = eight 16-byte chunks), chunk index
-//     XOR-swizzled by the row so that both the row-wise writer and the
-//     column-wise MFMA fragment reader are free of bank conflicts (page 1,
-//     "为什么 swizzle 重要", explains the conflict the swizzle removes).
-//     Two stages: the loads for K-step k+1 are in flight while the MFMAs of
-//     step k run (page 1, "内核 4", double buffering with STAGES = 2).
-//   * MFMA: v_mfma_f32_32x32x16_f16, fp32 accumulators in registers.  The B
-//     tile is fed as the instruction's first operand and the A tile as its
-//     second, so each lane's accumulators hold 4 consecutive columns n of D
-//     for one row m and the epilogue writes 8-byte vectors.
+//     XOR-swizzled by the row so that the MFMA fragment reader is free of
+//     bank conflicts (page 1, "为什么 swizzle 重要", explains the conflict
+//     the swizzle removes).  A ring of stages keeps the loads for later
+//     K-steps in flight while the MFMAs of the current one run (page 1,
+//     "内核 4", double buffering with STAGES = 2).
+//   * MFMA: v_mfma_f32_16x16x32_f16 (32x32x16 in two configurations), fp32
+//     accumulators in registers.  The B tile is fed as the instruction's
+//     first operand and the A tile as its second, so each lane's
+//     accumulators hold 4 consecutive columns n of D for one row m and the
+//     epilogue writes 8-byte vectors.
 //   * Epilogue: fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even),
 //     masked at the M and N edges.
 #include <hip/hip_runtime.h>
@@ -332,16 +334,6 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
 // global chunk chunk ^ swz_row(row) of that row.  Both swizzles were chosen
 // by measuring SQ_LDS_BANK_CONFLICT for the MFMA fragment read pattern
 // (32 rows x 16 bytes per half wave) on gfx950: zero conflicts.
-#ifndef GEMM_DMA_BK
-#define GEMM_DMA_BK 64
-#endif
-#ifndef GEMM_DMA_NSTAGE
-#define GEMM_DMA_NSTAGE 2
-#endif
-#ifndef GEMM_DMA_MF
-#define GEMM_DMA_MF 32
-#endif
-
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -409,12 +401,17 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_, bool SPLIT_>
 struct DmaCfg {
     // LB: bytes one lane moves per load: 16 (buffer_load_dwordx4 ... lds,
     // needs K % 8 == 0 and 16-byte aligned operands) or 4 (buffer_load_dword
     // ... lds, needs K even and 4-byte aligned operands).
     static constexpr int LB = LB_;
+    // SPLIT: a step's loads are issued half in the slice after the barrier
+    // and half in the next step's first slice; otherwise all of them in the
+    // slice after the barrier (which gives every load the longest time to
+    // land when a step has only two slices).
+    static constexpr bool SPLIT = SPLIT_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
     static constexpr int BK = BK_;
     // MF = 32: v_mfma_f32_32x32x16_f16; MF = 16: v_mfma_f32_16x16x32_f16.
@@ -445,6 +442,8 @@ struct DmaCfg {
     static_assert(ROWS_PER_INST >= 1, "a load covers whole LDS rows");
     // The largest vmcnt the pipeline waits on (prologue) must be encodable.
     static_assert(NSTAGE >= 2 && LPS * (NSTAGE - 2) + LPS / 2 < 64, "vmcnt budget");
+    static_assert(SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
+    static_assert(SPLIT || LPS * (NSTAGE - 1) < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
@@ -567,14 +566,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
 
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
     constexpr int LHALF = C::LPS / 2;
+    // Loads issued in one slice: half a step's or a whole step's.
+    constexpr int LSL = C::SPLIT ? LHALF : C::LPS;
     // Spacing of the loads over the NM MFMAs of a slice: one load every
     // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
     // than MFMAs (small tiles); the same for fragment reads (RPG).
-    constexpr int LSPACE = NM >= LHALF ? NM / LHALF : 1;
-    constexpr int LPG = NM >= LHALF ? 1 : LHALF / NM;
+    constexpr int LSPACE = NM >= LSL ? NM / LSL : 1;
+    constexpr int LPG = NM >= LSL ? 1 : LSL / NM;
     constexpr int RPG = (NR + NM - 1) / NM;
-    static_assert(C::LPS % 2 == 0 && (NM % LHALF == 0 || LHALF % NM == 0),
-                  "loads split evenly over two slices");
+    static_assert(C::LPS % 2 == 0 && (NM % LSL == 0 || LSL % NM == 0),
+                  "loads split evenly over the slices that issue them");
 
     // One slice: MFMA q of TM x TN, each followed by its share of fragment
     // reads for the next slice (stage RS, slice RT) and of the loads l0, l0+1,
@@ -616,10 +617,11 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // are double-buffered: slice t + 1 is read while slice t is multiplied.
     // Before the last slice of step u, the workgroup barrier makes step u + 1
     // readable and frees step u's stage, which is refilled with step
-    // u + NSTAGE: the first half of its loads during the last slice of step u,
-    // the second half during the first slice of step u + 1 (each step's loads
-    // stay contiguous in issue order, so "step u + 1 has landed" is "at most
-    // (NSTAGE - 2) * LPS loads outstanding").  Step u + 1's first fragments
+    // u + NSTAGE: all of its loads during the last slice of step u, or with
+    // SPLIT the first half there and the second half during the first slice
+    // of step u + 1 (each step's loads stay contiguous in issue order, so
+    // "step u + 1 has landed" is "at most (NSTAGE - 2) * LPS loads
+    // outstanding").  Step u + 1's first fragments
     // load under the last MFMAs of step u.  Every step, the last included,
     // runs the same code: refills of steps past the end read zeros into
     // stages no one reads again, which keeps the vmcnt accounting the same in
@@ -634,7 +636,7 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
             constexpr int t = decltype(tc)::value;
             constexpr int c = t & 1;
             using TN_ = std::integral_constant<int, t + 1>;
-            if constexpr (t == 0) {
+            if constexpr (t == 0 && C::SPLIT) {
                 // second half of step u - 1 + NSTAGE
                 slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{});
             } else if constexpr (t + 1 < C::SLICES) {
@@ -651,16 +653,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
             }
         });
     };
-    static_assert(C::SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
-
-    // Prologue: steps 0 .. NSTAGE-2 and the first half of step NSTAGE-1 (its
-    // second half is issued by step 0's first slice, like every later step).
+    // Prologue: steps 0 .. NSTAGE-2 and, with split loads, the first half of
+    // step NSTAGE-1 (its second half is issued by step 0's first slice, like
+    // every later step); otherwise all of step NSTAGE-1 too.
+    constexpr int PRO_LAST = C::SPLIT ? LHALF : C::LPS;
     static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
         constexpr int st = decltype(sc)::value;
-        static_for<0, (st + 1 < C::NSTAGE ? C::LPS : LHALF)>(
+        static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
             [&](auto qc) G18_INLINE { issue_one(st, sc, qc); });
     });
-    wait_vmcnt<C::LPS * (C::NSTAGE - 2) + LHALF>();
+    wait_vmcnt<C::LPS * (C::NSTAGE - 2) + PRO_LAST>();
     lds_barrier();
     static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], Z_{}, Z_{}, qc); });
 
@@ -696,17 +698,21 @@ __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
 using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
 using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
-using BigDma = DmaCfg<256, 256, 2, 2, GEMM_DMA_BK, GEMM_DMA_NSTAGE, GEMM_DMA_MF, 16>;
-// 128 x 128: 4 waves of 64 x 64, four 32 KB stages.
-using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 32, 16>;
+// 256 x 256: 4 waves of 128 x 128 on 16x16x32 MFMAs, two 64 KB stages, each
+// step's loads issued right after the barrier.  16x16x32 keeps half as many
+// accumulator registers busy per FLOP as 32x32x16, so the part draws less
+// power and holds a higher clock under its power limit.
+using BigDma = DmaCfg<256, 256, 2, 2, 64, 2, 16, 16, false>;
+// 128 x 128: 4 waves of 64 x 64 on 16x16x32 MFMAs, four 32 KB stages.
+using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
 // 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
 // eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
-using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16>;
+using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
 // 4-byte loads (K even, operands 4-byte aligned): four times as many load
 // instructions per step, so fewer stages keep the waits encodable.
-using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 32, 4>;
-using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4>;
-using BigDma4 = DmaCfg<256, 256, 2, 2, 64, 2, 32, 4>;
+using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 16, 4, true>;
+using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4, false>;
+using BigDma4 = DmaCfg<256, 256, 2, 2, 64, 2, 32, 4, true>;
 
 enum class Tile { kBig, kMid, kThin };
 

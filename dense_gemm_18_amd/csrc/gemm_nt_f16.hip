@@ -718,13 +718,25 @@ enum class Tile { kBig, kMid, kThin };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Tile choose_tile(int64_t M, int64_t N)
+// Tile choice: the one with the smaller (waves of workgroups) x (time of one
+// tile), one workgroup per CU on MI355X's 256 CUs.  Tile times relative to a
+// 128 x 128 x K tile at the big tile's rate, measured on MI355X: a 256 x 256
+// tile costs 4.0 and a 128 x 128 tile 1.4 with 16-byte loads (the big tile's
+// pipeline is ~40 % faster per FLOP); with 4-byte loads (K % 8 != 0) 6.6 and
+// 2.25.  So 3000 x 5000 runs one wave of 240 big tiles rather than four of
+// 960 mid tiles, and 2048 x 2048 runs 256 mid tiles rather than 64 big ones.
+// The choice assumes operands aligned to 16 bytes.
+constexpr int kCUs = 256;
+
+Tile choose_tile(int64_t M, int64_t N, int64_t K)
 {
-    if (cdiv(M, 256) * cdiv(N, 256) >= 256)
-        return Tile::kBig;
     if (M <= 64 || N <= 64)
         return Tile::kThin;
-    return Tile::kMid;
+    const bool wide = K % 8 == 0;
+    const double big_tile = wide ? 4.0 : 6.6, mid_tile = wide ? 1.4 : 2.25;
+    const int64_t big_waves = cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs);
+    const int64_t mid_waves = cdiv(cdiv(M, 128) * cdiv(N, 128), kCUs);
+    return big_waves * big_tile <= mid_waves * mid_tile ? Tile::kBig : Tile::kMid;
 }
 
 void tile_dims(Tile t, int &bm, int &bn)
@@ -817,7 +829,7 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (uint16_t *)D, count);
     } else {
-        switch (choose_tile(M, N)) {
+        switch (choose_tile(M, N, K)) {
         case Tile::kBig: launch_tile<Big, BigDma, BigDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         case Tile::kMid: launch_tile<Mid, MidDma, MidDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         default: launch_tile<Thin, ThinDma, ThinDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
@@ -840,7 +852,7 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk,
 {
     if (M < 0 || N < 0 || K < 0 || !bm || !bn || !bk || !workgroups)
         return GEMM_EINVAL;
-    tile_dims(choose_tile(M, N), *bm, *bn);
+    tile_dims(choose_tile(M, N, K), *bm, *bn);
     *bk = kBK;
     *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : cdiv(M, *bm) * cdiv(N, *bn);
     return GEMM_OK;

@@ -74,9 +74,10 @@ const char *gemm_nt_f16_strerror(int code);
 
 /*
  * Host-only introspection (no HIP call): the output tile BM x BN and the K
- * step BK that gemm_nt_f16 uses for an M x N x K problem, and the number of
- * workgroups it launches.  Tests use it to pick rows and columns at tile
- * edges.  Returns GEMM_OK or GEMM_EINVAL (negative size or NULL output).
+ * step BK that gemm_nt_f16 uses for an M x N x K problem with operands
+ * aligned to 16 bytes, and the number of workgroups it launches.  Tests use
+ * it to pick rows and columns at tile edges.  Returns GEMM_OK or GEMM_EINVAL
+ * (negative size or NULL output).
  */
 int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
                      int *bm, int *bn, int *bk, int64_t *workgroups);

@@ -88,6 +88,23 @@ def test_tile_introspection():
         binding.gemm_nt_f16_tile(-1, 5, 5)
 
 
+@pytest.mark.parametrize("M,N,K,bm", [
+    (8192, 8192, 8192, 256),    # 4 full waves of big tiles
+    (3000, 5000, 2048, 256),    # 240 big tiles (1 wave) beat 960 mid tiles (4 waves)
+    (3000, 5000, 2050, 256),    # the same with 4-byte loads
+    (3072, 3072, 3072, 256),    # 144 big tiles (1 wave) vs 576 mid tiles (3 waves)
+    (2048, 2048, 8192, 128),    # 64 big tiles would leave 3/4 of the CUs idle
+    (2560, 2560, 4096, 128),    # 100 big tiles vs 400 mid tiles (2 waves)
+    (2048, 2048, 8194, 128),
+    (1024, 1024, 1024, 128),
+    (64, 16384, 8192, 64),      # M <= 64: the thin tile
+    (16384, 33, 128, 64),
+])
+def test_tile_choice(M, N, K, bm):
+    # The choice minimises (waves of workgroups on 256 CUs) x (tile time).
+    assert binding.gemm_nt_f16_tile(M, N, K)[0] == bm
+
+
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (1, 7), (7, 1), (3, 5), (8, 8), (32, 32),
                                               (12, 20), (15, 20), (13, 17), (64, 43), (1, 256),
                                               (256, 1), (9, 31)])

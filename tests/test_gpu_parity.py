@@ -121,12 +121,16 @@ def test_mn_sweep(M, N):
     assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), f"{M}x{N}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1100, 1100, 96), (800, 2300, 72), (2000, 700, 136)])
-def test_big_tile_tails(M, N, K):
-    # shapes large enough for the 256 x 256 tile, with ragged M, N and K
+@pytest.mark.parametrize("M,N,K,bm", [(2900, 4100, 136, 256), (3000, 4999, 72, 256),
+                                    (2999, 5000, 98, 256), (1100, 1100, 96, 128),
+                                    (800, 2300, 72, 128), (2000, 700, 130, 128)])
+def test_tile_tails(M, N, K, bm):
+    # ragged M, N and K on the 256 x 256 and the 128 x 128 tiles (K = 98 and
+    # 130 take the 4-byte loads)
     A, B = wl.integer_free(3000 + K, M, N, K)
-    bm, bn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
-    note(f"big-tile tails {M}x{N}x{K} tile {bm}x{bn}")
+    tbm, tbn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
+    assert tbm == bm
+    note(f"tile tails {M}x{N}x{K} tile {tbm}x{tbn}")
     assert_bitexact(run_gemm(A, B), oracle.gemm_nt_f16(A, B), f"{M}x{N}x{K}")
 
 

@@ -18,7 +18,8 @@ GEMM_ELAUNCH = 2
 GEMM_MAX_K = 4194303
 
 # Every symbol the header declares.
-EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord")
+EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
+           "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile", "gemm_nt_f16_ws_items")
 
 
 class GemmError(RuntimeError):
@@ -40,6 +41,12 @@ def lib():
         raise RuntimeError(
             f"{_LIB_PATH} is missing: build it first with "
             "`python -c 'import __graft_entry__ as g; g.build()'`")
+    # One HIP runtime per process: PyTorch's bundled libamdhip64 must be the
+    # one loaded.  The library asks for libamdhip64.so.7, which resolves to
+    # an already-loaded runtime of that soname; loaded first, it would pull
+    # in the system runtime, and PyTorch (which asks for libamdhip64.so)
+    # would then load a second one that finds no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(str(_LIB_PATH))
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.gemm_nt_f16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -52,6 +59,14 @@ def lib():
     L.gemm_nt_f16_tile.restype = ctypes.c_int
     L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
     L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
+    L.gemm_nt_f16_ws.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    L.gemm_nt_f16_ws.restype = ctypes.c_int
+    L.gemm_nt_f16_ws_size.argtypes = [i64, i64, i64]
+    L.gemm_nt_f16_ws_size.restype = i64
+    L.gemm_nt_f16_ws_tile.argtypes = [i64, i64, i64, ip, ip, lp, lp]
+    L.gemm_nt_f16_ws_tile.restype = ctypes.c_int
+    L.gemm_nt_f16_ws_items.argtypes = [i64, i64, i64, i64, lp, i64, lp]
+    L.gemm_nt_f16_ws_items.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -85,6 +100,41 @@ def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_tile_coord")
     return tm.value, tn.value
+
+
+def gemm_nt_f16_ws(A: int, B: int, D: int, M: int, N: int, K: int, workspace: int,
+                   ws_bytes: int, stream: int = 0) -> int:
+    """Raw call of the stream-K form; returns the C return code."""
+    return lib().gemm_nt_f16_ws(A or None, B or None, D or None, M, N, K, workspace or None,
+                                ws_bytes, stream or None)
+
+
+def gemm_nt_f16_ws_size(M: int, N: int, K: int) -> int:
+    return lib().gemm_nt_f16_ws_size(M, N, K)
+
+
+def gemm_nt_f16_ws_tile(M: int, N: int, K: int):
+    """(BM, BN, workgroups, stream-K tiles) of the stream-K form's plan."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    wg, skt = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().gemm_nt_f16_ws_tile(M, N, K, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(wg),
+                                   ctypes.byref(skt))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_ws_tile")
+    return bm.value, bn.value, wg.value, skt.value
+
+
+def gemm_nt_f16_ws_items(M: int, N: int, K: int, wg: int):
+    """Work items (tile, s0, s1, w_first, w_last) of workgroup ``wg``."""
+    count = ctypes.c_int64()
+    rc = lib().gemm_nt_f16_ws_items(M, N, K, wg, None, 0, ctypes.byref(count))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_ws_items")
+    buf = (ctypes.c_int64 * (5 * max(count.value, 1)))()
+    rc = lib().gemm_nt_f16_ws_items(M, N, K, wg, buf, count.value, ctypes.byref(count))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_ws_items")
+    return [tuple(buf[5 * i:5 * i + 5]) for i in range(count.value)]
 
 
 # ---- tensor-level convenience ----------------------------------------------

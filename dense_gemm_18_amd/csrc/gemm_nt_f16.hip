@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_nt_f16.h"
@@ -139,27 +140,27 @@ __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t 
 // so each group of four accumulators is four consecutive columns of one row.
 // fp32 -> fp16 uses v_cvt_f16_f32 (round to nearest even); stores are masked
 // at the M and N edges.  vec_store: D is 8-byte aligned and N % 4 == 0.
-template <int TM, int TN>
-__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 *__restrict__ D,
-                                          int M, int N, int mbase, int nbase, int lane,
-                                          int vec_store)
+template <int TM, int TN, class Get>
+__device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, int M, int N,
+                                             int mbase, int nbase, int lane, int vec_store)
 {
     const int frow = lane & 31, fhi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = mbase + 32 * i + frow;
-        if (m >= M)
-            continue;
         _Float16 *drow = D + (int64_t)m * N;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+            const f32x16 v = get(i, j);
+            if (m >= M)
+                continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + 32 * j + 8 * g + 4 * fhi;
                 f16x4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)acc[i][j][4 * g + r];
+                    h[r] = (_Float16)v[4 * g + r];
                 if (vec_store) {
                     if (n < N)
                         *(f16x4 *)(drow + n) = h;
@@ -174,28 +175,37 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 
     }
 }
 
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 *__restrict__ D,
+                                          int M, int N, int mbase, int nbase, int lane,
+                                          int vec_store)
+{
+    store_blocks<TM, TN>([&](int i, int j) { return acc[i][j]; }, D, M, N, mbase, nbase, lane,
+                         vec_store);
+}
+
 // Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
 // accumulator r of block (i, j) holds D[m][n] for
 //   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
-template <int TM, int TN>
-__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16 *__restrict__ D,
-                                            int M, int N, int mbase, int nbase, int lane,
-                                            int vec_store)
+template <int TM, int TN, class Get>
+__device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D, int M, int N,
+                                               int mbase, int nbase, int lane, int vec_store)
 {
     const int frow = lane & 15, fq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = mbase + 16 * i + frow;
-        if (m >= M)
-            continue;
         _Float16 *drow = D + (int64_t)m * N;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+            const f32x4 v = get(i, j);
+            if (m >= M)
+                continue;
             const int n = nbase + 16 * j + 4 * fq;
             f16x4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h[r] = (_Float16)acc[i][j][r];
+                h[r] = (_Float16)v[r];
             if (vec_store) {
                 if (n < N)
                     *(f16x4 *)(drow + n) = h;
@@ -207,6 +217,15 @@ __device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16
             }
         }
     }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16 *__restrict__ D,
+                                            int M, int N, int mbase, int nbase, int lane,
+                                            int vec_store)
+{
+    store_blocks16<TM, TN>([&](int i, int j) { return acc[i][j]; }, D, M, N, mbase, nbase, lane,
+                           vec_store);
 }
 
 template <class C, int LOADB>
@@ -447,34 +466,117 @@ struct DmaCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 };
 
+// Stream-K work split of a persistent grid of P workgroups (one per CU, all
+// resident at once).  Tiles [0, dp_tiles) are whole tiles, dealt round-robin
+// (dp_tiles is a multiple of P, so every workgroup gets as many).  The K-steps
+// of tiles [dp_tiles, dp_tiles + sk_tiles), in tile-major order, are split
+// into P contiguous ranges: workgroup w gets base + (w < extra) of them.
+// A tile split over several workgroups is finished by its owner, the one that
+// runs the tile's first step: every other contributor starts its range inside
+// that tile, writes its fp32 partial sums to its own slot and raises its flag;
+// the owner adds the slots in ascending workgroup order (so results do not
+// depend on timing), rounds once to fp16, and lowers the flags again.
+struct SkPlan {
+    int dp_tiles, sk_tiles;
+    int base, extra;
+    uint32_t *flags;      // P words; zero before the call, zero after it
+    float *partials;      // P slots of BM * BN floats
+};
+
+// One work item of workgroup w: K-steps [s0, s1) of `tile`.  s0 > 0: w is a
+// contributor to that tile.  Otherwise w writes the tile, adding the partial
+// sums of workgroups w_first .. w_last (none when w_first > w_last).
+struct SkItem {
+    int tile, s0, s1, w_first, w_last;
+};
+
+// Walks workgroup w's items: its whole tiles w, w + P, ... below dp_tiles,
+// then the pieces of its stream-K range, each ending at a tile boundary or
+// at the range end.  Host and device run the same code (the host to test it).
+struct SkCursor {
+    int t_dp, i, iend;
+};
+
+__host__ __device__ inline int sk_wg_of(const SkPlan &sk, int i)   // the workgroup whose range holds step i
+{
+    const int cut = sk.extra * (sk.base + 1);
+    return i < cut ? i / (sk.base + 1) : sk.extra + (sk.base ? (i - cut) / sk.base : 0);
+}
+
+__host__ __device__ inline SkCursor sk_begin(const SkPlan &sk, int w)
+{
+    const int i = w * sk.base + (w < sk.extra ? w : sk.extra);
+    return SkCursor{w, i, i + sk.base + (w < sk.extra ? 1 : 0)};
+}
+
+__host__ __device__ inline bool sk_next(const SkPlan &sk, int nk, int P, SkCursor &c, SkItem &it)
+{
+    it.w_first = 1;
+    it.w_last = 0;
+    if (c.t_dp < sk.dp_tiles) {
+        it.tile = c.t_dp;
+        it.s0 = 0;
+        it.s1 = nk;
+        c.t_dp += P;
+        return true;
+    }
+    if (c.i >= c.iend)
+        return false;
+    const int j = c.i / nk;
+    it.s0 = c.i - j * nk;
+    it.s1 = it.s0 + (c.iend - c.i) < nk ? it.s0 + (c.iend - c.i) : nk;
+    it.tile = sk.dp_tiles + j;
+    c.i += it.s1 - it.s0;
+    if (it.s0 == 0 && it.s1 < nk) {
+        it.w_first = sk_wg_of(sk, j * nk + it.s1);
+        it.w_last = sk_wg_of(sk, j * nk + nk - 1);
+    }
+    return true;
+}
+
+// Polls of a contributor's flag before an owner gives up (~5 s at 1.6 GHz):
+// the tile is then written as NaN and the kernel still ends.
+constexpr int kSpinLimit = 1 << 24;
+
 // KTAIL: K % BK != 0, so the last step is partial and every load carries a
-// per-lane K mask; otherwise loads carry no mask at all.
-template <class C, bool KTAIL>
+// per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
+// stream-K form; otherwise one workgroup per tile.
+template <class C, bool KTAIL, bool SK>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                        _Float16 *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n,
-                       int vec_store)
+                       int vec_store, SkPlan sk)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+    __shared__ int sk_ok;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
     const int wm = wave % C::WM, wn = wave / C::WM;
 
-    int64_t tm64, tn64;
-    tile_coord(blockIdx.x, tiles_m, tiles_n, tm64, tn64);
-    const int m0 = (int)tm64 * C::BM, n0 = (int)tn64 * C::BN;
-    const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + (int64_t)m0 * K), (short)0, rows_a * K * 2, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(B + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcFlags);
+    // The current work item: tile origin (m0, n0), buffer resources spanning
+    // the tile's valid rows of A and B, and its K-steps [s0, s0 + n).
+    int m0 = 0, n0 = 0, kb = 0, n = 0;
+    __amdgpu_buffer_rsrc_t ra, rb;
     // Zero-length resource: every load through it reads zero.  Steps past the
-    // end of K use it, chosen per step in scalar registers.
+    // end of the item use it, chosen per step in scalar registers.
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void *)A, (short)0, 0, kRsrcFlags);
     const int nk = (K + C::BK - 1) / C::BK;
+    auto set_item = [&](int tile, int s0, int s1) G18_INLINE {
+        int64_t tm64, tn64;
+        tile_coord(tile, tiles_m, tiles_n, tm64, tn64);
+        m0 = (int)tm64 * C::BM;
+        n0 = (int)tn64 * C::BN;
+        const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
+        ra = __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0,
+                                               rows_a * K * 2, kRsrcFlags);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0,
+                                               rows_b * K * 2, kRsrcFlags);
+        kb = s0 * C::BK;
+        n = s1 - s0;
+    };
 
     // This lane's part of each load instruction: LDS slot `lane` of a block
     // of ROWS_PER_INST rows is row lane / CPR, chunk lane % CPR; it fetches
@@ -484,25 +586,32 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // the scalar offset, so a full step issues its loads with no VALU work.
     // With LB = 4 a lane moves one 4-byte quarter of a chunk (intra-chunk
     // byte offset `sub`).
-    const int slot_row = lane / C::LPR;
-    const int slot_byte = (lane % C::LPR) * C::LB;
-    const int sub = slot_byte % 16;
+    //
+    // These per-lane values, and the fragment addresses below, are set up
+    // per work item from `ln`, a copy of the lane id that the compiler must
+    // treat as changing: otherwise it keeps them live across the persistent
+    // loop's epilogues, where the 256 accumulators leave no registers free.
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_k[C::A_LOADS], b_k[C::B_LOADS];
+    auto setup_loads = [&](int ln) G18_INLINE {
+        const int slot_row = ln / C::LPR;
+        const int slot_byte = (ln % C::LPR) * C::LB;
+        const int sub = slot_byte % 16;
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-        const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-        a_k[i] = gch * 8 + sub / 2;
-        a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
-    }
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
+            const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
+            a_k[i] = gch * 8 + sub / 2;
+            a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
+        }
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-        const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-        const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-        b_k[i] = gch * 8 + sub / 2;
-        b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
-    }
+        for (int i = 0; i < C::B_LOADS; ++i) {
+            const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
+            const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
+            b_k[i] = gch * 8 + sub / 2;
+            b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
+        }
+    };
 
     // One global->LDS load q of step `step` into stage S: q < A_LOADS moves
     // A rows, the rest B rows; each instruction fills 1024 contiguous LDS
@@ -511,8 +620,8 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // resource; with KTAIL, chunks with k >= K get an out-of-range offset.
     auto issue_one = [&](int step, auto sc, auto qc) G18_INLINE {
         constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
-        const int k0 = step * C::BK;
-        const bool live = step < nk;
+        const int k0 = kb + step * C::BK;
+        const bool live = step < n;
         char *stage = smem + S * C::STAGE_BYTES;
         if constexpr (q < C::A_LOADS) {
             uint32_t off = a_off[q];
@@ -531,11 +640,6 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     };
 
     typename C::acc_t acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = typename C::acc_t{};
 
     // Fragments of one K slice (16 wide for 32x32x16, 32 wide for 16x16x32):
     // lane l holds row l % MF of each MF-row block and K chunk
@@ -543,18 +647,20 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // both K-contiguous).  Fragment q < TM is A block q, the rest B blocks.
     // The LDS address of every (stage, slice) is precomputed, so a fragment
     // read is one ds_read_b128 with an immediate offset.
-    const int frow = lane % C::MF, fhi = lane / C::MF;
-    const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
     uint32_t a_addr[C::NSTAGE][C::SLICES], b_addr[C::NSTAGE][C::SLICES];
+    auto setup_reads = [&](int ln) G18_INLINE {
+        const int frow = ln % C::MF, fhi = ln / C::MF;
+        const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
 #pragma unroll
-    for (int st = 0; st < C::NSTAGE; ++st)
+        for (int st = 0; st < C::NSTAGE; ++st)
 #pragma unroll
-        for (int t = 0; t < C::SLICES; ++t) {
-            const uint32_t ch = (uint32_t)(((C::CHS * t + fhi) ^ fsw) * 16);
-            a_addr[st][t] = st * C::STAGE_BYTES + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
-            b_addr[st][t] = st * C::STAGE_BYTES + C::BM * C::ROW_BYTES +
-                            (wn * C::WTN + frow) * C::ROW_BYTES + ch;
-        }
+            for (int t = 0; t < C::SLICES; ++t) {
+                const uint32_t ch = (uint32_t)(((C::CHS * t + fhi) ^ fsw) * 16);
+                a_addr[st][t] = st * C::STAGE_BYTES + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
+                b_addr[st][t] = st * C::STAGE_BYTES + C::BM * C::ROW_BYTES +
+                                (wn * C::WTN + frow) * C::ROW_BYTES + ch;
+            }
+    };
     f16x8 fr[2][C::TM + C::TN];
     auto read_one = [&](f16x8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
         constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
@@ -653,6 +759,19 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
             }
         });
     };
+    // acc = the sum over the current item's K-steps (steps are counted from
+    // the item's first one).
+    auto run_item = [&]() G18_INLINE {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    setup_loads(ln);
+    setup_reads(ln);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = typename C::acc_t{};
+
     // Prologue: steps 0 .. NSTAGE-2 and, with split loads, the first half of
     // step NSTAGE-1 (its second half is issued by step 0's first slice, like
     // every later step); otherwise all of step NSTAGE-1 too.
@@ -671,18 +790,136 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // an extra step multiplies the all-zero stage that the zero-length
     // resource filled, and adding +0 leaves every accumulator unchanged (an
     // fp32 sum that starts at +0 is never -0).
-    for (int u = 0; u < nk; u += C::NSTAGE)
+    for (int u = 0; u < n; u += C::NSTAGE)
         static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
-            if (C::NSTAGE <= 2 || u + decltype(sc)::value < nk)
+            if (C::NSTAGE <= 2 || u + decltype(sc)::value < n)
                 step_body(u + decltype(sc)::value, sc);
         });
-    wait_vmcnt<0>();      // drain the zero-filling prefetches before exit
+    wait_vmcnt<0>();      // drain the zero-filling prefetches
+    };
 
-    if constexpr (C::MF == 32)
-        store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
-    else
-        store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                  vec_store);
+    auto store_d = [&]() G18_INLINE {
+        if constexpr (C::MF == 32)
+            store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                    vec_store);
+        else
+            store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                      vec_store);
+    };
+
+    if constexpr (!SK) {
+        set_item(blockIdx.x, 0, nk);
+        run_item();
+        store_d();
+        return;
+    }
+
+    // ---- persistent stream-K form ----
+    // A partial slot holds each lane's accumulators in register order, 16
+    // bytes per lane per access: piece e of block q of wave v, lane l, is at
+    // byte (((v * NM + q) * P4 + e) * 64 + l) * 16, so every access is one
+    // fully coalesced 1 KB buffer access whose per-block part is a constant
+    // scalar offset (one lane offset in a VGPR for the whole slot).
+    constexpr int P4 = (int)(sizeof(typename C::acc_t) / 16);     // 16-byte pieces per block
+    auto slot_rsrc = [&](int wslot) G18_INLINE {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(sk.partials + (int64_t)wslot * (C::BM * C::BN)), (short)0,
+            C::BM * C::BN * 4, kRsrcFlags);
+    };
+    auto slot_store = [&](__amdgpu_buffer_rsrc_t rs, int voff) G18_INLINE {
+        static_for<0, NM>([&](auto qc) G18_INLINE {
+            constexpr int q = decltype(qc)::value;
+            const auto &a = acc[q / C::TN][q % C::TN];
+#pragma unroll
+            for (int e = 0; e < P4; ++e) {
+                const f32x4 v = {a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
+                                                       (q * P4 + e) * 1024, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);    // one block at a time: no register peak
+        });
+    };
+    // D for the current tile: the accumulators plus, block by block, the
+    // partial sums of slots w_first .. w_last (an empty range for a whole
+    // tile), in that order; ok == false writes NaN instead.
+    auto store_sum = [&](int w_first, int w_last, bool ok, int voff) G18_INLINE {
+        auto get = [&](int bi, int bj) G18_INLINE {
+            typename C::acc_t v = acc[bi][bj];
+            const int q = bi * C::TN + bj;
+            for (int w2 = w_first; w2 <= w_last; ++w2) {
+                const __amdgpu_buffer_rsrc_t rs = slot_rsrc(w2);
+#pragma unroll
+                for (int e = 0; e < P4; ++e) {
+                    const f32x4 p4 = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (q * P4 + e) * 1024, 0));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[4 * e + r] += p4[r];
+                }
+            }
+            if (!ok)
+                v = typename C::acc_t{} + __builtin_nanf("");
+            return v;
+        };
+        if constexpr (C::MF == 32)
+            store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                       vec_store);
+        else
+            store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                         vec_store);
+    };
+
+    const int w = blockIdx.x;
+    SkCursor cur = sk_begin(sk, w);
+    SkItem it;
+    while (sk_next(sk, nk, gridDim.x, cur, it)) {
+        const int s0 = it.s0, s1 = it.s1;
+        lds_barrier();                 // every wave is done with the LDS stages
+        set_item(it.tile, s0, s1);
+        run_item();
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int slot_voff = (wave * NM * P4 * 64 + ln) * 16;
+        if (s0 > 0) {
+            // Contributor: publish the partial sums, then the flag.
+            slot_store(slot_rsrc(w), slot_voff);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            continue;
+        }
+        // Owner of a split tile (or a whole tile: an empty range): wait for
+        // the contributors' flags, then add their partials while storing D.
+        const int w_first = it.w_first, w_last = it.w_last;
+        bool ok = true;
+        if (w_first <= w_last) {
+            for (int w2 = w_first; w2 <= w_last && ok; ++w2) {
+                if (tid == 0) {
+                    int got = 0;
+                    for (int poll = 0; poll < kSpinLimit; ++poll) {
+                        if (__hip_atomic_load(sk.flags + w2, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)) {
+                            got = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    sk_ok = got;
+                }
+                __syncthreads();
+                ok = sk_ok != 0;
+                __syncthreads();
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        store_sum(w_first, w_last, ok, slot_voff);
+        if (w_first <= w_last && tid == 0)
+            for (int w2 = w_first; w2 <= w_last; ++w2)
+                __hip_atomic_store(sk.flags + w2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // D = +0 everywhere (K == 0).
@@ -778,37 +1015,186 @@ void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int 
                        tm, tn, vec);
 }
 
-template <class C>
-void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s)
+template <class C, bool SK, bool ALLOW_TAIL = true>
+void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
+                const SkPlan &sk, int grid)
 {
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
+    if (!SK)
+        grid = tm * tn;
     if (K % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false>), dim3((unsigned)(tm * tn)),
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false, SK>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec);
-    else
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true>), dim3((unsigned)(tm * tn)),
+                           (_Float16 *)D, M, N, K, tm, tn, vec, sk);
+    else if constexpr (ALLOW_TAIL)
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true, SK>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec);
+                           (_Float16 *)D, M, N, K, tm, tn, vec, sk);
 }
 
 // CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
 // 4-byte loads; C: the register-staged kernel for whatever remains (odd K or
 // 2-byte aligned operands).
+// Bytes each lane moves per direct-to-LDS load for these operands: 16, 4,
+// or 0 when only the register-staged kernel can serve them.
+int load_bytes(const void *A, const void *B, int64_t K)
+{
+    const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
+    if (K % 8 == 0 && (ab & 15u) == 0)
+        return 16;
+    if (K % 2 == 0 && (ab & 3u) == 0)
+        return 4;
+    return 0;
+}
+
+// One workgroup per tile.
 template <class C, class CDma, class CDma4>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s)
 {
-    const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if (K % 8 == 0 && (ab & 15u) == 0) {
-        launch_dma<CDma>(A, B, D, M, N, K, vec, s);
-        return;
+    const SkPlan none{};
+    switch (load_bytes(A, B, K)) {
+    case 16: launch_dma<CDma, false>(A, B, D, M, N, K, vec, s, none, 0); return;
+    case 4: launch_dma<CDma4, false>(A, B, D, M, N, K, vec, s, none, 0); return;
+    default: launch_cfg<C, 2>(A, B, D, M, N, K, vec, s);
     }
-    if (K % 2 == 0 && (ab & 3u) == 0) {
-        launch_dma<CDma4>(A, B, D, M, N, K, vec, s);
-        return;
+}
+
+// The persistent stream-K grid (direct-to-LDS paths only).  The 256 x 256
+// form exists only for 16-byte loads with K % 64 == 0: with a K tail or
+// 4-byte loads its per-lane load state no longer fits beside the 256
+// accumulators and would spill inside the K-loop.
+void launch_sk_mid(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
+                   const SkPlan &sk, int grid)
+{
+    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    if (load_bytes(A, B, K) == 16)
+        launch_dma<MidDma, true>(A, B, D, M, N, K, vec, s, sk, grid);
+    else
+        launch_dma<MidDma4, true>(A, B, D, M, N, K, vec, s, sk, grid);
+}
+
+void launch_sk_big(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
+                   const SkPlan &sk, int grid)
+{
+    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    launch_dma<BigDma, true, false>(A, B, D, M, N, K, vec, s, sk, grid);
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K planning.  Times are in units of one K-step of a 256 x 256 tile
+// with 16-byte loads on one CU (~1.5 us at the power-limited clock), from
+// measurements on MI355X: a 128 x 128 step costs 0.35 (1.65 and 0.56 with
+// 4-byte loads); filling the pipeline plus the epilogue of one work item
+// 1.5; writing or reading one fp32 partial tile 1.8 (256 x 256) or 0.45
+// (128 x 128); the flag hand-off and fences a further 2.
+struct Plan {
+    Tile tile = Tile::kThin;
+    bool sk = false;
+    int grid = 0;
+    SkPlan split{};
+};
+
+constexpr double kFill = 1.5, kSkFixed = 2.0;
+
+double step_cost(Tile t, int lb)
+{
+    const bool wide = lb == 16;
+    return t == Tile::kBig ? (wide ? 1.0 : 1.65) : (wide ? 0.35 : 0.56);
+}
+
+double partial_cost(Tile t) { return t == Tile::kBig ? 1.8 : 0.45; }
+
+// Whole-tile time on P workgroups.
+double dp_time(int64_t tiles, int64_t steps, double step, int P)
+{
+    return (double)cdiv(tiles, P) * ((double)steps * step + kFill);
+}
+
+// Stream-K split of `tiles` tiles of `steps` K-steps over P workgroups: if
+// the tiles fill whole waves, none; otherwise the last partial wave plus one
+// full wave (or every tile, if there are fewer than P) is split by steps, so
+// each workgroup gets between one and two tiles of work.
+SkPlan sk_split(int64_t tiles, int64_t steps, int P)
+{
+    SkPlan sp{};
+    sp.sk_tiles = (int)(tiles < P ? tiles : tiles % P + P);
+    sp.dp_tiles = (int)(tiles - sp.sk_tiles);
+    const int64_t total = (int64_t)sp.sk_tiles * steps;
+    sp.base = (int)(total / P);
+    sp.extra = (int)(total % P);
+    return sp;
+}
+
+double sk_time(Tile t, int64_t tiles, int64_t steps, int lb, int P)
+{
+    const SkPlan sp = sk_split(tiles, steps, P);
+    const double step = step_cost(t, lb);
+    const int64_t per_wg = sp.base + (sp.extra ? 1 : 0);
+    const int64_t pieces = cdiv(steps, per_wg) + 1;     // most workgroups one tile can span
+    return (double)(sp.dp_tiles / P) * ((double)steps * step + kFill) + (double)per_wg * step +
+           2.0 * kFill + (double)pieces * partial_cost(t) + kSkFixed;
+}
+
+int64_t tiles_of(Tile t, int64_t M, int64_t N)
+{
+    const int b = t == Tile::kBig ? 256 : 128;
+    return cdiv(M, b) * cdiv(N, b);
+}
+
+// The fastest of: whole tiles on the tile choose_tile picks, or stream-K on
+// the 256 x 256 or the 128 x 128 tile.  lb: 16 or 4 (0: no stream-K).
+Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
+{
+    Plan best;
+    best.tile = choose_tile(M, N, K);
+    if (lb == 0 || best.tile == Tile::kThin || K == 0)
+        return best;
+    const int64_t steps = cdiv(K, 64);
+    double t_best = dp_time(tiles_of(best.tile, M, N), steps, step_cost(best.tile, lb), P);
+    for (Tile t : {Tile::kBig, Tile::kMid}) {
+        const int64_t tiles = tiles_of(t, M, N);
+        if (tiles % P == 0 || (t == Tile::kBig && (lb != 16 || K % 64 != 0)))
+            continue;
+        const double ts = sk_time(t, tiles, steps, lb, P);
+        if (ts < t_best) {
+            t_best = ts;
+            best.tile = t;
+            best.sk = true;
+            best.grid = P;
+            best.split = sk_split(tiles, steps, P);
+        }
     }
-    launch_cfg<C, 2>(A, B, D, M, N, K, vec, s);
+    return best;
+}
+
+int64_t flag_bytes(int P) { return cdiv((int64_t)P * 4, 256) * 256; }
+
+int64_t workspace_bytes(const Plan &pl)
+{
+    if (!pl.sk)
+        return 0;
+    const int64_t tile = pl.tile == Tile::kBig ? 256 * 256 : 128 * 128;
+    return flag_bytes(pl.grid) + (int64_t)pl.grid * tile * 4;
+}
+
+// Workgroups the stream-K grid may use on the current device: one per CU,
+// at most kCUs.  The count is read once per device.
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return kCUs;
+    if (dev >= 0 && dev < 64 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+        return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return kCUs;
+    cus = cus < kCUs ? cus : kCUs;
+    if (dev >= 0 && dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 } // namespace
@@ -836,6 +1222,91 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
         }
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
+}
+
+int64_t gemm_nt_f16_ws_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > INT32_MAX || N > INT32_MAX || K > GEMM_MAX_K)
+        return 0;
+    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    return workspace_bytes(make_plan(M, N, K, lb, kCUs));
+}
+
+int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                   void *workspace, int64_t ws_bytes, hipStream_t stream)
+{
+    const int rc = validate(A, B, D, M, N, K);
+    if (rc != GEMM_OK)
+        return rc;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !workspace) || ((uintptr_t)workspace & 255u))
+        return GEMM_EINVAL;
+    if (ws_bytes > 0) {
+        const uintptr_t w = (uintptr_t)workspace;
+        auto hits = [&](const void *p, int64_t bytes) {
+            const uintptr_t q = (uintptr_t)p;
+            return bytes > 0 && w < q + (uint64_t)bytes && q < w + (uint64_t)ws_bytes;
+        };
+        if (hits(A, M * K * 2) || hits(B, N * K * 2) || hits(D, M * N * 2))
+            return GEMM_EINVAL;
+    }
+    const int lb = load_bytes(A, B, K);
+    if (M == 0 || N == 0 || K == 0 || lb == 0)
+        return gemm_nt_f16(A, B, D, M, N, K, stream);
+    const Plan pl = make_plan(M, N, K, lb, device_cus());
+    const int64_t need = workspace_bytes(pl);
+    if (!pl.sk || need > ws_bytes)
+        return gemm_nt_f16(A, B, D, M, N, K, stream);
+    SkPlan sp = pl.split;
+    sp.flags = (uint32_t *)workspace;
+    sp.partials = (float *)((char *)workspace + flag_bytes(pl.grid));
+    if (pl.tile == Tile::kBig)
+        launch_sk_big(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
+    else
+        launch_sk_mid(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
+}
+
+int gemm_nt_f16_ws_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int64_t *workgroups,
+                        int64_t *sk_tiles)
+{
+    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !workgroups || !sk_tiles)
+        return GEMM_EINVAL;
+    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    const Plan pl = make_plan(M, N, K, (M && N && K) ? lb : 0, kCUs);
+    tile_dims(pl.tile, *bm, *bn);
+    *sk_tiles = pl.sk ? pl.split.sk_tiles : 0;
+    *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : (pl.sk ? pl.grid : cdiv(M, *bm) * cdiv(N, *bn));
+    return GEMM_OK;
+}
+
+int gemm_nt_f16_ws_items(int64_t M, int64_t N, int64_t K, int64_t wg, int64_t *items,
+                         int64_t max_items, int64_t *count)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || M > INT32_MAX || N > INT32_MAX || K > GEMM_MAX_K ||
+        max_items < 0 || (max_items && !items) || !count)
+        return GEMM_EINVAL;
+    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    const Plan pl = make_plan(M, N, K, lb, kCUs);
+    *count = 0;
+    if (!pl.sk)
+        return GEMM_OK;
+    if (wg < 0 || wg >= pl.grid)
+        return GEMM_EINVAL;
+    const int nk = (int)cdiv(K, 64);
+    SkCursor cur = sk_begin(pl.split, (int)wg);
+    SkItem it;
+    while (sk_next(pl.split, nk, pl.grid, cur, it)) {
+        if (*count < max_items) {
+            int64_t *o = items + 5 * *count;
+            o[0] = it.tile;
+            o[1] = it.s0;
+            o[2] = it.s1;
+            o[3] = it.w_first;
+            o[4] = it.w_last;
+        }
+        ++*count;
+    }
+    return GEMM_OK;
 }
 
 const char *gemm_nt_f16_strerror(int code)

@@ -69,6 +69,74 @@ typedef struct ihipStream_t *hipStream_t;
 int gemm_nt_f16(const void *A, const void *B, void *D,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * Stream-K form of gemm_nt_f16 for shapes whose tiles do not fill whole
+ * waves of the GPU's CUs (page 2, "构建 Tiled GEMM", names persistent kernels
+ * with a software pipeline as the next step after its tiled kernel; page 1
+ * notes that persistent kernels amortise launch costs at large sizes).  The
+ * result is D = A * B^T exactly as gemm_nt_f16 defines it; only the order of
+ * the fp32 additions differs, and it is fixed for a given shape, so repeated
+ * calls are bitwise identical.
+ *
+ * A persistent grid of one workgroup per CU (at most 256) computes whole
+ * tiles round-robin and splits the K-steps of the remaining tiles evenly;
+ * a tile split over several workgroups is summed in fp32 through
+ * `workspace` and rounded to fp16 once.
+ *
+ * workspace: device memory of at least gemm_nt_f16_ws_size(M, N, K) bytes,
+ *   256-byte aligned, not overlapping A, B or D, owned by the caller.  It
+ *   must be zero-filled before its first use; every call that completes
+ *   leaves it ready for the next one (its flag words zero again), so it is
+ *   reused without clearing, for any shape.  Calls that share a workspace
+ *   must not run concurrently (order them on one stream).
+ * ws_bytes: its size in bytes.  When the shape does not benefit from
+ *   stream-K, or ws_bytes is too small for the plan, the call runs exactly
+ *   as gemm_nt_f16 (workspace unused; it may then be NULL with ws_bytes 0).
+ *
+ * All workgroups of the grid must be resident at once: the call expects the
+ * GPU's CUs not to be held by other long-running work.  A workgroup that
+ * waits more than ~5 s for another writes its tile as NaN (0x7E00) and
+ * ends, so the kernel always terminates; the workspace must then be zeroed
+ * again.
+ *
+ * Returns GEMM_OK, GEMM_EINVAL (as gemm_nt_f16, or ws_bytes < 0, a NULL or
+ * misaligned workspace with ws_bytes > 0, or a workspace overlapping A, B or
+ * D) or GEMM_ELAUNCH.
+ */
+int gemm_nt_f16_ws(const void *A, const void *B, void *D,
+                   int64_t M, int64_t N, int64_t K,
+                   void *workspace, int64_t ws_bytes, hipStream_t stream);
+
+/*
+ * Host-only (no HIP call): bytes of workspace gemm_nt_f16_ws needs for this
+ * shape with operands aligned to 16 bytes (0: it would not use stream-K).
+ * Sizes out of range give 0.
+ */
+int64_t gemm_nt_f16_ws_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Host-only introspection (no HIP call) of gemm_nt_f16_ws's plan for 16-byte
+ * aligned operands on 256 CUs: the tile, the workgroups launched and how
+ * many tiles are split by K-steps (0: the plain one-workgroup-per-tile
+ * launch).  Returns GEMM_OK or GEMM_EINVAL (negative size or NULL output).
+ */
+int gemm_nt_f16_ws_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn,
+                        int64_t *workgroups, int64_t *sk_tiles);
+
+/*
+ * Host-only (no HIP call): the work items workgroup `wg` runs under that
+ * plan, in order, 5 values each: tile, first K-step, end K-step (K-steps
+ * of 64), and the first and last workgroup whose partial sums it adds (none
+ * when first > last).  A first K-step > 0 means the workgroup only
+ * contributes a partial sum to that tile.  Writes at most max_items items
+ * to `items` and the full count to *count (0 when the plan is not
+ * stream-K).  Tiles are numbered as gemm_nt_f16_tile_coord maps them.
+ * Returns GEMM_OK or GEMM_EINVAL (sizes out of range, wg outside the grid,
+ * NULL outputs).
+ */
+int gemm_nt_f16_ws_items(int64_t M, int64_t N, int64_t K, int64_t wg,
+                         int64_t *items, int64_t max_items, int64_t *count);
+
 /* Static text for a return code; never NULL. */
 const char *gemm_nt_f16_strerror(int code);
 

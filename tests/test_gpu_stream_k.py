@@ -1,0 +1,98 @@
+"""GPU parity of the stream-K entry point gemm_nt_f16_ws against the oracle.
+
+Shapes are chosen so that every form of the persistent kernel runs: 256x256
+and 128x128 tiles, fewer tiles than CUs and whole tiles followed by split
+ones, one to three contributors per tile, 4-byte loads with a K tail.  The
+bar is the one of the plain entry point: integer inputs bit-exact, random
+inputs within 2^-10 |D_ref| + 1e-3 sqrt(K).  The summation order is fixed
+per shape, so repeated calls must agree bit for bit, and the workspace must
+come back with its flag words zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_18_amd import binding
+from dense_gemm_18_amd import workloads as wl
+from tests.gpu_util import assert_bitexact, assert_tolerance, device, note, run_gemm_ws
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    (3072, 3072, 2048),      # 256x256, 144 tiles split, 2 contributors
+    (6144, 6144, 512),       # 256x256, 256 whole tiles then 320 split
+    (1024, 1024, 8192),      # 128x128, 3 contributors
+    (1536, 2048, 4096),      # 128x128, 192 tiles split
+    (2304, 2304, 1030),      # 128x128, 4-byte loads, K tail
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library_present():
+    assert binding.library_path().exists(), "libgemm18.so not built"
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_stream_k_integer_bitexact(M, N, K):
+    assert binding.gemm_nt_f16_ws_tile(M, N, K)[3] > 0, "shape must take the stream-K plan"
+    A, B = wl.integer_free(6000 + K, M, N, K)
+    note(f"stream-K integer {M}x{N}x{K} plan {binding.gemm_nt_f16_ws_tile(M, N, K)}")
+    d = run_gemm_ws(A, B)
+    ref = oracle.gemm_nt_f16(A, B)
+    assert np.abs(oracle.decode(ref)).max() <= 2048
+    assert_bitexact(d, ref, f"stream-K {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_stream_k_random_tolerance(M, N, K):
+    A, B = wl.uniform_inputs(7000 + K, M, N, K)
+    note(f"stream-K random {M}x{N}x{K}")
+    d = run_gemm_ws(A, B)
+    assert_tolerance(d, oracle.gemm_nt_f16(A, B), K, f"stream-K random {M}x{N}x{K}")
+
+
+def test_stream_k_deterministic_and_reusable():
+    import torch
+    dev = device()
+    ws = torch.zeros(max(binding.gemm_nt_f16_ws_size(*s) for s in SHAPES[:3]), dtype=torch.uint8,
+                     device=dev)
+    A1, B1 = wl.uniform_inputs(8001, 3072, 3072, 2048)
+    A2, B2 = wl.uniform_inputs(8002, 1024, 1024, 8192)
+    note("stream-K reuse: shape 1 twice, shape 2, shape 1")
+    d1 = run_gemm_ws(A1, B1, ws, repeat=2)
+    d2 = run_gemm_ws(A2, B2, ws)
+    d1b = run_gemm_ws(A1, B1, ws)
+    assert np.array_equal(d1, d1b)
+    assert_tolerance(d2, oracle.gemm_nt_f16(A2, B2), 8192, "stream-K reuse shape 2")
+    flags = ws[:1024].cpu().numpy()
+    assert not flags.any(), "flag words must be zero after a completed call"
+
+
+def test_stream_k_too_small_workspace_runs_plain():
+    A, B = wl.integer_free(8100, 3072, 3072, 2048)
+    import torch
+    ws = torch.zeros(4096, dtype=torch.uint8, device=device())
+    note("stream-K with a too-small workspace")
+    d = run_gemm_ws(A, B, ws)
+    assert_bitexact(d, oracle.gemm_nt_f16(A, B), "too-small workspace")
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 8192), (3072, 3072, 3072)])
+def test_stream_k_sampled_large(M, N, K):
+    # 256x256 tiles split four ways (2048^2) and the 3072^3 split; sampled
+    # entries plus the rows and columns at tile edges against the oracle.
+    A, B = wl.uniform_inputs(8200 + K, M, N, K)
+    note(f"stream-K sampled {M}x{N}x{K}")
+    d = run_gemm_ws(A, B, repeat=2)
+    rng = np.random.default_rng(8300)
+    flat = rng.choice(M * N, 4096, replace=False)
+    rows, cols = flat // N, flat % N
+    er = wl.edge_lines(M, 256)
+    rr = np.repeat(er, N)
+    rc = np.tile(np.arange(N), er.size)
+    rows = np.concatenate([rows, rr])
+    cols = np.concatenate([cols, rc])
+    ref = oracle.gemm_nt_f16_entries(A, B, rows, cols)
+    assert_tolerance(d[rows, cols], ref, K, f"stream-K sampled {M}x{N}x{K}")

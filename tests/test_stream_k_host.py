@@ -1,0 +1,128 @@
+"""CPU-only checks of the stream-K entry point's host logic (no kernel launch).
+
+The work items each workgroup runs come from the same host/device code the
+kernel uses (gemm_nt_f16_ws_items).  For every plan: each K-step of each tile
+is computed exactly once; each tile has exactly one owner (the item holding
+its first K-step), which adds the partials of exactly the workgroups that
+contribute to it; every workgroup contributes at most once, as its first
+stream-K item, and only to a lower-numbered owner (so waits cannot form a
+cycle); every index stays inside the grid and the tile range.
+"""
+from __future__ import annotations
+
+import pytest
+
+from dense_gemm_18_amd import binding
+
+FAKE = 0x10000000
+
+SK_SHAPES = [
+    (3072, 3072, 2048),      # 256x256 tiles, fewer tiles than CUs, 2 contributors
+    (2560, 2560, 4096),      # 256x256 tiles, 3 contributors
+    (6144, 6144, 512),       # 256x256: 256 whole tiles, then 320 split ones
+    (3072, 3072, 3072),
+    (2048, 2048, 8192),
+    (1536, 8192, 8192),
+    (1024, 1024, 8192),      # 128x128 tiles, 3 contributors
+    (1536, 2048, 4096),
+    (2304, 2304, 1030),      # 128x128, 4-byte loads and a K tail
+    (2560, 2560, 2048),
+    (1280, 1280, 8192),
+]
+
+
+def _steps(K):
+    return -(-K // 64)
+
+
+@pytest.mark.parametrize("M,N,K", SK_SHAPES)
+def test_schedule_covers_each_step_once(M, N, K):
+    bm, bn, grid, sk_tiles = binding.gemm_nt_f16_ws_tile(M, N, K)
+    assert sk_tiles > 0 and 0 < grid <= 256
+    tiles = -(-M // bm) * -(-N // bn)
+    nk = _steps(K)
+    covered = {}                         # tile -> list of (s0, s1)
+    owner = {}                           # tile -> (wg, w_first, w_last)
+    contrib = {}                         # tile -> set of wgs
+    for wg in range(grid):
+        items = binding.gemm_nt_f16_ws_items(M, N, K, wg)
+        seen_split = False
+        n_contrib = 0
+        for tile, s0, s1, wf, wl in items:
+            assert 0 <= tile < tiles and 0 <= s0 < s1 <= nk
+            covered.setdefault(tile, []).append((s0, s1))
+            whole = s0 == 0 and s1 == nk
+            if s0 > 0:
+                n_contrib += 1
+                assert not seen_split, "a contribution must be the first split item"
+                contrib.setdefault(tile, set()).add(wg)
+                assert wf > wl
+            else:
+                assert tile not in owner
+                owner[tile] = (wg, wf, wl)
+                if whole:
+                    assert wf > wl
+                else:
+                    assert wg < wf <= wl < grid
+            if not whole:
+                seen_split = True
+        assert n_contrib <= 1
+    assert sorted(covered) == list(range(tiles))
+    for tile, spans in covered.items():
+        spans.sort()
+        assert spans[0][0] == 0 and spans[-1][1] == nk
+        for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+            assert a1 == b0, (tile, spans)
+        wg, wf, wl = owner[tile]
+        got = contrib.get(tile, set())
+        assert got == set(range(wf, wl + 1)) if wf <= wl else not got
+    # the split tiles are the last sk_tiles ones
+    assert all(len(covered[t]) == 1 for t in range(tiles - sk_tiles))
+
+
+@pytest.mark.parametrize("M,N,K,bm,sk", [
+    (8192, 8192, 8192, 256, 0),      # whole waves: plain launch
+    (4096, 4096, 4096, 256, 0),
+    (3000, 5000, 2048, 256, 0),      # 240 tiles: the last 16 CUs idle beats splitting
+    (1024, 1024, 1024, 128, 0),      # too small to pay for the hand-off
+    (64, 16384, 8192, 64, 0),        # thin tiles never split
+    (3072, 3072, 3072, 256, 144),
+    (2048, 2048, 8192, 256, 64),
+    (1024, 1024, 8192, 128, 64),
+    (2304, 2304, 1030, 128, 324),    # K % 64 != 0: 128x128 tiles only
+])
+def test_plan_choice(M, N, K, bm, sk):
+    got = binding.gemm_nt_f16_ws_tile(M, N, K)
+    assert (got[0], got[3]) == (bm, sk)
+    need = binding.gemm_nt_f16_ws_size(M, N, K)
+    if sk:
+        assert need == 1024 + 256 * bm * bm * 4     # 256 flag words, 256 fp32 tile slots
+    else:
+        assert need == 0 and binding.gemm_nt_f16_ws_items(M, N, K, 0) == []
+
+
+def test_ws_size_out_of_range():
+    assert binding.gemm_nt_f16_ws_size(-1, 5, 5) == 0
+    assert binding.gemm_nt_f16_ws_size(0, 5, 5) == 0
+    assert binding.gemm_nt_f16_ws_size(5, 5, binding.GEMM_MAX_K + 1) == 0
+
+
+@pytest.mark.parametrize("ws,ws_bytes", [
+    (FAKE + 0x8000000, -1),                     # negative size
+    (0, 1 << 20),                               # NULL with a size
+    (FAKE + 0x8000000 + 128, 1 << 26),          # not 256-byte aligned
+    (FAKE, 1 << 26),                            # overlaps A
+    (FAKE + 0x1000000 - 256, 1 << 26),          # overlaps B
+    (FAKE + 0x2000000 + 256, 1 << 26),          # overlaps D
+])
+def test_ws_validation_rejects_before_any_hip_call(ws, ws_bytes):
+    rc = binding.gemm_nt_f16_ws(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 64, 64, 64, ws,
+                                ws_bytes, 0)
+    assert rc == binding.GEMM_EINVAL
+
+
+def test_ws_items_rejects_bad_arguments():
+    with pytest.raises(binding.GemmError):
+        binding.gemm_nt_f16_ws_items(3072, 3072, 3072, 256)      # outside the 256 workgroups
+    with pytest.raises(binding.GemmError):
+        binding.gemm_nt_f16_ws_items(0, 3072, 3072, 0)

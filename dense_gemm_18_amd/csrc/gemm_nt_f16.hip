@@ -761,7 +761,111 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     };
     // acc = the sum over the current item's K-steps (steps are counted from
     // the item's first one).
-    auto run_item = [&]() G18_INLINE {
+
+    auto store_d = [&]() G18_INLINE {
+        if constexpr (C::MF == 32)
+            store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                    vec_store);
+        else
+            store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                      vec_store);
+    };
+
+    // ---- stream-K epilogue helpers ----
+    // Hand-off between workgroups on different XCDs, whose L2 caches are not
+    // coherent with each other: partial sums and flags move with the sc1
+    // cache policy (coherent at device scope, like device-scope atomics), and
+    // a contributor's stores are complete (vmcnt 0) before its flag is
+    // raised.  No device-scope fence is used: on this part a fence writes
+    // back or invalidates a whole L2, which would evict every other
+    // workgroup's staged A and B lines.
+    constexpr int kSc1 = 16;    // cache-policy bits of a buffer access: sc1
+    // A partial slot holds each lane's accumulators in register order, 16
+    // bytes per lane per access: piece e of block q of wave v, lane l, is at
+    // byte (((v * NM + q) * P4 + e) * 64 + l) * 16, so every access is one
+    // fully coalesced 1 KB buffer access whose per-block part is a constant
+    // scalar offset (one lane offset in a VGPR for the whole slot).
+    constexpr int P4 = (int)(sizeof(typename C::acc_t) / 16);     // 16-byte pieces per block
+    auto slot_rsrc = [&](int wslot) G18_INLINE {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(sk.partials + (int64_t)wslot * (C::BM * C::BN)), (short)0,
+            C::BM * C::BN * 4, kRsrcFlags);
+    };
+    auto slot_store = [&](__amdgpu_buffer_rsrc_t rs, int voff) G18_INLINE {
+        static_for<0, NM>([&](auto qc) G18_INLINE {
+            constexpr int q = decltype(qc)::value;
+            const auto &a = acc[q / C::TN][q % C::TN];
+#pragma unroll
+            for (int e = 0; e < P4; ++e) {
+                const f32x4 v = {a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
+                                                       (q * P4 + e) * 1024, kSc1);
+            }
+            __builtin_amdgcn_sched_barrier(0);    // one block at a time: no register peak
+        });
+    };
+    // Owner: add the partial sums of slots w_first .. w_last, in that order.
+    // Loads are issued RB blocks at a time (the fragment registers are free
+    // here), so one memory latency covers RB KB per wave instead of one.
+    constexpr int RB = NM % 16 == 0 ? 16 : NM;
+    auto add_partials = [&](int w_first, int w_last, int voff) G18_INLINE {
+        for (int w2 = w_first; w2 <= w_last; ++w2) {
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(w2);
+            static_for<0, NM / RB>([&](auto bc) G18_INLINE {
+                constexpr int b0 = decltype(bc)::value * RB;
+                f32x4 pf[RB][P4];
+                static_for<0, RB>([&](auto gc) G18_INLINE {
+                    constexpr int q = b0 + decltype(gc)::value;
+#pragma unroll
+                    for (int e = 0; e < P4; ++e)
+                        pf[decltype(gc)::value][e] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rs, voff, (q * P4 + e) * 1024, kSc1));
+                });
+                static_for<0, RB>([&](auto gc) G18_INLINE {
+                    constexpr int q = b0 + decltype(gc)::value;
+                    auto &a = acc[q / C::TN][q % C::TN];
+#pragma unroll
+                    for (int e = 0; e < P4; ++e)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            a[4 * e + r] += pf[decltype(gc)::value][e][r];
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    };
+    // D for the current tile; ok == false (a contributor never arrived)
+    // writes NaN instead.
+    auto store_ok = [&](bool ok) G18_INLINE {
+        auto get = [&](int bi, int bj) G18_INLINE {
+            return ok ? acc[bi][bj] : typename C::acc_t{} + __builtin_nanf("");
+        };
+        if constexpr (C::MF == 32)
+            store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                       vec_store);
+        else
+            store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                         vec_store);
+    };
+
+    // The work loop: one pass (this workgroup's tile) for the one-tile-per-
+    // workgroup form; the persistent form walks its items.  The pipeline is
+    // written out here once, not wrapped in a lambda: wrapped, the register
+    // allocator moves accumulators and fragments between register files
+    // inside the K-loop.
+    const int w = blockIdx.x;
+    SkCursor cur = sk_begin(sk, w);
+    for (;;) {
+        SkItem it{};
+        if constexpr (SK) {
+            if (!sk_next(sk, nk, gridDim.x, cur, it))
+                break;
+            lds_barrier();             // every wave is done with the LDS stages
+            set_item(it.tile, it.s0, it.s1);
+        } else {
+            set_item(blockIdx.x, 0, nk);
+        }
     int ln = lane;
     asm volatile("" : "+v"(ln));
     setup_loads(ln);
@@ -796,103 +900,26 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                 step_body(u + decltype(sc)::value, sc);
         });
     wait_vmcnt<0>();      // drain the zero-filling prefetches
-    };
 
-    auto store_d = [&]() G18_INLINE {
-        if constexpr (C::MF == 32)
-            store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                    vec_store);
-        else
-            store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                      vec_store);
-    };
-
-    if constexpr (!SK) {
-        set_item(blockIdx.x, 0, nk);
-        run_item();
-        store_d();
-        return;
-    }
-
-    // ---- persistent stream-K form ----
-    // A partial slot holds each lane's accumulators in register order, 16
-    // bytes per lane per access: piece e of block q of wave v, lane l, is at
-    // byte (((v * NM + q) * P4 + e) * 64 + l) * 16, so every access is one
-    // fully coalesced 1 KB buffer access whose per-block part is a constant
-    // scalar offset (one lane offset in a VGPR for the whole slot).
-    constexpr int P4 = (int)(sizeof(typename C::acc_t) / 16);     // 16-byte pieces per block
-    auto slot_rsrc = [&](int wslot) G18_INLINE {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(sk.partials + (int64_t)wslot * (C::BM * C::BN)), (short)0,
-            C::BM * C::BN * 4, kRsrcFlags);
-    };
-    auto slot_store = [&](__amdgpu_buffer_rsrc_t rs, int voff) G18_INLINE {
-        static_for<0, NM>([&](auto qc) G18_INLINE {
-            constexpr int q = decltype(qc)::value;
-            const auto &a = acc[q / C::TN][q % C::TN];
-#pragma unroll
-            for (int e = 0; e < P4; ++e) {
-                const f32x4 v = {a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
-                                                       (q * P4 + e) * 1024, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);    // one block at a time: no register peak
-        });
-    };
-    // D for the current tile: the accumulators plus, block by block, the
-    // partial sums of slots w_first .. w_last (an empty range for a whole
-    // tile), in that order; ok == false writes NaN instead.
-    auto store_sum = [&](int w_first, int w_last, bool ok, int voff) G18_INLINE {
-        auto get = [&](int bi, int bj) G18_INLINE {
-            typename C::acc_t v = acc[bi][bj];
-            const int q = bi * C::TN + bj;
-            for (int w2 = w_first; w2 <= w_last; ++w2) {
-                const __amdgpu_buffer_rsrc_t rs = slot_rsrc(w2);
-#pragma unroll
-                for (int e = 0; e < P4; ++e) {
-                    const f32x4 p4 = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (q * P4 + e) * 1024, 0));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[4 * e + r] += p4[r];
-                }
-            }
-            if (!ok)
-                v = typename C::acc_t{} + __builtin_nanf("");
-            return v;
-        };
-        if constexpr (C::MF == 32)
-            store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                       vec_store);
-        else
-            store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                         vec_store);
-    };
-
-    const int w = blockIdx.x;
-    SkCursor cur = sk_begin(sk, w);
-    SkItem it;
-    while (sk_next(sk, nk, gridDim.x, cur, it)) {
-        const int s0 = it.s0, s1 = it.s1;
-        lds_barrier();                 // every wave is done with the LDS stages
-        set_item(it.tile, s0, s1);
-        run_item();
+        if constexpr (!SK) {
+            store_d();
+            break;
+        } else {
+        const int s0 = it.s0;
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int slot_voff = (wave * NM * P4 * 64 + ln) * 16;
         if (s0 > 0) {
             // Contributor: publish the partial sums, then the flag.
             slot_store(slot_rsrc(w), slot_voff);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            wait_vmcnt<0>();
             __syncthreads();
-            if (tid == 0) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (tid == 0)
                 __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
             continue;
         }
         // Owner of a split tile (or a whole tile: an empty range): wait for
-        // the contributors' flags, then add their partials while storing D.
+        // the contributors' flags, add their partials, store D.
         const int w_first = it.w_first, w_last = it.w_last;
         bool ok = true;
         if (w_first <= w_last) {
@@ -913,12 +940,14 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                 ok = sk_ok != 0;
                 __syncthreads();
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        store_sum(w_first, w_last, ok, slot_voff);
+        if (ok)
+            add_partials(w_first, w_last, slot_voff);
+        store_ok(ok);
         if (w_first <= w_last && tid == 0)
             for (int w2 = w_first; w2 <= w_last; ++w2)
                 __hip_atomic_store(sk.flags + w2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

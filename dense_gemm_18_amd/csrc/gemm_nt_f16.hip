@@ -535,7 +535,11 @@ __host__ __device__ inline bool sk_next(const SkPlan &sk, int nk, int P, SkCurso
 }
 
 // Polls of a contributor's flag before an owner gives up (~5 s at 1.6 GHz):
-// the tile is then written as NaN and the kernel still ends.
+// the tile is then written as NaN and the kernel still ends.  Every wave
+// polls for itself: the kernel keeps a single LDS object (a second one, to
+// broadcast the result, costs the compiler its proof that fragment reads do
+// not overlap in-flight direct-to-LDS loads, and it then waits for all of
+// them before every read).
 constexpr int kSpinLimit = 1 << 24;
 
 // KTAIL: K % BK != 0, so the last step is partial and every load carries a
@@ -548,7 +552,6 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                        int vec_store, SkPlan sk)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-    __shared__ int sk_ok;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -924,21 +927,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
         bool ok = true;
         if (w_first <= w_last) {
             for (int w2 = w_first; w2 <= w_last && ok; ++w2) {
-                if (tid == 0) {
-                    int got = 0;
-                    for (int poll = 0; poll < kSpinLimit; ++poll) {
-                        if (__hip_atomic_load(sk.flags + w2, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT)) {
-                            got = 1;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(8);
+                int got = 0;
+                for (int poll = 0; poll < kSpinLimit; ++poll) {
+                    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                            sk.flags + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                        got = 1;
+                        break;
                     }
-                    sk_ok = got;
+                    __builtin_amdgcn_s_sleep(8);
                 }
-                __syncthreads();
-                ok = sk_ok != 0;
-                __syncthreads();
+                ok = got != 0;
             }
         }
         if (ok)
@@ -1044,7 +1042,7 @@ void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int 
                        tm, tn, vec);
 }
 
-template <class C, bool SK, bool ALLOW_TAIL = true>
+template <class C, bool SK>
 void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
                 const SkPlan &sk, int grid)
 {
@@ -1055,7 +1053,7 @@ void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int 
         hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false, SK>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
                            (_Float16 *)D, M, N, K, tm, tn, vec, sk);
-    else if constexpr (ALLOW_TAIL)
+    else
         hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true, SK>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
                            (_Float16 *)D, M, N, K, tm, tn, vec, sk);
@@ -1089,12 +1087,9 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
     }
 }
 
-// The persistent stream-K grid (direct-to-LDS paths only).  The 256 x 256
-// form exists only for 16-byte loads with K % 64 == 0: with a K tail or
-// 4-byte loads its per-lane load state no longer fits beside the 256
-// accumulators and would spill inside the K-loop.
-void launch_sk_mid(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-                   const SkPlan &sk, int grid)
+// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
+void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
+               const SkPlan &sk, int grid)
 {
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
     if (load_bytes(A, B, K) == 16)
@@ -1103,20 +1098,17 @@ void launch_sk_mid(const void *A, const void *B, void *D, int M, int N, int K, h
         launch_dma<MidDma4, true>(A, B, D, M, N, K, vec, s, sk, grid);
 }
 
-void launch_sk_big(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-                   const SkPlan &sk, int grid)
-{
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    launch_dma<BigDma, true, false>(A, B, D, M, N, K, vec, s, sk, grid);
-}
 
 // ---------------------------------------------------------------------------
-// Stream-K planning.  Times are in units of one K-step of a 256 x 256 tile
-// with 16-byte loads on one CU (~1.5 us at the power-limited clock), from
-// measurements on MI355X: a 128 x 128 step costs 0.35 (1.65 and 0.56 with
-// 4-byte loads); filling the pipeline plus the epilogue of one work item
-// 1.5; writing or reading one fp32 partial tile 1.8 (256 x 256) or 0.45
-// (128 x 128); the flag hand-off and fences a further 2.
+// Stream-K planning.  Measured on MI355X (TFLOPS, stream-K / one workgroup
+// per tile): 512x640x16384 312/135, 1024^2x16384 858/424, 768x1024x8192
+// 509/299, 900x1000x4098 234/142, 1024^2x4096 417/362; but 1024^2x2048
+// 238/312, 1280^2x8192 444/624, 1536^2x8192 684/792.  Stream-K runs on the
+// 128 x 128 tile when its tiles fill at most a quarter of the CUs and K
+// spans at least 64 K-steps: the partial-sum hand-off (one fp32 tile per
+// contributor through memory) then costs less than the idle CUs.  The
+// 256 x 256 tile is not used for it: its hand-off moves 256 KB per
+// contributor and its pipeline leaves no registers for the persistent loop.
 struct Plan {
     Tile tile = Tile::kThin;
     bool sk = false;
@@ -1124,26 +1116,10 @@ struct Plan {
     SkPlan split{};
 };
 
-constexpr double kFill = 1.5, kSkFixed = 2.0;
-
-double step_cost(Tile t, int lb)
-{
-    const bool wide = lb == 16;
-    return t == Tile::kBig ? (wide ? 1.0 : 1.65) : (wide ? 0.35 : 0.56);
-}
-
-double partial_cost(Tile t) { return t == Tile::kBig ? 1.8 : 0.45; }
-
-// Whole-tile time on P workgroups.
-double dp_time(int64_t tiles, int64_t steps, double step, int P)
-{
-    return (double)cdiv(tiles, P) * ((double)steps * step + kFill);
-}
-
 // Stream-K split of `tiles` tiles of `steps` K-steps over P workgroups: if
-// the tiles fill whole waves, none; otherwise the last partial wave plus one
-// full wave (or every tile, if there are fewer than P) is split by steps, so
-// each workgroup gets between one and two tiles of work.
+// there are fewer tiles than workgroups, every tile; otherwise the last
+// partial wave plus one full wave is split by steps (each workgroup then
+// gets between one and two tiles of work) and the rest run whole.
 SkPlan sk_split(int64_t tiles, int64_t steps, int P)
 {
     SkPlan sp{};
@@ -1155,56 +1131,29 @@ SkPlan sk_split(int64_t tiles, int64_t steps, int P)
     return sp;
 }
 
-double sk_time(Tile t, int64_t tiles, int64_t steps, int lb, int P)
-{
-    const SkPlan sp = sk_split(tiles, steps, P);
-    const double step = step_cost(t, lb);
-    const int64_t per_wg = sp.base + (sp.extra ? 1 : 0);
-    const int64_t pieces = cdiv(steps, per_wg) + 1;     // most workgroups one tile can span
-    return (double)(sp.dp_tiles / P) * ((double)steps * step + kFill) + (double)per_wg * step +
-           2.0 * kFill + (double)pieces * partial_cost(t) + kSkFixed;
-}
-
-int64_t tiles_of(Tile t, int64_t M, int64_t N)
-{
-    const int b = t == Tile::kBig ? 256 : 128;
-    return cdiv(M, b) * cdiv(N, b);
-}
-
-// The fastest of: whole tiles on the tile choose_tile picks, or stream-K on
-// the 256 x 256 or the 128 x 128 tile.  lb: 16 or 4 (0: no stream-K).
+// lb: 16 or 4 (0: the register-staged path, no stream-K).
 Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
 {
-    Plan best;
-    best.tile = choose_tile(M, N, K);
-    if (lb == 0 || best.tile == Tile::kThin || K == 0)
-        return best;
+    Plan pl;
+    pl.tile = choose_tile(M, N, K);
+    if (lb == 0 || pl.tile == Tile::kThin || K == 0)
+        return pl;
     const int64_t steps = cdiv(K, 64);
-    double t_best = dp_time(tiles_of(best.tile, M, N), steps, step_cost(best.tile, lb), P);
-    for (Tile t : {Tile::kBig, Tile::kMid}) {
-        const int64_t tiles = tiles_of(t, M, N);
-        if (tiles % P == 0 || (t == Tile::kBig && (lb != 16 || K % 64 != 0)))
-            continue;
-        const double ts = sk_time(t, tiles, steps, lb, P);
-        if (ts < t_best) {
-            t_best = ts;
-            best.tile = t;
-            best.sk = true;
-            best.grid = P;
-            best.split = sk_split(tiles, steps, P);
-        }
+    const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
+    if (4 * tiles <= P && steps >= 64) {
+        pl.tile = Tile::kMid;
+        pl.sk = true;
+        pl.grid = P;
+        pl.split = sk_split(tiles, steps, P);
     }
-    return best;
+    return pl;
 }
 
 int64_t flag_bytes(int P) { return cdiv((int64_t)P * 4, 256) * 256; }
 
 int64_t workspace_bytes(const Plan &pl)
 {
-    if (!pl.sk)
-        return 0;
-    const int64_t tile = pl.tile == Tile::kBig ? 256 * 256 : 128 * 128;
-    return flag_bytes(pl.grid) + (int64_t)pl.grid * tile * 4;
+    return pl.sk ? flag_bytes(pl.grid) + (int64_t)pl.grid * 128 * 128 * 4 : 0;
 }
 
 // Workgroups the stream-K grid may use on the current device: one per CU,
@@ -1288,10 +1237,7 @@ int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, 
     SkPlan sp = pl.split;
     sp.flags = (uint32_t *)workspace;
     sp.partials = (float *)((char *)workspace + flag_bytes(pl.grid));
-    if (pl.tile == Tile::kBig)
-        launch_sk_big(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
-    else
-        launch_sk_mid(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
+    launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }
 

@@ -78,10 +78,12 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
  * the fp32 additions differs, and it is fixed for a given shape, so repeated
  * calls are bitwise identical.
  *
- * A persistent grid of one workgroup per CU (at most 256) computes whole
- * tiles round-robin and splits the K-steps of the remaining tiles evenly;
- * a tile split over several workgroups is summed in fp32 through
- * `workspace` and rounded to fp16 once.
+ * When the problem's 128 x 128 output tiles fill at most a quarter of the
+ * GPU's CUs and K spans at least 64 steps of 64 (K > 4032), a persistent
+ * grid of one workgroup per CU (at most 256) splits the K-steps of the
+ * tiles evenly over all workgroups; a tile split over several workgroups
+ * is summed in fp32 through `workspace` and rounded to fp16 once.  Other
+ * shapes run exactly as gemm_nt_f16.
  *
  * workspace: device memory of at least gemm_nt_f16_ws_size(M, N, K) bytes,
  *   256-byte aligned, not overlapping A, B or D, owned by the caller.  It

@@ -1,8 +1,8 @@
 """GPU parity of the stream-K entry point gemm_nt_f16_ws against the oracle.
 
-Shapes are chosen so that every form of the persistent kernel runs: 256x256
-and 128x128 tiles, fewer tiles than CUs and whole tiles followed by split
-ones, one to three contributors per tile, 4-byte loads with a K tail.  The
+Shapes are chosen so that the persistent kernel runs with 3 to 12
+contributors per tile, pieces that cross tile boundaries, a single tile
+row, and 4-byte loads with a K tail.  The
 bar is the one of the plain entry point: integer inputs bit-exact, random
 inputs within 2^-10 |D_ref| + 1e-3 sqrt(K).  The summation order is fixed
 per shape, so repeated calls must agree bit for bit, and the workspace must
@@ -21,11 +21,11 @@ from tests.gpu_util import assert_bitexact, assert_tolerance, device, note, run_
 pytestmark = pytest.mark.gpu
 
 SHAPES = [
-    (3072, 3072, 2048),      # 256x256, 144 tiles split, 2 contributors
-    (6144, 6144, 512),       # 256x256, 256 whole tiles then 320 split
-    (1024, 1024, 8192),      # 128x128, 3 contributors
-    (1536, 2048, 4096),      # 128x128, 192 tiles split
-    (2304, 2304, 1030),      # 128x128, 4-byte loads, K tail
+    (1024, 1024, 8192),      # 64 tiles, 3 contributors each
+    (768, 768, 8192),        # 36 tiles, pieces cross tile boundaries
+    (512, 640, 16384),       # 20 tiles, up to 12 contributors each
+    (900, 1000, 4098),       # ragged M, N; 4-byte loads and a K tail
+    (100, 8192, 32768),      # one tile row, K = 32768
 ]
 
 
@@ -58,7 +58,7 @@ def test_stream_k_deterministic_and_reusable():
     dev = device()
     ws = torch.zeros(max(binding.gemm_nt_f16_ws_size(*s) for s in SHAPES[:3]), dtype=torch.uint8,
                      device=dev)
-    A1, B1 = wl.uniform_inputs(8001, 3072, 3072, 2048)
+    A1, B1 = wl.uniform_inputs(8001, 768, 768, 8192)
     A2, B2 = wl.uniform_inputs(8002, 1024, 1024, 8192)
     note("stream-K reuse: shape 1 twice, shape 2, shape 1")
     d1 = run_gemm_ws(A1, B1, ws, repeat=2)
@@ -71,7 +71,7 @@ def test_stream_k_deterministic_and_reusable():
 
 
 def test_stream_k_too_small_workspace_runs_plain():
-    A, B = wl.integer_free(8100, 3072, 3072, 2048)
+    A, B = wl.integer_free(8100, 1024, 1024, 8192)
     import torch
     ws = torch.zeros(4096, dtype=torch.uint8, device=device())
     note("stream-K with a too-small workspace")
@@ -79,17 +79,18 @@ def test_stream_k_too_small_workspace_runs_plain():
     assert_bitexact(d, oracle.gemm_nt_f16(A, B), "too-small workspace")
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 2048, 8192), (3072, 3072, 3072)])
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 65536), (2048, 2048, 4096)])
 def test_stream_k_sampled_large(M, N, K):
-    # 256x256 tiles split four ways (2048^2) and the 3072^3 split; sampled
-    # entries plus the rows and columns at tile edges against the oracle.
+    # K = 65536 (1024 K-steps split over 4 workgroups per tile) and a
+    # plain-path shape through the same entry point; sampled entries plus
+    # the rows at tile edges against the oracle.
     A, B = wl.uniform_inputs(8200 + K, M, N, K)
     note(f"stream-K sampled {M}x{N}x{K}")
     d = run_gemm_ws(A, B, repeat=2)
     rng = np.random.default_rng(8300)
     flat = rng.choice(M * N, 4096, replace=False)
     rows, cols = flat // N, flat % N
-    er = wl.edge_lines(M, 256)
+    er = wl.edge_lines(M, 128)
     rr = np.repeat(er, N)
     rc = np.tile(np.arange(N), er.size)
     rows = np.concatenate([rows, rr])

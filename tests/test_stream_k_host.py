@@ -17,17 +17,14 @@ from dense_gemm_18_amd import binding
 FAKE = 0x10000000
 
 SK_SHAPES = [
-    (3072, 3072, 2048),      # 256x256 tiles, fewer tiles than CUs, 2 contributors
-    (2560, 2560, 4096),      # 256x256 tiles, 3 contributors
-    (6144, 6144, 512),       # 256x256: 256 whole tiles, then 320 split ones
-    (3072, 3072, 3072),
-    (2048, 2048, 8192),
-    (1536, 8192, 8192),
-    (1024, 1024, 8192),      # 128x128 tiles, 3 contributors
-    (1536, 2048, 4096),
-    (2304, 2304, 1030),      # 128x128, 4-byte loads and a K tail
-    (2560, 2560, 2048),
-    (1280, 1280, 8192),
+    (1024, 1024, 8192),      # 64 tiles, 4 pieces each: 3 contributors
+    (768, 768, 8192),        # 36 tiles, pieces cross tile boundaries
+    (512, 640, 16384),       # 20 tiles of 256 steps: up to 13 workgroups per tile
+    (900, 1000, 4098),       # ragged M, N; 4-byte loads and a K tail
+    (1024, 1024, 4096),
+    (100, 8192, 32768),      # one tile row
+    (65, 300, 4096),         # one tile row of 3 tiles, ragged
+    (64 * 128, 65, 8192),    # a tall single column of tiles
 ]
 
 
@@ -82,21 +79,22 @@ def test_schedule_covers_each_step_once(M, N, K):
 
 @pytest.mark.parametrize("M,N,K,bm,sk", [
     (8192, 8192, 8192, 256, 0),      # whole waves: plain launch
-    (4096, 4096, 4096, 256, 0),
-    (3000, 5000, 2048, 256, 0),      # 240 tiles: the last 16 CUs idle beats splitting
-    (1024, 1024, 1024, 128, 0),      # too small to pay for the hand-off
-    (64, 16384, 8192, 64, 0),        # thin tiles never split
-    (3072, 3072, 3072, 256, 144),
-    (2048, 2048, 8192, 256, 64),
+    (3072, 3072, 3072, 256, 0),      # 576 128x128 tiles: more than a quarter of the CUs
+    (1280, 1280, 8192, 128, 0),      # 100 tiles
+    (1024, 1024, 2048, 128, 0),      # only 32 K-steps
+    (1024, 1024, 4032, 128, 0),      # 63 K-steps
+    (1024, 1024, 4096, 128, 64),
     (1024, 1024, 8192, 128, 64),
-    (2304, 2304, 1030, 128, 324),    # K % 64 != 0: 128x128 tiles only
+    (900, 1000, 4098, 128, 64),      # 4-byte loads
+    (64, 16384, 8192, 64, 0),        # thin tiles never split
+    (1024, 1024, 8191, 128, 0),      # odd K: register-staged path, no stream-K
 ])
 def test_plan_choice(M, N, K, bm, sk):
     got = binding.gemm_nt_f16_ws_tile(M, N, K)
     assert (got[0], got[3]) == (bm, sk)
     need = binding.gemm_nt_f16_ws_size(M, N, K)
     if sk:
-        assert need == 1024 + 256 * bm * bm * 4     # 256 flag words, 256 fp32 tile slots
+        assert need == 1024 + 256 * 128 * 128 * 4  # 256 flag words, 256 fp32 128x128 slots
     else:
         assert need == 0 and binding.gemm_nt_f16_ws_items(M, N, K, 0) == []
 
@@ -123,6 +121,6 @@ def test_ws_validation_rejects_before_any_hip_call(ws, ws_bytes):
 
 def test_ws_items_rejects_bad_arguments():
     with pytest.raises(binding.GemmError):
-        binding.gemm_nt_f16_ws_items(3072, 3072, 3072, 256)      # outside the 256 workgroups
+        binding.gemm_nt_f16_ws_items(1024, 1024, 8192, 256)      # outside the 256 workgroups
     with pytest.raises(binding.GemmError):
-        binding.gemm_nt_f16_ws_items(0, 3072, 3072, 0)
+        binding.gemm_nt_f16_ws_items(0, 1024, 8192, 0)

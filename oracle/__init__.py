@@ -56,6 +56,9 @@ def _load():
     lib.oracle_gemm_nt_f16.restype = ctypes.c_int
     lib.oracle_gemm_nt_f16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
     lib.oracle_gemm_nt_f16_entries.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -120,6 +123,36 @@ def gemm_nt_f16_entries(A: np.ndarray, B: np.ndarray, rows, cols,
     _load().oracle_gemm_nt_f16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c),
                                        r.size, _ptr(out), int(threads))
     return out
+
+
+def gemm_nt_f16_ex(A: np.ndarray, B: np.ndarray, C=None, bias=None, alpha: float = 1.0,
+                   beta: float = 0.0, threads: int = 0) -> np.ndarray:
+    """D = alpha * A * B^T + beta * C + bias (bias per column) as fp16 bit
+    patterns.  alpha and beta are taken as fp32 values; C is not read when
+    beta == 0."""
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    alpha32, beta32 = float(np.float32(alpha)), float(np.float32(beta))
+    c = None
+    if beta32 != 0.0:
+        if C is None:
+            raise ValueError("beta != 0 needs C")
+        c = _bits(C)
+        if c.shape != (M, N):
+            raise ValueError(f"C has shape {c.shape}, expected {(M, N)}")
+    bb = None
+    if bias is not None:
+        bb = _bits(bias).ravel()
+        if bb.size != N:
+            raise ValueError(f"bias has {bb.size} entries, expected {N}")
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_f16_ex(_ptr(a), _ptr(b), _ptr(c) if c is not None else None,
+                                  _ptr(bb) if bb is not None else None, _ptr(d), M, N, K,
+                                  alpha32, beta32, int(threads))
+    return d
 
 
 def threads_available() -> int:

@@ -29,6 +29,17 @@
  *  - K = 0 gives D = +0 everywhere (the empty sum);
  *  - NaN results are returned as the canonical quiet NaN 0x7E00.
  *
+ * Fused epilogue (oracle_gemm_nt_f16_ex): the standard GEMM form that
+ * scales the product and adds a scaled second matrix and a bias,
+ *
+ *     D[m,n] = alpha * sum_k A[m,k] * B[n,k] + beta * C[m,n] + bias[n]
+ *
+ * with C an M x N fp16 matrix and bias one fp16 value per output column (a
+ * linear layer's bias).  Readings taken: alpha and beta are fp32 values
+ * (widened exactly); the three terms are formed and added in fp64 in the
+ * order written, and the result is rounded once to fp16; when beta == 0, C
+ * is not read (BLAS convention) and contributes nothing; a missing bias is 0.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
  */
@@ -123,13 +134,19 @@ static int pick_threads(int nthreads)
 #endif
 }
 
-/* One output entry: fp64 sum over ascending k, rounded once. */
-static uint16_t entry(const uint16_t *arow, const uint16_t *brow, int64_t K)
+/* The fp64 sum of one output entry, ascending k from +0.0. */
+static double dot(const uint16_t *arow, const uint16_t *brow, int64_t K)
 {
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k)
         acc += g_lut[arow[k]] * g_lut[brow[k]];
-    return f16_encode_rne(acc);
+    return acc;
+}
+
+/* One output entry: the sum, rounded once. */
+static uint16_t entry(const uint16_t *arow, const uint16_t *brow, int64_t K)
+{
+    return f16_encode_rne(dot(arow, brow, K));
 }
 
 /* ---- exported API ------------------------------------------------------ */
@@ -178,5 +195,27 @@ int oracle_gemm_nt_f16_entries(const uint16_t *A, const uint16_t *B,
         else
             out[i] = entry(A + m * K, B + n * K, K);
     }
+    return nt;
+}
+
+/* Full D = alpha * (A * B^T) + beta * C + bias (see the header comment).
+ * C may be NULL when beta == 0 (it is not read then); bias may be NULL. */
+int oracle_gemm_nt_f16_ex(const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                          const uint16_t *bias, uint16_t *D, int64_t M, int64_t N, int64_t K,
+                          float alpha, float beta, int nthreads)
+{
+    lut_init();
+    int nt = pick_threads(nthreads);
+    const double a = (double)alpha, b = (double)beta;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double r = a * dot(A + m * K, B + n * K, K);
+            if (b != 0.0)
+                r = r + b * g_lut[C[m * N + n]];
+            if (bias)
+                r = r + g_lut[bias[n]];
+            D[m * N + n] = f16_encode_rne(r);
+        }
     return nt;
 }

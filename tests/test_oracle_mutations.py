@@ -3,7 +3,9 @@
 Each case copies ``oracle/gemm_oracle.c`` to a temporary directory, plants one
 mistake by a textual edit (a dropped term, a wrong sign, a transposed index,
 a detour through fp32, flushed subnormals, ties rounded away, a wrong zero
-sign, saturation instead of infinity), compiles the copy with gcc, points the oracle wrapper at it and runs
+sign, saturation instead of infinity; in the fused epilogue a bias per row,
+beta or alpha on the wrong term, a transposed C, a rounding before the
+epilogue), compiles the copy with gcc, points the oracle wrapper at it and runs
 the pin battery.  At least one pin must fail for every planted mistake.  All
 of this runs on the CPU; the real oracle is not modified.
 """
@@ -17,6 +19,7 @@ from pathlib import Path
 import pytest
 
 import oracle
+from tests import test_oracle_epilogue_pins as epins
 from tests import test_oracle_pins as pins
 
 SRC = Path(oracle.__file__).resolve().parent / "gemm_oracle.c"
@@ -27,12 +30,20 @@ MUTATIONS = {
     "transposed_output": ("D[m * N + n] = entry(", "D[n * M + m] = entry("),
     "b_row_index": ("D[m * N + n] = entry(A + m * K, B + n * K, K);",
                     "D[m * N + n] = entry(A + m * K, B + ((n + 1) % N) * K, K);"),
-    "round_via_fp32": ("return f16_encode_rne(acc);", "return f16_encode_rne((double)(float)acc);"),
+    "round_via_fp32": ("return f16_encode_rne(dot(arow, brow, K));",
+                       "return f16_encode_rne((double)(float)dot(arow, brow, K));"),
     "flush_subnormals": ("v = ldexp((double)frac, -24);", "v = 0.0 * frac;"),
     "ties_away": ("if (rem > 0.5 || (rem == 0.5 && (n & 1)))", "if (rem >= 0.5)"),
     "negative_zero_start": ("double acc = 0.0;", "double acc = -0.0;"),
     "saturating_overflow": ("if (E > 15)\n        return sign | 0x7c00;\n    if (n < 1024)",
                             "if (E > 15)\n        return sign | 0x7bff;\n    if (n < 1024)"),
+    # fused epilogue
+    "bias_per_row": ("r = r + g_lut[bias[n]];", "r = r + g_lut[bias[m % N]];"),
+    "beta_scales_bias": ("r = r + g_lut[bias[n]];", "r = r + b * g_lut[bias[n]];"),
+    "alpha_scales_c": ("r = r + b * g_lut[C[m * N + n]];", "r = r + a * b * g_lut[C[m * N + n]];"),
+    "c_transposed": ("r = r + b * g_lut[C[m * N + n]];", "r = r + b * g_lut[C[(n * M + m) % (M * N)]];"),
+    "epilogue_double_rounding": ("double r = a * dot(A + m * K, B + n * K, K);",
+                                 "double r = a * g_lut[f16_encode_rne(dot(A + m * K, B + n * K, K))];"),
 }
 
 
@@ -54,6 +65,13 @@ def _battery():
         pins.test_p7_ties_and_double_rounding,
         lambda: pins.test_p8_subnormal_inputs(64),
         pins.test_p8_overflow_and_signed_zero_and_empty,
+        lambda: epins.test_e1_integer_exact(2.0, -1.0, 7, 9, 13),
+        lambda: epins.test_e1_integer_exact(-0.5, 3.0, 33, 17, 64),
+        lambda: epins.test_e2_brute_force(3, 31),
+        lambda: epins.test_e2_brute_force(16, 32),
+        epins.test_e3_zero_product_is_scaled_c_plus_bias,
+        epins.test_e4_bias_is_per_column,
+        epins.test_e5_reduces_to_plain_and_ignores_c_at_beta_zero,
     ]
 
 
@@ -77,6 +95,9 @@ def _wrap(path: Path):
     lib.oracle_gemm_nt_f16.restype = ctypes.c_int
     lib.oracle_gemm_nt_f16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
     lib.oracle_gemm_nt_f16_entries.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
     return lib
 
 

@@ -19,7 +19,8 @@ GEMM_MAX_K = 4194303
 
 # Every symbol the header declares.
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
-           "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile", "gemm_nt_f16_ws_items")
+           "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
+           "gemm_nt_f16_ws_items")
 
 
 class GemmError(RuntimeError):
@@ -59,6 +60,9 @@ def lib():
     L.gemm_nt_f16_tile.restype = ctypes.c_int
     L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
     L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
+    L.gemm_nt_f16_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
+                                 ctypes.c_float, vp]
+    L.gemm_nt_f16_ex.restype = ctypes.c_int
     L.gemm_nt_f16_ws.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
     L.gemm_nt_f16_ws.restype = ctypes.c_int
     L.gemm_nt_f16_ws_size.argtypes = [i64, i64, i64]
@@ -100,6 +104,13 @@ def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_tile_coord")
     return tm.value, tn.value
+
+
+def gemm_nt_f16_ex(A: int, B: int, C: int, bias: int, D: int, M: int, N: int, K: int,
+                   alpha: float = 1.0, beta: float = 0.0, stream: int = 0) -> int:
+    """Raw call of the fused-epilogue form (C, bias: 0 for none)."""
+    return lib().gemm_nt_f16_ex(A or None, B or None, C or None, bias or None, D or None,
+                                M, N, K, alpha, beta, stream or None)
 
 
 def gemm_nt_f16_ws(A: int, B: int, D: int, M: int, N: int, K: int, workspace: int,

@@ -134,15 +134,67 @@ __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t 
     return v;
 }
 
+// Fused epilogue of gemm_nt_f16_ex: the four consecutive columns n .. n+3
+// of row m become alpha * v + beta * C[m][n..] + bias[n..], formed in fp32
+// in that order.  beta == 0: C is not read; bias == nullptr: no bias.
+// Columns >= N are never read.  vec: C and bias are 8-byte aligned and
+// N % 4 == 0 (the same condition as D's vector stores).
+struct Epi {
+    const _Float16 *C;
+    const _Float16 *bias;
+    float alpha, beta;
+};
+
+__device__ __forceinline__ f32x4 load4(const _Float16 *p, int n, int N, int vec)
+{
+    f32x4 v;
+    if (vec) {
+        const f16x4 h = *(const f16x4 *)(p + n);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            v[r] = (float)h[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            v[r] = n + r < N ? (float)p[n + r] : 0.0f;
+    }
+    return v;
+}
+
+struct EpiFin {
+    Epi e;
+    int N, vec;
+    __device__ __forceinline__ f32x4 operator()(f32x4 v, int m, int n) const
+    {
+        v = v * e.alpha;
+        if (e.beta != 0.0f)
+            v = v + e.beta * load4(e.C + (int64_t)m * N, n, N, vec);
+        if (e.bias)
+            v = v + load4(e.bias, n, N, vec);
+        return v;
+    }
+};
+
+struct NoFin {
+    __device__ __forceinline__ f32x4 operator()(f32x4 v, int, int) const { return v; }
+};
+
+// Kernels without the fused epilogue take this empty argument instead.
+struct NoEpi {
+};
+template <bool EPI>
+using EpiArg = typename std::conditional<EPI, Epi, NoEpi>::type;
+
 // Epilogue shared by the kernels.  With B as the MFMA's first operand,
 // accumulator r of MFMA block (i, j) holds D[m][n] for
 //   m = mbase + 32 i + lane % 32,  n = nbase + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4,
 // so each group of four accumulators is four consecutive columns of one row.
 // fp32 -> fp16 uses v_cvt_f16_f32 (round to nearest even); stores are masked
 // at the M and N edges.  vec_store: D is 8-byte aligned and N % 4 == 0.
-template <int TM, int TN, class Get>
+template <int TM, int TN, class Get, class Fin = NoFin>
 __device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, int M, int N,
-                                             int mbase, int nbase, int lane, int vec_store)
+                                             int mbase, int nbase, int lane, int vec_store,
+                                             Fin fin = Fin{})
 {
     const int frow = lane & 31, fhi = lane >> 5;
 #pragma unroll
@@ -157,10 +209,11 @@ __device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + 32 * j + 8 * g + 4 * fhi;
+                const f32x4 u = fin(f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]}, m, n);
                 f16x4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)v[4 * g + r];
+                    h[r] = (_Float16)u[r];
                 if (vec_store) {
                     if (n < N)
                         *(f16x4 *)(drow + n) = h;
@@ -187,9 +240,10 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 
 // Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
 // accumulator r of block (i, j) holds D[m][n] for
 //   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
-template <int TM, int TN, class Get>
+template <int TM, int TN, class Get, class Fin = NoFin>
 __device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D, int M, int N,
-                                               int mbase, int nbase, int lane, int vec_store)
+                                               int mbase, int nbase, int lane, int vec_store,
+                                               Fin fin = Fin{})
 {
     const int frow = lane & 15, fq = lane >> 4;
 #pragma unroll
@@ -202,10 +256,11 @@ __device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D
             if (m >= M)
                 continue;
             const int n = nbase + 16 * j + 4 * fq;
+            const f32x4 u = fin(v, m, n);
             f16x4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h[r] = (_Float16)v[r];
+                h[r] = (_Float16)u[r];
             if (vec_store) {
                 if (n < N)
                     *(f16x4 *)(drow + n) = h;
@@ -228,11 +283,11 @@ __device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16
                            vec_store);
 }
 
-template <class C, int LOADB>
+template <class C, int LOADB, bool EPI>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                    _Float16 *__restrict__ D, int M, int N, int K,
-                   int tiles_m, int tiles_n, int vec_store)
+                   int tiles_m, int tiles_n, int vec_store, EpiArg<EPI> epi)
 {
     __shared__ __attribute__((aligned(16))) _Float16 smem[2 * C::STAGE];
 
@@ -333,7 +388,13 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
         __syncthreads();
     }
 
-    store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store);
+    if constexpr (EPI)
+        store_blocks<C::TM, C::TN>([&](int i, int j) { return acc[i][j]; }, D, M, N,
+                                   m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store,
+                                   EpiFin{epi, N, vec_store});
+    else
+        store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
+                                vec_store);
 }
 
 // ---------------------------------------------------------------------------
@@ -545,11 +606,11 @@ constexpr int kSpinLimit = 1 << 24;
 // KTAIL: K % BK != 0, so the last step is partial and every load carries a
 // per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
 // stream-K form; otherwise one workgroup per tile.
-template <class C, bool KTAIL, bool SK>
+template <class C, bool KTAIL, bool SK, bool EPI>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                        _Float16 *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n,
-                       int vec_store, SkPlan sk)
+                       int vec_store, SkPlan sk, EpiArg<EPI> epi)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
@@ -766,12 +827,21 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // the item's first one).
 
     auto store_d = [&]() G18_INLINE {
-        if constexpr (C::MF == 32)
+        if constexpr (EPI) {
+            auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
+            if constexpr (C::MF == 32)
+                store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
+                                           lane, vec_store, EpiFin{epi, N, vec_store});
+            else
+                store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
+                                             lane, vec_store, EpiFin{epi, N, vec_store});
+        } else if constexpr (C::MF == 32) {
             store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
                                     vec_store);
-        else
+        } else {
             store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
                                       vec_store);
+        }
     };
 
     // ---- stream-K epilogue helpers ----
@@ -949,6 +1019,21 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     }
 }
 
+// K == 0 with the fused epilogue: D = alpha * (+0) + beta * C + bias.
+__global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M, int64_t N)
+{
+    const int64_t count = M * N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float v = e.alpha * 0.0f;
+        if (e.beta != 0.0f)
+            v = v + e.beta * (float)e.C[i];
+        if (e.bias)
+            v = v + (float)e.bias[i % N];
+        D[i] = (_Float16)v;
+    }
+}
+
 // D = +0 everywhere (K == 0).
 __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 {
@@ -1033,30 +1118,40 @@ int validate(const void *A, const void *B, const void *D, int64_t M, int64_t N, 
     return GEMM_OK;
 }
 
-template <class C, int LOADB>
-void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s)
+template <bool EPI>
+EpiArg<EPI> epi_arg(const Epi &e)
 {
-    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    hipLaunchKernelGGL((gemm_nt_f16_kernel<C, LOADB>), dim3((unsigned)(tm * tn)), dim3(C::THREADS),
-                       0, s, (const _Float16 *)A, (const _Float16 *)B, (_Float16 *)D, M, N, K,
-                       tm, tn, vec);
+    if constexpr (EPI)
+        return e;
+    else
+        return NoEpi{};
 }
 
-template <class C, bool SK>
+template <class C, int LOADB, bool EPI>
+void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
+                const Epi &epi)
+{
+    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
+    hipLaunchKernelGGL((gemm_nt_f16_kernel<C, LOADB, EPI>), dim3((unsigned)(tm * tn)),
+                       dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
+                       (_Float16 *)D, M, N, K, tm, tn, vec, epi_arg<EPI>(epi));
+}
+
+template <class C, bool SK, bool EPI>
 void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
-                const SkPlan &sk, int grid)
+                const SkPlan &sk, int grid, const Epi &epi)
 {
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
     if (!SK)
         grid = tm * tn;
     if (K % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false, SK>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false, SK, EPI>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec, sk);
+                           (_Float16 *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
     else
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true, SK>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true, SK, EPI>), dim3((unsigned)grid),
                            dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec, sk);
+                           (_Float16 *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
 }
 
 // CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
@@ -1074,16 +1169,19 @@ int load_bytes(const void *A, const void *B, int64_t K)
     return 0;
 }
 
-// One workgroup per tile.
-template <class C, class CDma, class CDma4>
-void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s)
+// One workgroup per tile.  EPI: with the fused epilogue `epi`, whose C and
+// bias must then also be 8-byte aligned for vector accesses.
+template <class C, class CDma, class CDma4, bool EPI = false>
+void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
+                 const Epi &epi = Epi{})
 {
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    const uintptr_t dcb = (uintptr_t)D | (uintptr_t)epi.C | (uintptr_t)epi.bias;
+    const int vec = ((dcb & 7u) == 0 && N % 4 == 0) ? 1 : 0;
     const SkPlan none{};
     switch (load_bytes(A, B, K)) {
-    case 16: launch_dma<CDma, false>(A, B, D, M, N, K, vec, s, none, 0); return;
-    case 4: launch_dma<CDma4, false>(A, B, D, M, N, K, vec, s, none, 0); return;
-    default: launch_cfg<C, 2>(A, B, D, M, N, K, vec, s);
+    case 16: launch_dma<CDma, false, EPI>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
+    case 4: launch_dma<CDma4, false, EPI>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
+    default: launch_cfg<C, 2, EPI>(A, B, D, M, N, K, vec, s, epi);
     }
 }
 
@@ -1093,9 +1191,9 @@ void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipSt
 {
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
     if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true>(A, B, D, M, N, K, vec, s, sk, grid);
+        launch_dma<MidDma, true, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
     else
-        launch_dma<MidDma4, true>(A, B, D, M, N, K, vec, s, sk, grid);
+        launch_dma<MidDma4, true, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
 }
 
 
@@ -1282,6 +1380,52 @@ int gemm_nt_f16_ws_items(int64_t M, int64_t N, int64_t K, int64_t wg, int64_t *i
         ++*count;
     }
     return GEMM_OK;
+}
+
+int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias, void *D,
+                   int64_t M, int64_t N, int64_t K, float alpha, float beta, hipStream_t stream)
+{
+    int rc = validate(A, B, D, M, N, K);
+    if (rc != GEMM_OK)
+        return rc;
+    const uint64_t d_bytes = (uint64_t)M * (uint64_t)N * 2u;
+    auto overlaps_d = [&](const void *p, uint64_t bytes) {
+        const uintptr_t a = (uintptr_t)p, d = (uintptr_t)D;
+        return bytes && d_bytes && a < d + d_bytes && d < a + bytes;
+    };
+    if (beta != 0.0f) {
+        if ((d_bytes && !C) || ((uintptr_t)C & 1u) || (C != D && overlaps_d(C, d_bytes)))
+            return GEMM_EINVAL;
+    } else {
+        C = nullptr;                      // not read
+    }
+    if (bias && (((uintptr_t)bias & 1u) || overlaps_d(bias, (uint64_t)N * 2u)))
+        return GEMM_EINVAL;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (alpha == 1.0f && !C && !bias)
+        return gemm_nt_f16(A, B, D, M, N, K, stream);
+    const Epi epi{(const _Float16 *)C, (const _Float16 *)bias, alpha, beta};
+    if (K == 0) {
+        const int64_t count = M * N;
+        const int64_t blocks = cdiv(count, 256) < 4096 ? cdiv(count, 256) : 4096;
+        hipLaunchKernelGGL(epilogue_only_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (_Float16 *)D, epi, M, N);
+    } else {
+        switch (choose_tile(M, N, K)) {
+        case Tile::kBig:
+            launch_tile<Big, BigDma, BigDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
+            break;
+        case Tile::kMid:
+            launch_tile<Mid, MidDma, MidDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
+            break;
+        default:
+            launch_tile<Thin, ThinDma, ThinDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream,
+                                                       epi);
+            break;
+        }
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }
 
 const char *gemm_nt_f16_strerror(int code)

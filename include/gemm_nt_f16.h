@@ -70,6 +70,30 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * Fused epilogue, the standard GEMM form:
+ *
+ *     D[m,n] = alpha * sum_{k<K} A[m,k] * B[n,k] + beta * C[m,n] + bias[n]
+ *
+ * The product is the one gemm_nt_f16 computes (fp32 accumulation); the
+ * epilogue is formed in fp32 in the order written and rounded once to fp16
+ * (round to nearest even).  bias holds one value per output column, as a
+ * linear layer's bias does.
+ *
+ * C: M x N fp16, row-major, read only when beta != 0 (it may then be NULL
+ *   otherwise); it may be D itself (in place) but must not otherwise overlap
+ *   D.  bias: N fp16 values or NULL (no bias); must not overlap D.
+ * alpha, beta: fp32 scalars.  alpha == 1, beta == 0 and no bias is exactly
+ *   gemm_nt_f16.  K == 0 gives alpha * (+0) + beta * C + bias.
+ *
+ * Returns as gemm_nt_f16, and GEMM_EINVAL also for beta != 0 with a NULL C,
+ * C or bias not 2-byte aligned, C overlapping D without being D, or bias
+ * overlapping D.
+ */
+int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias, void *D,
+                   int64_t M, int64_t N, int64_t K, float alpha, float beta,
+                   hipStream_t stream);
+
+/*
  * Stream-K form of gemm_nt_f16 for shapes whose tiles do not fill whole
  * waves of the GPU's CUs (page 2, "构建 Tiled GEMM", names persistent kernels
  * with a software pipeline as the next step after its tiled kernel; page 1

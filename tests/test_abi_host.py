@@ -149,3 +149,20 @@ def test_grid_counts_from_the_pages():
     # the library's own map covers the page-2 exercise grid exactly once
     seen = {binding.gemm_nt_f16_tile_coord(w, 32, 32) for w in range(1024)}
     assert len(seen) == 1024
+
+
+@pytest.mark.parametrize("C,bias,beta", [
+    (0, 0, 1.0),                                  # beta != 0 needs C
+    (FAKE + 0x3000001, 0, 1.0),                   # C not 2-byte aligned
+    (FAKE + 0x2000000 + 8, 0, 1.0),               # C overlaps D without being D
+    (FAKE + 0x3000000, FAKE + 0x2000000 + 2, 0.0),   # bias overlaps D
+    (FAKE + 0x3000000, FAKE + 0x4000001, 0.0),    # bias not 2-byte aligned
+])
+def test_ex_validation_rejects_before_any_hip_call(C, bias, beta):
+    rc = binding.gemm_nt_f16_ex(FAKE, FAKE + 0x1000000, C, bias, FAKE + 0x2000000, 16, 16, 16,
+                                2.0, beta, 0)
+    assert rc == binding.GEMM_EINVAL
+
+
+def test_ex_empty_output_is_a_no_op():
+    assert binding.gemm_nt_f16_ex(0, FAKE, 0, 0, 0, 0, 5, 5, 2.0, 1.0, 0) == binding.GEMM_OK

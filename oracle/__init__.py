@@ -59,6 +59,14 @@ def _load():
     lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
+    lib.oracle_bf16_decode.argtypes = [p, p, i64]
+    lib.oracle_bf16_decode.restype = None
+    lib.oracle_bf16_encode.argtypes = [p, p, i64]
+    lib.oracle_bf16_encode.restype = None
+    lib.oracle_gemm_nt_bf16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_bf16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_bf16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
+    lib.oracle_gemm_nt_bf16_entries.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -153,6 +161,56 @@ def gemm_nt_f16_ex(A: np.ndarray, B: np.ndarray, C=None, bias=None, alpha: float
                                   _ptr(bb) if bb is not None else None, _ptr(d), M, N, K,
                                   alpha32, beta32, int(threads))
     return d
+
+
+def _u16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError(f"expected uint16 bit patterns, got {x.dtype}")
+    return x
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exact fp64 values."""
+    b = _u16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_bf16_decode(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def bf16_encode(values: np.ndarray) -> np.ndarray:
+    """fp64 values -> bfloat16 bit patterns, round to nearest, ties to even."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_bf16_encode(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def gemm_nt_bf16(A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
+    """Full D = A * B^T on bfloat16 bit patterns (uint16 in, uint16 out)."""
+    a, b = _u16(A), _u16(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_bf16(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(threads))
+    return d
+
+
+def gemm_nt_bf16_entries(A: np.ndarray, B: np.ndarray, rows, cols, threads: int = 0):
+    """Entries D[rows[i], cols[i]] of the bfloat16 product (uint16, 1-D)."""
+    a, b = _u16(A), _u16(B)
+    r = np.ascontiguousarray(rows, dtype=np.int64).ravel()
+    c = np.ascontiguousarray(cols, dtype=np.int64).ravel()
+    M, K = a.shape
+    N = b.shape[0]
+    if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+        raise IndexError("entry index outside D")
+    out = np.empty(r.shape, dtype=np.uint16)
+    _load().oracle_gemm_nt_bf16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c), r.size,
+                                        _ptr(out), int(threads))
+    return out
 
 
 def threads_available() -> int:

@@ -40,6 +40,11 @@
  * order written, and the result is rounded once to fp16; when beta == 0, C
  * is not read (BLAS convention) and contributes nothing; a missing bias is 0.
  *
+ * bfloat16 (oracle_gemm_nt_bf16): the same definition on bfloat16 storage
+ * (1 sign bit, 8 exponent bits with bias 127, 7 fraction bits: the upper
+ * half of an IEEE binary32), decoded exactly, summed in fp64 and rounded
+ * once to bfloat16 with round to nearest, ties to even.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
  */
@@ -109,6 +114,75 @@ static uint16_t f16_encode_rne(double x)
     if (n < 1024)                 /* only possible when E == -14       */
         return sign | (uint16_t)n;
     return sign | (uint16_t)(((E + 15) << 10) | (n - 1024));
+}
+
+/* ---- bfloat16 decode and encode ----------------------------------------
+ * Layout: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ *   exponent 0       : subnormal, value = fraction * 2^-133
+ *   exponent 1..254  : normal,    value = (128 + fraction) * 2^(exponent-134)
+ *   exponent 255     : infinity (fraction 0) or NaN                      */
+static double bf16_decode(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 7) & 0xff;
+    int frac = h & 0x7f;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -133);
+    else if (expo == 255)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + frac), expo - 134);
+    return sign ? -v : v;
+}
+
+/* fp64 -> bfloat16, round to nearest, ties to even: the same construction as
+ * f16_encode_rne with 7 fraction bits, minimum normal exponent -126 and
+ * maximum 127.                                                            */
+static uint16_t bf16_encode_rne(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a))
+        return sign | 0x7f80;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    (void)frexp(a, &e2);
+    int E = e2 - 1;               /* a in [2^E, 2^(E+1))               */
+    if (E > 127)
+        return sign | 0x7f80;
+    if (E < -126)
+        E = -126;                 /* subnormal quantum 2^-133          */
+    double scaled = ldexp(a, 7 - E);
+    double lo = floor(scaled);
+    double rem = scaled - lo;
+    long n = (long)lo;
+    if (rem > 0.5 || (rem == 0.5 && (n & 1)))
+        n += 1;
+    if (n == 256) {
+        n = 128;
+        E += 1;
+    }
+    if (E > 127)
+        return sign | 0x7f80;
+    if (n < 128)
+        return sign | (uint16_t)n;
+    return sign | (uint16_t)(((E + 127) << 7) | (n - 128));
+}
+
+static double g_lut_bf[65536];
+static int g_lut_bf_ready = 0;
+
+static void lut_bf_init(void)
+{
+    if (g_lut_bf_ready)
+        return;
+    for (int h = 0; h < 65536; ++h)
+        g_lut_bf[h] = bf16_decode((uint16_t)h);
+    g_lut_bf_ready = 1;
 }
 
 /* Decoded value of every binary16 pattern, filled once from f16_decode. */
@@ -217,5 +291,59 @@ int oracle_gemm_nt_f16_ex(const uint16_t *A, const uint16_t *B, const uint16_t *
                 r = r + g_lut[bias[n]];
             D[m * N + n] = f16_encode_rne(r);
         }
+    return nt;
+}
+
+/* ---- bfloat16 ---------------------------------------------------------- */
+
+void oracle_bf16_decode(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = bf16_decode(in[i]);
+}
+
+void oracle_bf16_encode(const double *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = bf16_encode_rne(in[i]);
+}
+
+static uint16_t entry_bf(const uint16_t *arow, const uint16_t *brow, int64_t K)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += g_lut_bf[arow[k]] * g_lut_bf[brow[k]];
+    return bf16_encode_rne(acc);
+}
+
+/* Full D = A * B^T on bfloat16 storage. */
+int oracle_gemm_nt_bf16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                        int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    lut_bf_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            D[m * N + n] = entry_bf(A + m * K, B + n * K, K);
+    return nt;
+}
+
+/* Selected entries of the bfloat16 product (index outside: 0x7FC0, NaN). */
+int oracle_gemm_nt_bf16_entries(const uint16_t *A, const uint16_t *B,
+                                int64_t M, int64_t N, int64_t K,
+                                const int64_t *rows, const int64_t *cols,
+                                int64_t count, uint16_t *out, int nthreads)
+{
+    lut_bf_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = rows[i], n = cols[i];
+        if (m < 0 || m >= M || n < 0 || n >= N)
+            out[i] = 0x7fc0;
+        else
+            out[i] = entry_bf(A + m * K, B + n * K, K);
+    }
     return nt;
 }

@@ -19,13 +19,15 @@ from pathlib import Path
 import pytest
 
 import oracle
+from tests import test_oracle_bf16_pins as bpins
 from tests import test_oracle_epilogue_pins as epins
 from tests import test_oracle_pins as pins
 
 SRC = Path(oracle.__file__).resolve().parent / "gemm_oracle.c"
 
 MUTATIONS = {
-    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k)\n        acc += g_lut[arow[k]]",
+                          "for (int64_t k = 0; k + 1 < K; ++k)\n        acc += g_lut[arow[k]]"),
     "wrong_sign": ("acc += g_lut[arow[k]] * g_lut[brow[k]];", "acc -= g_lut[arow[k]] * g_lut[brow[k]];"),
     "transposed_output": ("D[m * N + n] = entry(", "D[n * M + m] = entry("),
     "b_row_index": ("D[m * N + n] = entry(A + m * K, B + n * K, K);",
@@ -33,8 +35,10 @@ MUTATIONS = {
     "round_via_fp32": ("return f16_encode_rne(dot(arow, brow, K));",
                        "return f16_encode_rne((double)(float)dot(arow, brow, K));"),
     "flush_subnormals": ("v = ldexp((double)frac, -24);", "v = 0.0 * frac;"),
-    "ties_away": ("if (rem > 0.5 || (rem == 0.5 && (n & 1)))", "if (rem >= 0.5)"),
-    "negative_zero_start": ("double acc = 0.0;", "double acc = -0.0;"),
+    "ties_away": ("    if (rem > 0.5 || (rem == 0.5 && (n & 1)))\n        n += 1;\n    if (n == 2048)",
+                  "    if (rem >= 0.5)\n        n += 1;\n    if (n == 2048)"),
+    "negative_zero_start": ("double acc = 0.0;\n    for (int64_t k = 0; k < K; ++k)\n        acc += g_lut[arow[k]]",
+                            "double acc = -0.0;\n    for (int64_t k = 0; k < K; ++k)\n        acc += g_lut[arow[k]]"),
     "saturating_overflow": ("if (E > 15)\n        return sign | 0x7c00;\n    if (n < 1024)",
                             "if (E > 15)\n        return sign | 0x7bff;\n    if (n < 1024)"),
     # fused epilogue
@@ -44,6 +48,15 @@ MUTATIONS = {
     "c_transposed": ("r = r + b * g_lut[C[m * N + n]];", "r = r + b * g_lut[C[(n * M + m) % (M * N)]];"),
     "epilogue_double_rounding": ("double r = a * dot(A + m * K, B + n * K, K);",
                                  "double r = a * g_lut[f16_encode_rne(dot(A + m * K, B + n * K, K))];"),
+    # bfloat16
+    "bf16_exponent_bias": ("v = ldexp((double)(128 + frac), expo - 134);",
+                           "v = ldexp((double)(128 + frac), expo - 133);"),
+    "bf16_ties_away": ("    if (rem > 0.5 || (rem == 0.5 && (n & 1)))\n        n += 1;\n    if (n == 256)",
+                       "    if (rem >= 0.5)\n        n += 1;\n    if (n == 256)"),
+    "bf16_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n        acc += g_lut_bf[arow[k]] * g_lut_bf[brow[k]];",
+                          "for (int64_t k = 1; k < K; ++k)\n        acc += g_lut_bf[arow[k]] * g_lut_bf[brow[k]];"),
+    "bf16_via_fp32_rounding": ("    return bf16_encode_rne(acc);\n}",
+                               "    return bf16_encode_rne((double)(float)acc);\n}"),
 }
 
 
@@ -72,6 +85,13 @@ def _battery():
         epins.test_e3_zero_product_is_scaled_c_plus_bias,
         epins.test_e4_bias_is_per_column,
         epins.test_e5_reduces_to_plain_and_ignores_c_at_beta_zero,
+        bpins.test_b1_decode_exhaustive,
+        bpins.test_b2_encode_roundtrip_and_midpoints,
+        bpins.test_b2_encode_overflow_and_random,
+        lambda: bpins.test_b3_brute_force(8, 61),
+        lambda: bpins.test_b3_brute_force(17, 62),
+        lambda: bpins.test_b4_integer_exact_then_rounded(33, 20, 300),
+        bpins.test_b5_ties_and_double_rounding,
     ]
 
 
@@ -98,6 +118,12 @@ def _wrap(path: Path):
     lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
+    lib.oracle_bf16_decode.argtypes = [p, p, i64]
+    lib.oracle_bf16_encode.argtypes = [p, p, i64]
+    lib.oracle_gemm_nt_bf16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_bf16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_bf16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
+    lib.oracle_gemm_nt_bf16_entries.restype = ctypes.c_int
     return lib
 
 

@@ -19,7 +19,7 @@ GEMM_MAX_K = 4194303
 
 # Every symbol the header declares.
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
-           "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
+           "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
            "gemm_nt_f16_ws_items")
 
 
@@ -60,6 +60,8 @@ def lib():
     L.gemm_nt_f16_tile.restype = ctypes.c_int
     L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
     L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
+    L.gemm_nt_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_nt_bf16.restype = ctypes.c_int
     L.gemm_nt_f16_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
                                  ctypes.c_float, vp]
     L.gemm_nt_f16_ex.restype = ctypes.c_int
@@ -104,6 +106,11 @@ def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_tile_coord")
     return tm.value, tn.value
+
+
+def gemm_nt_bf16(A: int, B: int, D: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Raw call of the bfloat16 form; returns the C return code."""
+    return lib().gemm_nt_bf16(A or None, B or None, D or None, M, N, K, stream or None)
 
 
 def gemm_nt_f16_ex(A: int, B: int, C: int, bias: int, D: int, M: int, N: int, K: int,

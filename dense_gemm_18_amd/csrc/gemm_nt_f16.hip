@@ -49,10 +49,55 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element type of A, B and D: fp16, or bfloat16 (BF).  Both are 2 bytes,
+// so loads, LDS layout and swizzle are shared; the MFMA, the fragment vector
+// type and the fp32 -> storage conversion (round to nearest even) differ.
+template <bool BF>
+struct Elem {
+    using T = _Float16;
+    using x8 = f16x8;
+    using x4 = f16x4;
+};
+template <>
+struct Elem<true> {
+    using T = __bf16;
+    using x8 = bf16x8;
+    using x4 = bf16x4;
+};
+template <class T>
+struct Vec4 {
+    using type = f16x4;
+};
+template <>
+struct Vec4<__bf16> {
+    using type = bf16x4;
+};
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma16(typename Elem<BF>::x8 b, typename Elem<BF>::x8 a, f32x4 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+}
+
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma32(typename Elem<BF>::x8 b, typename Elem<BF>::x8 a,
+                                         f32x16 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+}
 
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
 constexpr int kGroupM = 4;         // tile rows per rasterisation group
@@ -191,16 +236,17 @@ using EpiArg = typename std::conditional<EPI, Epi, NoEpi>::type;
 // so each group of four accumulators is four consecutive columns of one row.
 // fp32 -> fp16 uses v_cvt_f16_f32 (round to nearest even); stores are masked
 // at the M and N edges.  vec_store: D is 8-byte aligned and N % 4 == 0.
-template <int TM, int TN, class Get, class Fin = NoFin>
-__device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, int M, int N,
+template <int TM, int TN, class T, class Get, class Fin = NoFin>
+__device__ __forceinline__ void store_blocks(Get get, T *__restrict__ D, int M, int N,
                                              int mbase, int nbase, int lane, int vec_store,
                                              Fin fin = Fin{})
 {
+    using X4 = typename Vec4<T>::type;
     const int frow = lane & 31, fhi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = mbase + 32 * i + frow;
-        _Float16 *drow = D + (int64_t)m * N;
+        T *drow = D + (int64_t)m * N;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const f32x16 v = get(i, j);
@@ -210,13 +256,13 @@ __device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, 
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + 32 * j + 8 * g + 4 * fhi;
                 const f32x4 u = fin(f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]}, m, n);
-                f16x4 h;
+                X4 h;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[r] = (_Float16)u[r];
+                    h[r] = (T)u[r];
                 if (vec_store) {
                     if (n < N)
-                        *(f16x4 *)(drow + n) = h;
+                        *(X4 *)(drow + n) = h;
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -228,8 +274,8 @@ __device__ __forceinline__ void store_blocks(Get get, _Float16 *__restrict__ D, 
     }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 *__restrict__ D,
+template <int TM, int TN, class T>
+__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], T *__restrict__ D,
                                           int M, int N, int mbase, int nbase, int lane,
                                           int vec_store)
 {
@@ -240,16 +286,17 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], _Float16 
 // Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
 // accumulator r of block (i, j) holds D[m][n] for
 //   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
-template <int TM, int TN, class Get, class Fin = NoFin>
-__device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D, int M, int N,
+template <int TM, int TN, class T, class Get, class Fin = NoFin>
+__device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M, int N,
                                                int mbase, int nbase, int lane, int vec_store,
                                                Fin fin = Fin{})
 {
+    using X4 = typename Vec4<T>::type;
     const int frow = lane & 15, fq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = mbase + 16 * i + frow;
-        _Float16 *drow = D + (int64_t)m * N;
+        T *drow = D + (int64_t)m * N;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const f32x4 v = get(i, j);
@@ -257,13 +304,13 @@ __device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D
                 continue;
             const int n = nbase + 16 * j + 4 * fq;
             const f32x4 u = fin(v, m, n);
-            f16x4 h;
+            X4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                h[r] = (_Float16)u[r];
+                h[r] = (T)u[r];
             if (vec_store) {
                 if (n < N)
-                    *(f16x4 *)(drow + n) = h;
+                    *(X4 *)(drow + n) = h;
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -274,8 +321,8 @@ __device__ __forceinline__ void store_blocks16(Get get, _Float16 *__restrict__ D
     }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16 *__restrict__ D,
+template <int TM, int TN, class T>
+__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], T *__restrict__ D,
                                             int M, int N, int mbase, int nbase, int lane,
                                             int vec_store)
 {
@@ -283,12 +330,13 @@ __device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], _Float16
                            vec_store);
 }
 
-template <class C, int LOADB, bool EPI>
+template <class C, int LOADB, bool EPI, bool BF>
 __global__ void __launch_bounds__(C::THREADS, 1)
-gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
-                   _Float16 *__restrict__ D, int M, int N, int K,
-                   int tiles_m, int tiles_n, int vec_store, EpiArg<EPI> epi)
+gemm_nt_reg_kernel(const typename Elem<BF>::T *__restrict__ A,
+                   const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
+                   int M, int N, int K, int tiles_m, int tiles_n, int vec_store, EpiArg<EPI> epi)
 {
+    using X8 = typename Elem<BF>::x8;
     __shared__ __attribute__((aligned(16))) _Float16 smem[2 * C::STAGE];
 
     const int tid = threadIdx.x;
@@ -358,18 +406,18 @@ gemm_nt_f16_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ 
 #pragma unroll
         for (int s = 0; s < kBK / 16; ++s) {
             const int ch = ((2 * s + fhi) ^ fsw) << 3;
-            f16x8 af[C::TM], bf[C::TN];
+            X8 af[C::TM], bf[C::TN];
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
-                af[i] = *(const f16x8 *)(sa + (a_row0 + 32 * i) * kBK + ch);
+                af[i] = *(const X8 *)(sa + (a_row0 + 32 * i) * kBK + ch);
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
-                bf[j] = *(const f16x8 *)(sb + (b_row0 + 32 * j) * kBK + ch);
+                bf[j] = *(const X8 *)(sb + (b_row0 + 32 * j) * kBK + ch);
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma32<BF>(bf[j], af[i], acc[i][j]);
         }
     };
 
@@ -606,12 +654,14 @@ constexpr int kSpinLimit = 1 << 24;
 // KTAIL: K % BK != 0, so the last step is partial and every load carries a
 // per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
 // stream-K form; otherwise one workgroup per tile.
-template <class C, bool KTAIL, bool SK, bool EPI>
+template <class C, bool KTAIL, bool SK, bool EPI, bool BF>
 __global__ void __launch_bounds__(C::THREADS, 1)
-gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
-                       _Float16 *__restrict__ D, int M, int N, int K, int tiles_m, int tiles_n,
-                       int vec_store, SkPlan sk, EpiArg<EPI> epi)
+gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
+                   const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
+                   int M, int N, int K, int tiles_m, int tiles_n, int vec_store, SkPlan sk,
+                   EpiArg<EPI> epi)
 {
+    using X8 = typename Elem<BF>::x8;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -725,13 +775,13 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
                                 (wn * C::WTN + frow) * C::ROW_BYTES + ch;
             }
     };
-    f16x8 fr[2][C::TM + C::TN];
-    auto read_one = [&](f16x8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
+    X8 fr[2][C::TM + C::TN];
+    auto read_one = [&](X8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
         constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
         if constexpr (q < C::TM)
-            f[q] = *(const f16x8 *)(smem + a_addr[S][t] + C::MF * q * C::ROW_BYTES);
+            f[q] = *(const X8 *)(smem + a_addr[S][t] + C::MF * q * C::ROW_BYTES);
         else
-            f[q] = *(const f16x8 *)(smem + b_addr[S][t] + C::MF * (q - C::TM) * C::ROW_BYTES);
+            f[q] = *(const X8 *)(smem + b_addr[S][t] + C::MF * (q - C::TM) * C::ROW_BYTES);
     };
 
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
@@ -753,18 +803,16 @@ gemm_nt_f16_dma_kernel(const _Float16 *__restrict__ A, const _Float16 *__restric
     // this issue order: with one wavefront per SIMD nothing else fills an
     // issue gap, and the four waves share the CU's load pipe (about 25 cycles
     // per 1 KB load), so loads are spread evenly rather than issued in a burst.
-    auto slice = [&](const f16x8 (&cur)[C::TM + C::TN], f16x8 (&nxt)[C::TM + C::TN],
+    auto slice = [&](const X8 (&cur)[C::TM + C::TN], X8 (&nxt)[C::TM + C::TN],
                      auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
                      auto l0) G18_INLINE {
         static_for<0, NM>([&](auto qc) G18_INLINE {
             constexpr int q = decltype(qc)::value;
             constexpr int i = q / C::TN, j = q % C::TN;
             if constexpr (C::MF == 32)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[C::TM + j], cur[i],
-                                                                    acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma32<BF>(cur[C::TM + j], cur[i], acc[i][j]);
             else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[C::TM + j], cur[i],
-                                                                    acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma16<BF>(cur[C::TM + j], cur[i], acc[i][j]);
             if constexpr (decltype(do_read)::value)
                 static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
                     [&](auto rc) G18_INLINE { read_one(nxt, rs, rt, rc); });
@@ -1127,31 +1175,33 @@ EpiArg<EPI> epi_arg(const Epi &e)
         return NoEpi{};
 }
 
-template <class C, int LOADB, bool EPI>
+template <class C, int LOADB, bool EPI, bool BF>
 void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
                 const Epi &epi)
 {
+    using T = typename Elem<BF>::T;
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    hipLaunchKernelGGL((gemm_nt_f16_kernel<C, LOADB, EPI>), dim3((unsigned)(tm * tn)),
-                       dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                       (_Float16 *)D, M, N, K, tm, tn, vec, epi_arg<EPI>(epi));
+    hipLaunchKernelGGL((gemm_nt_reg_kernel<C, LOADB, EPI, BF>), dim3((unsigned)(tm * tn)),
+                       dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm, tn,
+                       vec, epi_arg<EPI>(epi));
 }
 
-template <class C, bool SK, bool EPI>
+template <class C, bool SK, bool EPI, bool BF>
 void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
                 const SkPlan &sk, int grid, const Epi &epi)
 {
+    using T = typename Elem<BF>::T;
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
     if (!SK)
         grid = tm * tn;
     if (K % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, false, SK, EPI>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, SK, EPI, BF>), dim3((unsigned)grid),
+                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
+                           tn, vec, sk, epi_arg<EPI>(epi));
     else
-        hipLaunchKernelGGL((gemm_nt_f16_dma_kernel<C, true, SK, EPI>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const _Float16 *)A, (const _Float16 *)B,
-                           (_Float16 *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, SK, EPI, BF>), dim3((unsigned)grid),
+                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
+                           tn, vec, sk, epi_arg<EPI>(epi));
 }
 
 // CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
@@ -1171,7 +1221,7 @@ int load_bytes(const void *A, const void *B, int64_t K)
 
 // One workgroup per tile.  EPI: with the fused epilogue `epi`, whose C and
 // bias must then also be 8-byte aligned for vector accesses.
-template <class C, class CDma, class CDma4, bool EPI = false>
+template <class C, class CDma, class CDma4, bool EPI = false, bool BF = false>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
                  const Epi &epi = Epi{})
 {
@@ -1179,9 +1229,9 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
     const int vec = ((dcb & 7u) == 0 && N % 4 == 0) ? 1 : 0;
     const SkPlan none{};
     switch (load_bytes(A, B, K)) {
-    case 16: launch_dma<CDma, false, EPI>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    case 4: launch_dma<CDma4, false, EPI>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    default: launch_cfg<C, 2, EPI>(A, B, D, M, N, K, vec, s, epi);
+    case 16: launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
+    case 4: launch_dma<CDma4, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
+    default: launch_cfg<C, 2, EPI, BF>(A, B, D, M, N, K, vec, s, epi);
     }
 }
 
@@ -1191,9 +1241,9 @@ void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipSt
 {
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
     if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
     else
-        launch_dma<MidDma4, true, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
 }
 
 
@@ -1422,6 +1472,36 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
         default:
             launch_tile<Thin, ThinDma, ThinDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream,
                                                        epi);
+            break;
+        }
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
+}
+
+int gemm_nt_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                 hipStream_t stream)
+{
+    const int rc = validate(A, B, D, M, N, K);
+    if (rc != GEMM_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return GEMM_OK;
+    if (K == 0) {
+        const int64_t count = M * N;
+        const int64_t blocks = cdiv(count, 256) < 4096 ? cdiv(count, 256) : 4096;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (uint16_t *)D, count);
+    } else {
+        switch (choose_tile(M, N, K)) {
+        case Tile::kBig:
+            launch_tile<Big, BigDma, BigDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
+            break;
+        case Tile::kMid:
+            launch_tile<Mid, MidDma, MidDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
+            break;
+        default:
+            launch_tile<Thin, ThinDma, ThinDma4, false, true>(A, B, D, (int)M, (int)N, (int)K,
+                                                              stream);
             break;
         }
     }

@@ -143,3 +143,25 @@ def edge_lines(extent: int, tile: int) -> np.ndarray:
     cand = {0, 1, tile - 1, tile, 2 * tile - 1, 2 * tile, full - 1, full,
             extent - 2, extent - 1, 63, 64, 127, 128, 255, 256}
     return np.array(sorted(c for c in cand if 0 <= c < extent), dtype=np.int64)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float values -> bfloat16 bit patterns (uint16): round the fp32 value to
+    its upper 16 bits, nearest with ties to even (input preparation only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_uniform(seed: int, M: int, N: int, K: int):
+    """bfloat16 A [M, K], B [N, K], uniform[-1, 1] (bit patterns, uint16)."""
+    rng = np.random.default_rng(seed)
+    return (to_bf16_bits(rng.uniform(-1.0, 1.0, size=(M, K))),
+            to_bf16_bits(rng.uniform(-1.0, 1.0, size=(N, K))))
+
+
+def bf16_integers(seed: int, M: int, N: int, K: int, lo: int = -2, hi: int = 2):
+    """bfloat16 A, B with integer entries in {lo..hi} (exact in bfloat16)."""
+    rng = np.random.default_rng(seed)
+    return (to_bf16_bits(rng.integers(lo, hi + 1, size=(M, K))),
+            to_bf16_bits(rng.integers(lo, hi + 1, size=(N, K))))

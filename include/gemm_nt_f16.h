@@ -70,6 +70,15 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * The same operation on bfloat16 storage: A, B and D hold bfloat16 (1 sign,
+ * 8 exponent, 7 fraction bits), products are accumulated in fp32 and the sum
+ * is converted to bfloat16 with round-to-nearest-even.  Arguments, layout,
+ * ownership, degenerate sizes and errors exactly as gemm_nt_f16.
+ */
+int gemm_nt_bf16(const void *A, const void *B, void *D,
+                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Fused epilogue, the standard GEMM form:
  *
  *     D[m,n] = alpha * sum_{k<K} A[m,k] * B[n,k] + beta * C[m,n] + bias[n]

@@ -30,7 +30,8 @@ sys.path.insert(0, str(ROOT))
 # (AMD's published 2.5 PFLOP/s dense fp16 figure).
 PEAK_FP16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCE = ROOT / "dense_gemm_18_amd" / "csrc" / "gemm_nt_f16.hip"
+KERNEL_SOURCES = [ROOT / "dense_gemm_18_amd" / "csrc" / "gemm_kernels.h",
+                  ROOT / "dense_gemm_18_amd" / "csrc" / "gemm_nt_f16.hip"]
 TRAFFIC_SUMMARY = ROOT / "profiles" / "gemm_nt_f16_square_8192_traffic.md"
 
 
@@ -47,7 +48,7 @@ def algorithmic_bytes(M: int, N: int, K: int) -> float:
 def kernel_source_hash() -> str:
     """Hash of the kernel source's code: comments and whitespace are dropped,
     so only a change to the code itself invalidates recorded counters."""
-    text = KERNEL_SOURCE.read_text()
+    text = "\n".join(p.read_text() for p in KERNEL_SOURCES)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     code = " ".join(text.split())

@@ -8,8 +8,11 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRC = PKG / "csrc" / "gemm_nt_f16.hip"
-HEADER = ROOT / "include" / "gemm_nt_f16.h"
+CSRC = PKG / "csrc"
+# One translation unit per entry-point family; they share gemm_kernels.h and
+# compile in parallel.
+SOURCES = [CSRC / "gemm_nt_f16.hip", CSRC / "gemm_nt_f16_ex.hip", CSRC / "gemm_nt_bf16.hip"]
+HEADERS = [CSRC / "gemm_kernels.h", ROOT / "include" / "gemm_nt_f16.h"]
 LIB = PKG / "libgemm18.so"
 
 HIPCC_FLAGS = [
@@ -17,7 +20,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # Packed fp32 VALU forms stay off; hipcc's host pass warns that it does
     # not know the feature, which is harmless.
@@ -34,15 +36,33 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> Path:
-    """Compile the library; always recompiles.  Returns the library path."""
-    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
-    cmd = [hipcc(), *HIPCC_FLAGS, str(SRC), "-o", str(tmp)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
-    if verbose and res.stderr:
-        print(res.stderr)
-    os.replace(tmp, LIB)
+    """Compile every translation unit (in parallel) and link the library;
+    always recompiles.  Returns the library path."""
+    tag = f"tmp{os.getpid()}"
+    objs = [LIB.with_name(f"{src.stem}.{tag}.o") for src in SOURCES]
+    procs = [subprocess.Popen([hipcc(), *HIPCC_FLAGS, "-c", str(src), "-o", str(obj)],
+                              stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+             for src, obj in zip(SOURCES, objs)]
+    errors = []
+    for src, proc in zip(SOURCES, procs):
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            errors.append(f"{src.name}: hipcc failed ({proc.returncode}):\n{err}")
+        elif verbose and err:
+            print(err)
+    try:
+        if errors:
+            raise RuntimeError("\n".join(errors))
+        tmp = LIB.with_suffix(f".so.{tag}")
+        res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC",
+                              *map(str, objs), "-o", str(tmp)], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
+        os.replace(tmp, LIB)
+    finally:
+        for obj in objs:
+            if obj.exists():
+                obj.unlink()
     return LIB
 
 
@@ -51,7 +71,7 @@ def stale() -> bool:
     if not LIB.exists():
         return True
     t = LIB.stat().st_mtime
-    return any(p.stat().st_mtime > t for p in (SRC, HEADER))
+    return any(p.stat().st_mtime > t for p in (*SOURCES, *HEADERS))
 
 
 if __name__ == "__main__":

@@ -1,1332 +1,9 @@
-// gemm_nt_f16.hip -- dense fp16 "NT" GEMM for AMD MI355X (gfx950, CDNA4).
-//
-//   D[m,n] = sum_k A[m,k] * B[n,k]      A: M x K, B: N x K, D: M x N, fp16
-//
-// Operation, storage types (fp16 in and out, fp32 accumulator) and the
-// NT layout follow page "构建 Tiled GEMM" ("Building a Tiled GEMM", mlc.ai
-// modern-gpu-programming-for-mlsys, chapter gemm_basics), section "GEMM".
-// The kernel design is gfx950's own; what it keeps from the pages is listed
-// next to each part.
-//
-// One workgroup computes one BM x BN output tile:
-//   * Tile -> workgroup map: an XCD-aware remap (consecutive workgroup ids
-//     land on different XCDs, each with its own L2) followed by grouped
-//     rasterisation, so tiles that share A rows or B rows run on one XCD.
-//     Page 2's step 3 ("第 3 步：空间 Tiling（Multi-CTA）", section
-//     "Grid 映射") maps the grid straight onto tiles with no reuse between
-//     blocks; page 1 ("内核 4：生产级调优") notes that a larger M tile
-//     improves L2 reuse of B.
-//   * Global -> LDS staging: A and B are both K-contiguous, so one loader
-//     serves both.  Each lane moves 16-byte chunks (8 fp16 along K), or
-//     4-byte pieces of them when K is not a multiple of 8, with buffer loads
-//     that write LDS directly; 8 lanes cover one 128-byte row of a K-step, so
-//     the accesses are fully coalesced (page 1, "内核 1：共享内存分块", shows
-//     the cooperative coalesced tile copy).  The buffer resource of each
-//     workgroup spans only its valid rows, so rows past M or N read as zero
-//     in hardware; K tails are masked per load.
-//   * LDS layout: rows of 64 fp16 (128 B = eight 16-byte chunks), chunk index
-//     XOR-swizzled by the row so that the MFMA fragment reader is free of
-//     bank conflicts (page 1, "为什么 swizzle 重要", explains the conflict
-//     the swizzle removes).  A ring of stages keeps the loads for later
-//     K-steps in flight while the MFMAs of the current one run (page 1,
-//     "内核 4", double buffering with STAGES = 2).
-//   * MFMA: v_mfma_f32_16x16x32_f16 (32x32x16 in two configurations), fp32
-//     accumulators in registers.  The B tile is fed as the instruction's
-//     first operand and the A tile as its second, so each lane's
-//     accumulators hold 4 consecutive columns n of D for one row m and the
-//     epilogue writes 8-byte vectors.
-//   * Epilogue: fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even),
-//     masked at the M and N edges.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <atomic>
-#include <type_traits>
-
-#include "gemm_nt_f16.h"
-
-namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Element type of A, B and D: fp16, or bfloat16 (BF).  Both are 2 bytes,
-// so loads, LDS layout and swizzle are shared; the MFMA, the fragment vector
-// type and the fp32 -> storage conversion (round to nearest even) differ.
-template <bool BF>
-struct Elem {
-    using T = _Float16;
-    using x8 = f16x8;
-    using x4 = f16x4;
-};
-template <>
-struct Elem<true> {
-    using T = __bf16;
-    using x8 = bf16x8;
-    using x4 = bf16x4;
-};
-template <class T>
-struct Vec4 {
-    using type = f16x4;
-};
-template <>
-struct Vec4<__bf16> {
-    using type = bf16x4;
-};
-
-template <bool BF>
-__device__ __forceinline__ f32x4 mfma16(typename Elem<BF>::x8 b, typename Elem<BF>::x8 a, f32x4 c)
-{
-    if constexpr (BF)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
-}
-
-template <bool BF>
-__device__ __forceinline__ f32x16 mfma32(typename Elem<BF>::x8 b, typename Elem<BF>::x8 a,
-                                         f32x16 c)
-{
-    if constexpr (BF)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
-}
-
-constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
-constexpr int kGroupM = 4;         // tile rows per rasterisation group
-constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr uint32_t kOob = 0x80000000u;   // a buffer offset past every range
-constexpr int kRsrcFlags = 0x00020000;   // gfx9 buffer descriptor word 3
-
-// ---------------------------------------------------------------------------
-// Tile -> workgroup map (shared by the kernels and the host introspection).
-__host__ __device__ inline void tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n,
-                                           int64_t &tm, int64_t &tn)
-{
-    const int64_t total = tiles_m * tiles_n;
-    // Hardware deals workgroup ids round-robin over the XCDs; give every XCD
-    // a contiguous range of logical ids.
-    const int64_t q = total / kXcds, r = total % kXcds;
-    const int64_t x = wg % kXcds, i = wg / kXcds;
-    const int64_t logical = x * q + (x < r ? x : r) + i;
-    // Grouped rasterisation: kGroupM tile rows at a time, rows fastest.
-    const int64_t per_group = (int64_t)kGroupM * tiles_n;
-    const int64_t g = logical / per_group;
-    const int64_t first_m = g * kGroupM;
-    const int64_t rows = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-    const int64_t within = logical - g * per_group;
-    tm = first_m + within % rows;
-    tn = within / rows;
-}
-
-// Swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Any 8
-// consecutive rows take 8 distinct chunks, and so do the 8 even and the 8
-// odd rows among any 16 consecutive ones: a column of 16 B per row read by
-// consecutive lanes touches every bank once, whether the LDS serves 128 or
-// 256 bytes per clock.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// ---------------------------------------------------------------------------
-// Tile configuration.
-template <int BM_, int BN_, int WM_, int WN_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int THREADS = WM * WN * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA blocks per wave
-    static constexpr int CA = BM * 8 / THREADS;             // A chunks per thread per K-step
-    static constexpr int CB = BN * 8 / THREADS;
-    static constexpr int STAGE = (BM + BN) * kBK;           // fp16 elements per LDS stage
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
-    static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "chunks must split evenly");
-    static_assert(THREADS % 8 == 0, "8 lanes per LDS row");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
-};
-
-// Load one chunk (8 fp16 along K) of a row panel.  `off` is the byte offset
-// of the chunk's first element, `k` its K index.  LOADB is the width of one
-// load: 16 (K % 8 == 0, 16-byte aligned panel), 4 (K even, 4-byte aligned)
-// or 2 (anything).  Elements with k >= K read as zero; rows past the panel's
-// valid rows lie past the buffer range and read as zero in hardware.
-template <int LOADB>
-__device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off, int k, int K)
-{
-    u32x4 v;
-    if constexpr (LOADB == 16) {
-        v = __builtin_amdgcn_raw_buffer_load_b128(rs, k < K ? off : kOob, 0, 0);
-    } else if constexpr (LOADB == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, k + 2 * j < K ? off + 4 * j : kOob, 0, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, k + 2 * j < K ? off + 4 * j : kOob, 0, 0);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, k + 2 * j + 1 < K ? off + 4 * j + 2 : kOob, 0, 0);
-            v[j] = lo | (hi << 16);
-        }
-    }
-    return v;
-}
-
-// Fused epilogue of gemm_nt_f16_ex: the four consecutive columns n .. n+3
-// of row m become alpha * v + beta * C[m][n..] + bias[n..], formed in fp32
-// in that order.  beta == 0: C is not read; bias == nullptr: no bias.
-// Columns >= N are never read.  vec: C and bias are 8-byte aligned and
-// N % 4 == 0 (the same condition as D's vector stores).
-struct Epi {
-    const _Float16 *C;
-    const _Float16 *bias;
-    float alpha, beta;
-};
-
-__device__ __forceinline__ f32x4 load4(const _Float16 *p, int n, int N, int vec)
-{
-    f32x4 v;
-    if (vec) {
-        const f16x4 h = *(const f16x4 *)(p + n);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            v[r] = (float)h[r];
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            v[r] = n + r < N ? (float)p[n + r] : 0.0f;
-    }
-    return v;
-}
-
-struct EpiFin {
-    Epi e;
-    int N, vec;
-    __device__ __forceinline__ f32x4 operator()(f32x4 v, int m, int n) const
-    {
-        v = v * e.alpha;
-        if (e.beta != 0.0f)
-            v = v + e.beta * load4(e.C + (int64_t)m * N, n, N, vec);
-        if (e.bias)
-            v = v + load4(e.bias, n, N, vec);
-        return v;
-    }
-};
-
-struct NoFin {
-    __device__ __forceinline__ f32x4 operator()(f32x4 v, int, int) const { return v; }
-};
-
-// Kernels without the fused epilogue take this empty argument instead.
-struct NoEpi {
-};
-template <bool EPI>
-using EpiArg = typename std::conditional<EPI, Epi, NoEpi>::type;
-
-// Epilogue shared by the kernels.  With B as the MFMA's first operand,
-// accumulator r of MFMA block (i, j) holds D[m][n] for
-//   m = mbase + 32 i + lane % 32,  n = nbase + 32 j + 8 (r / 4) + 4 (lane / 32) + r % 4,
-// so each group of four accumulators is four consecutive columns of one row.
-// fp32 -> fp16 uses v_cvt_f16_f32 (round to nearest even); stores are masked
-// at the M and N edges.  vec_store: D is 8-byte aligned and N % 4 == 0.
-template <int TM, int TN, class T, class Get, class Fin = NoFin>
-__device__ __forceinline__ void store_blocks(Get get, T *__restrict__ D, int M, int N,
-                                             int mbase, int nbase, int lane, int vec_store,
-                                             Fin fin = Fin{})
-{
-    using X4 = typename Vec4<T>::type;
-    const int frow = lane & 31, fhi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = mbase + 32 * i + frow;
-        T *drow = D + (int64_t)m * N;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const f32x16 v = get(i, j);
-            if (m >= M)
-                continue;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = nbase + 32 * j + 8 * g + 4 * fhi;
-                const f32x4 u = fin(f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]}, m, n);
-                X4 h;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[r] = (T)u[r];
-                if (vec_store) {
-                    if (n < N)
-                        *(X4 *)(drow + n) = h;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            drow[n + r] = h[r];
-                }
-            }
-        }
-    }
-}
-
-template <int TM, int TN, class T>
-__device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], T *__restrict__ D,
-                                          int M, int N, int mbase, int nbase, int lane,
-                                          int vec_store)
-{
-    store_blocks<TM, TN>([&](int i, int j) { return acc[i][j]; }, D, M, N, mbase, nbase, lane,
-                         vec_store);
-}
-
-// Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
-// accumulator r of block (i, j) holds D[m][n] for
-//   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
-template <int TM, int TN, class T, class Get, class Fin = NoFin>
-__device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M, int N,
-                                               int mbase, int nbase, int lane, int vec_store,
-                                               Fin fin = Fin{})
-{
-    using X4 = typename Vec4<T>::type;
-    const int frow = lane & 15, fq = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = mbase + 16 * i + frow;
-        T *drow = D + (int64_t)m * N;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const f32x4 v = get(i, j);
-            if (m >= M)
-                continue;
-            const int n = nbase + 16 * j + 4 * fq;
-            const f32x4 u = fin(v, m, n);
-            X4 h;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                h[r] = (T)u[r];
-            if (vec_store) {
-                if (n < N)
-                    *(X4 *)(drow + n) = h;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < N)
-                        drow[n + r] = h[r];
-            }
-        }
-    }
-}
-
-template <int TM, int TN, class T>
-__device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], T *__restrict__ D,
-                                            int M, int N, int mbase, int nbase, int lane,
-                                            int vec_store)
-{
-    store_blocks16<TM, TN>([&](int i, int j) { return acc[i][j]; }, D, M, N, mbase, nbase, lane,
-                           vec_store);
-}
-
-template <class C, int LOADB, bool EPI, bool BF>
-__global__ void __launch_bounds__(C::THREADS, 1)
-gemm_nt_reg_kernel(const typename Elem<BF>::T *__restrict__ A,
-                   const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
-                   int M, int N, int K, int tiles_m, int tiles_n, int vec_store, EpiArg<EPI> epi)
-{
-    using X8 = typename Elem<BF>::x8;
-    __shared__ __attribute__((aligned(16))) _Float16 smem[2 * C::STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave % C::WM, wn = wave / C::WM;
-
-    int64_t tm64, tn64;
-    tile_coord(blockIdx.x, tiles_m, tiles_n, tm64, tn64);
-    const int m0 = (int)tm64 * C::BM, n0 = (int)tn64 * C::BN;
-    const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
-
-    // Buffer resources spanning only this tile's valid rows.
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + (int64_t)m0 * K), (short)0, rows_a * K * 2, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(B + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcFlags);
-
-    // Loader mapping: thread t moves chunk (t & 7) of rows (t >> 3) + i * THREADS/8.
-    const int lrow = tid >> 3, lch = tid & 7;
-    constexpr int ROWS_PER_PASS = C::THREADS / 8;
-    const uint32_t row_bytes = (uint32_t)K * 2;
-
-    u32x4 stA[C::CA], stB[C::CB];
-    auto load_tiles = [&](int k0) {
-        const int k = k0 + lch * 8;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i)
-            stA[i] = load_chunk<LOADB>(ra, (uint32_t)(lrow + i * ROWS_PER_PASS) * row_bytes + (uint32_t)k * 2, k, K);
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i)
-            stB[i] = load_chunk<LOADB>(rb, (uint32_t)(lrow + i * ROWS_PER_PASS) * row_bytes + (uint32_t)k * 2, k, K);
-    };
-    auto store_tiles = [&](int stage) {
-        _Float16 *sa = smem + stage * C::STAGE;
-        _Float16 *sb = sa + C::BM * kBK;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i) {
-            const int row = lrow + i * ROWS_PER_PASS;
-            *(u32x4 *)(sa + row * kBK + ((lch ^ swz(row)) << 3)) = stA[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i) {
-            const int row = lrow + i * ROWS_PER_PASS;
-            *(u32x4 *)(sb + row * kBK + ((lch ^ swz(row)) << 3)) = stB[i];
-        }
-    };
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = f32x16{};
-
-    // MFMA fragment rows of this lane (same pattern for A and B: both are
-    // K-contiguous).  Lane l supplies row l % 32 and K chunk 2s + l / 32 of
-    // each 16-wide K slice s.
-    const int frow = lane & 31, fhi = lane >> 5;
-    const int a_row0 = wm * C::WTM + frow;
-    const int b_row0 = wn * C::WTN + frow;
-    const int fsw = swz(frow);   // rows differ from frow by multiples of 32
-
-    auto compute = [&](int stage) {
-        const _Float16 *sa = smem + stage * C::STAGE;
-        const _Float16 *sb = sa + C::BM * kBK;
-#pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            const int ch = ((2 * s + fhi) ^ fsw) << 3;
-            X8 af[C::TM], bf[C::TN];
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-                af[i] = *(const X8 *)(sa + (a_row0 + 32 * i) * kBK + ch);
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                bf[j] = *(const X8 *)(sb + (b_row0 + 32 * j) * kBK + ch);
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = mfma32<BF>(bf[j], af[i], acc[i][j]);
-        }
-    };
-
-    const int nk = (K + kBK - 1) / kBK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more)
-            load_tiles((kt + 1) * kBK);
-        compute(cur);
-        if (more)
-            store_tiles(cur ^ 1);
-        __syncthreads();
-    }
-
-    if constexpr (EPI)
-        store_blocks<C::TM, C::TN>([&](int i, int j) { return acc[i][j]; }, D, M, N,
-                                   m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store,
-                                   EpiFin{epi, N, vec_store});
-    else
-        store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                vec_store);
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS kernel (fast path: K % 8 == 0, A and B 16-byte aligned).
-//
-// gfx950's buffer_load_dwordx4 ... lds writes each lane's 16 bytes straight
-// into LDS, at M0 + 16 * lane: one instruction fills 1024 contiguous bytes
-// and needs no staging registers and no ds_write.  That leaves room for a
-// ring of NSTAGE LDS stages of BK = 32, so the loads for K-step u + NSTAGE - 1
-// are in flight while step u is multiplied (page 1, "内核 3：Warp 特化" and
-// "内核 4", overlaps loads with MMAs through a STAGES-deep ring; here one
-// wavefront both loads and multiplies, and the ring is tracked with vmcnt
-// and one workgroup barrier per K-step instead of full/empty events).
-//
-// LDS rows are BK fp16 (64 or 128 bytes, four or eight 16-byte chunks).  The
-// swizzle is applied on the global side: LDS slot (row, chunk) receives
-// global chunk chunk ^ swz_row(row) of that row.  Both swizzles were chosen
-// by measuring SQ_LDS_BANK_CONFLICT for the MFMA fragment read pattern
-// (32 rows x 16 bytes per half wave) on gfx950: zero conflicts.
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct-to-LDS buffer load of LB bytes per lane.  The size is spelled as a
-// literal in each branch: the builtin's host-side check of a dependent size
-// argument rejects 16 (a gfx950-only width) and silently drops the kernel.
-template <int LB>
-__device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, char *dst, uint32_t voff,
-                                         uint32_t soff)
-{
-    if constexpr (LB == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
-    else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-
-// 128-byte rows read by 16x16x32 fragments (16 rows x 16 bytes per quarter
-// wave): measured conflict-free, and also for the 32x32x16 pattern.
-__device__ __forceinline__ int swz128_q(int row) { return (row >> 1) & 7; }
-
-// Chunk swizzle of an LDS row of BK fp16 read by MF x MF MFMA fragments.
-template <int BK, int MF>
-__device__ __forceinline__ int swz_row(int row)
-{
-    return BK == 64 ? (MF == 32 ? swz(row) : swz128_q(row)) : swz64(row);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt
-// left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Kernel-local lambdas must always inline: an out-of-line call would keep
-// every array they capture by reference in scratch memory.
-#define G18_INLINE __attribute__((always_inline))
-
-// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1, so that
-// register arrays are only ever indexed by constants.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for every
-// outstanding direct-to-LDS load, prefetches included).  This wave's LDS
-// reads complete first (lgkmcnt 0, issued as the builtin so the compiler's
-// own wait tracking sees it); the empty asm with a "memory" clobber keeps
-// the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_, bool SPLIT_>
-struct DmaCfg {
-    // LB: bytes one lane moves per load: 16 (buffer_load_dwordx4 ... lds,
-    // needs K % 8 == 0 and 16-byte aligned operands) or 4 (buffer_load_dword
-    // ... lds, needs K even and 4-byte aligned operands).
-    static constexpr int LB = LB_;
-    // SPLIT: a step's loads are issued half in the slice after the barrier
-    // and half in the next step's first slice; otherwise all of them in the
-    // slice after the barrier (which gives every load the longest time to
-    // land when a step has only two slices).
-    static constexpr bool SPLIT = SPLIT_;
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NSTAGE = NSTAGE_;
-    static constexpr int BK = BK_;
-    // MF = 32: v_mfma_f32_32x32x16_f16; MF = 16: v_mfma_f32_16x16x32_f16.
-    static constexpr int MF = MF_;
-    static constexpr int KSL = MF == 32 ? 16 : 32;           // K per MFMA (one slice)
-    static constexpr int SLICES = BK / KSL;                  // slices per step
-    static constexpr int CHS = KSL / 8;                      // 16-byte chunks per slice
-    static constexpr int CPR = BK / 8;                       // 16-byte chunks per LDS row
-    static constexpr int NWAVES = WM * WN, THREADS = NWAVES * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int TM = WTM / MF, TN = WTN / MF;
-    using acc_t = typename std::conditional<MF == 32, f32x16, f32x4>::type;
-    static constexpr int ROW_BYTES = BK * 2;                 // 64 or 128
-    static constexpr int INST_BYTES = 64 * LB;               // LDS bytes one load instruction fills
-    static constexpr int ROWS_PER_INST = INST_BYTES / ROW_BYTES;
-    static constexpr int LPR = ROW_BYTES / LB;               // lanes per LDS row in one load
-    static constexpr int A_LOADS = BM / ROWS_PER_INST / NWAVES;   // per wave per stage
-    static constexpr int B_LOADS = BN / ROWS_PER_INST / NWAVES;
-    static constexpr int LPS = A_LOADS + B_LOADS;            // vmcnt units per stage
-    static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-    static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-    static_assert(MF == 32 || MF == 16, "MFMA block of 32x32 or 16x16");
-    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
-    static_assert(BM % (ROWS_PER_INST * NWAVES) == 0 && BN % (ROWS_PER_INST * NWAVES) == 0,
-                  "load instructions must split evenly over the waves");
-    static_assert(BK == 32 || BK == 64, "LDS rows of 64 or 128 bytes");
-    static_assert(LB == 16 || LB == 4, "16- or 4-byte loads");
-    static_assert(ROWS_PER_INST >= 1, "a load covers whole LDS rows");
-    // The largest vmcnt the pipeline waits on (prologue) must be encodable.
-    static_assert(NSTAGE >= 2 && LPS * (NSTAGE - 2) + LPS / 2 < 64, "vmcnt budget");
-    static_assert(SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
-    static_assert(SPLIT || LPS * (NSTAGE - 1) < 64, "vmcnt budget");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
-};
-
-// Stream-K work split of a persistent grid of P workgroups (one per CU, all
-// resident at once).  Tiles [0, dp_tiles) are whole tiles, dealt round-robin
-// (dp_tiles is a multiple of P, so every workgroup gets as many).  The K-steps
-// of tiles [dp_tiles, dp_tiles + sk_tiles), in tile-major order, are split
-// into P contiguous ranges: workgroup w gets base + (w < extra) of them.
-// A tile split over several workgroups is finished by its owner, the one that
-// runs the tile's first step: every other contributor starts its range inside
-// that tile, writes its fp32 partial sums to its own slot and raises its flag;
-// the owner adds the slots in ascending workgroup order (so results do not
-// depend on timing), rounds once to fp16, and lowers the flags again.
-struct SkPlan {
-    int dp_tiles, sk_tiles;
-    int base, extra;
-    uint32_t *flags;      // P words; zero before the call, zero after it
-    float *partials;      // P slots of BM * BN floats
-};
-
-// One work item of workgroup w: K-steps [s0, s1) of `tile`.  s0 > 0: w is a
-// contributor to that tile.  Otherwise w writes the tile, adding the partial
-// sums of workgroups w_first .. w_last (none when w_first > w_last).
-struct SkItem {
-    int tile, s0, s1, w_first, w_last;
-};
-
-// Walks workgroup w's items: its whole tiles w, w + P, ... below dp_tiles,
-// then the pieces of its stream-K range, each ending at a tile boundary or
-// at the range end.  Host and device run the same code (the host to test it).
-struct SkCursor {
-    int t_dp, i, iend;
-};
-
-__host__ __device__ inline int sk_wg_of(const SkPlan &sk, int i)   // the workgroup whose range holds step i
-{
-    const int cut = sk.extra * (sk.base + 1);
-    return i < cut ? i / (sk.base + 1) : sk.extra + (sk.base ? (i - cut) / sk.base : 0);
-}
-
-__host__ __device__ inline SkCursor sk_begin(const SkPlan &sk, int w)
-{
-    const int i = w * sk.base + (w < sk.extra ? w : sk.extra);
-    return SkCursor{w, i, i + sk.base + (w < sk.extra ? 1 : 0)};
-}
-
-__host__ __device__ inline bool sk_next(const SkPlan &sk, int nk, int P, SkCursor &c, SkItem &it)
-{
-    it.w_first = 1;
-    it.w_last = 0;
-    if (c.t_dp < sk.dp_tiles) {
-        it.tile = c.t_dp;
-        it.s0 = 0;
-        it.s1 = nk;
-        c.t_dp += P;
-        return true;
-    }
-    if (c.i >= c.iend)
-        return false;
-    const int j = c.i / nk;
-    it.s0 = c.i - j * nk;
-    it.s1 = it.s0 + (c.iend - c.i) < nk ? it.s0 + (c.iend - c.i) : nk;
-    it.tile = sk.dp_tiles + j;
-    c.i += it.s1 - it.s0;
-    if (it.s0 == 0 && it.s1 < nk) {
-        it.w_first = sk_wg_of(sk, j * nk + it.s1);
-        it.w_last = sk_wg_of(sk, j * nk + nk - 1);
-    }
-    return true;
-}
-
-// Polls of a contributor's flag before an owner gives up (~5 s at 1.6 GHz):
-// the tile is then written as NaN and the kernel still ends.  Every wave
-// polls for itself: the kernel keeps a single LDS object (a second one, to
-// broadcast the result, costs the compiler its proof that fragment reads do
-// not overlap in-flight direct-to-LDS loads, and it then waits for all of
-// them before every read).
-constexpr int kSpinLimit = 1 << 24;
-
-// KTAIL: K % BK != 0, so the last step is partial and every load carries a
-// per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
-// stream-K form; otherwise one workgroup per tile.
-template <class C, bool KTAIL, bool SK, bool EPI, bool BF>
-__global__ void __launch_bounds__(C::THREADS, 1)
-gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
-                   const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
-                   int M, int N, int K, int tiles_m, int tiles_n, int vec_store, SkPlan sk,
-                   EpiArg<EPI> epi)
-{
-    using X8 = typename Elem<BF>::x8;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
-    const int wm = wave % C::WM, wn = wave / C::WM;
-
-    // The current work item: tile origin (m0, n0), buffer resources spanning
-    // the tile's valid rows of A and B, and its K-steps [s0, s0 + n).
-    int m0 = 0, n0 = 0, kb = 0, n = 0;
-    __amdgpu_buffer_rsrc_t ra, rb;
-    // Zero-length resource: every load through it reads zero.  Steps past the
-    // end of the item use it, chosen per step in scalar registers.
-    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)A, (short)0, 0, kRsrcFlags);
-    const int nk = (K + C::BK - 1) / C::BK;
-    auto set_item = [&](int tile, int s0, int s1) G18_INLINE {
-        int64_t tm64, tn64;
-        tile_coord(tile, tiles_m, tiles_n, tm64, tn64);
-        m0 = (int)tm64 * C::BM;
-        n0 = (int)tn64 * C::BN;
-        const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
-        ra = __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0,
-                                               rows_a * K * 2, kRsrcFlags);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0,
-                                               rows_b * K * 2, kRsrcFlags);
-        kb = s0 * C::BK;
-        n = s1 - s0;
-    };
-
-    // This lane's part of each load instruction: LDS slot `lane` of a block
-    // of ROWS_PER_INST rows is row lane / CPR, chunk lane % CPR; it fetches
-    // the global chunk that the swizzle places there.  Instruction i of this
-    // wave covers rows ROWS_PER_INST * (wave + NWAVES * i) and up.  The
-    // vector offsets carry rows and chunks only; a step's K offset travels in
-    // the scalar offset, so a full step issues its loads with no VALU work.
-    // With LB = 4 a lane moves one 4-byte quarter of a chunk (intra-chunk
-    // byte offset `sub`).
-    //
-    // These per-lane values, and the fragment addresses below, are set up
-    // per work item from `ln`, a copy of the lane id that the compiler must
-    // treat as changing: otherwise it keeps them live across the persistent
-    // loop's epilogues, where the 256 accumulators leave no registers free.
-    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
-    int a_k[C::A_LOADS], b_k[C::B_LOADS];
-    auto setup_loads = [&](int ln) G18_INLINE {
-        const int slot_row = ln / C::LPR;
-        const int slot_byte = (ln % C::LPR) * C::LB;
-        const int sub = slot_byte % 16;
-#pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) {
-            const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-            const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-            a_k[i] = gch * 8 + sub / 2;
-            a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
-        }
-#pragma unroll
-        for (int i = 0; i < C::B_LOADS; ++i) {
-            const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
-            const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-            b_k[i] = gch * 8 + sub / 2;
-            b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
-        }
-    };
-
-    // One global->LDS load q of step `step` into stage S: q < A_LOADS moves
-    // A rows, the rest B rows; each instruction fills 1024 contiguous LDS
-    // bytes.  Rows past the tile's valid rows lie past the buffer range and
-    // read as zero; steps past the end load through the zero-length
-    // resource; with KTAIL, chunks with k >= K get an out-of-range offset.
-    auto issue_one = [&](int step, auto sc, auto qc) G18_INLINE {
-        constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
-        const int k0 = kb + step * C::BK;
-        const bool live = step < n;
-        char *stage = smem + S * C::STAGE_BYTES;
-        if constexpr (q < C::A_LOADS) {
-            uint32_t off = a_off[q];
-            if constexpr (KTAIL)
-                off = (k0 + a_k[q] < K) ? off : kOob;
-            char *dst = stage + (wave + C::NWAVES * q) * C::INST_BYTES;
-            load_lds<C::LB>(live ? ra : rz, dst, off, k0 * 2);
-        } else {
-            constexpr int i = q - C::A_LOADS;
-            uint32_t off = b_off[i];
-            if constexpr (KTAIL)
-                off = (k0 + b_k[i] < K) ? off : kOob;
-            char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * C::INST_BYTES;
-            load_lds<C::LB>(live ? rb : rz, dst, off, k0 * 2);
-        }
-    };
-
-    typename C::acc_t acc[C::TM][C::TN];
-
-    // Fragments of one K slice (16 wide for 32x32x16, 32 wide for 16x16x32):
-    // lane l holds row l % MF of each MF-row block and K chunk
-    // CHS * t + l / MF of slice t (the same pattern for A and B, which are
-    // both K-contiguous).  Fragment q < TM is A block q, the rest B blocks.
-    // The LDS address of every (stage, slice) is precomputed, so a fragment
-    // read is one ds_read_b128 with an immediate offset.
-    uint32_t a_addr[C::NSTAGE][C::SLICES], b_addr[C::NSTAGE][C::SLICES];
-    auto setup_reads = [&](int ln) G18_INLINE {
-        const int frow = ln % C::MF, fhi = ln / C::MF;
-        const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
-#pragma unroll
-        for (int st = 0; st < C::NSTAGE; ++st)
-#pragma unroll
-            for (int t = 0; t < C::SLICES; ++t) {
-                const uint32_t ch = (uint32_t)(((C::CHS * t + fhi) ^ fsw) * 16);
-                a_addr[st][t] = st * C::STAGE_BYTES + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
-                b_addr[st][t] = st * C::STAGE_BYTES + C::BM * C::ROW_BYTES +
-                                (wn * C::WTN + frow) * C::ROW_BYTES + ch;
-            }
-    };
-    X8 fr[2][C::TM + C::TN];
-    auto read_one = [&](X8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
-        constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
-        if constexpr (q < C::TM)
-            f[q] = *(const X8 *)(smem + a_addr[S][t] + C::MF * q * C::ROW_BYTES);
-        else
-            f[q] = *(const X8 *)(smem + b_addr[S][t] + C::MF * (q - C::TM) * C::ROW_BYTES);
-    };
-
-    constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
-    constexpr int LHALF = C::LPS / 2;
-    // Loads issued in one slice: half a step's or a whole step's.
-    constexpr int LSL = C::SPLIT ? LHALF : C::LPS;
-    // Spacing of the loads over the NM MFMAs of a slice: one load every
-    // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
-    // than MFMAs (small tiles); the same for fragment reads (RPG).
-    constexpr int LSPACE = NM >= LSL ? NM / LSL : 1;
-    constexpr int LPG = NM >= LSL ? 1 : LSL / NM;
-    constexpr int RPG = (NR + NM - 1) / NM;
-    static_assert(C::LPS % 2 == 0 && (NM % LSL == 0 || LSL % NM == 0),
-                  "loads split evenly over the slices that issue them");
-
-    // One slice: MFMA q of TM x TN, each followed by its share of fragment
-    // reads for the next slice (stage RS, slice RT) and of the loads l0, l0+1,
-    // ... of step lstep into stage LS.  The scheduling fences keep exactly
-    // this issue order: with one wavefront per SIMD nothing else fills an
-    // issue gap, and the four waves share the CU's load pipe (about 25 cycles
-    // per 1 KB load), so loads are spread evenly rather than issued in a burst.
-    auto slice = [&](const X8 (&cur)[C::TM + C::TN], X8 (&nxt)[C::TM + C::TN],
-                     auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
-                     auto l0) G18_INLINE {
-        static_for<0, NM>([&](auto qc) G18_INLINE {
-            constexpr int q = decltype(qc)::value;
-            constexpr int i = q / C::TN, j = q % C::TN;
-            if constexpr (C::MF == 32)
-                acc[i][j] = mfma32<BF>(cur[C::TM + j], cur[i], acc[i][j]);
-            else
-                acc[i][j] = mfma16<BF>(cur[C::TM + j], cur[i], acc[i][j]);
-            if constexpr (decltype(do_read)::value)
-                static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
-                    [&](auto rc) G18_INLINE { read_one(nxt, rs, rt, rc); });
-            if constexpr (decltype(do_load)::value && q % LSPACE == 0)
-                static_for<0, LPG>([&](auto gc) G18_INLINE {
-                    issue_one(lstep, ls,
-                              std::integral_constant<int, decltype(l0)::value + (q / LSPACE) * LPG +
-                                                              decltype(gc)::value>{});
-                });
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    using Z_ = std::integral_constant<int, 0>;
-    using H_ = std::integral_constant<int, LHALF>;
-
-    // Software pipeline over K-steps of BK (SLICES slices each).  Fragments
-    // are double-buffered: slice t + 1 is read while slice t is multiplied.
-    // Before the last slice of step u, the workgroup barrier makes step u + 1
-    // readable and frees step u's stage, which is refilled with step
-    // u + NSTAGE: all of its loads during the last slice of step u, or with
-    // SPLIT the first half there and the second half during the first slice
-    // of step u + 1 (each step's loads stay contiguous in issue order, so
-    // "step u + 1 has landed" is "at most (NSTAGE - 2) * LPS loads
-    // outstanding").  Step u + 1's first fragments
-    // load under the last MFMAs of step u.  Every step, the last included,
-    // runs the same code: refills of steps past the end read zeros into
-    // stages no one reads again, which keeps the vmcnt accounting the same in
-    // every iteration.  S is step u's stage, a compile-time constant: the
-    // step loop is unrolled NSTAGE times.
-    auto step_body = [&](int u, auto sc) G18_INLINE {
-        constexpr int S = decltype(sc)::value;
-        using S_ = std::integral_constant<int, S>;
-        using SP_ = std::integral_constant<int, (S + C::NSTAGE - 1) % C::NSTAGE>;   // step u-1+NSTAGE
-        using SN_ = std::integral_constant<int, (S + 1) % C::NSTAGE>;               // step u+1
-        static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
-            constexpr int t = decltype(tc)::value;
-            constexpr int c = t & 1;
-            using TN_ = std::integral_constant<int, t + 1>;
-            if constexpr (t == 0 && C::SPLIT) {
-                // second half of step u - 1 + NSTAGE
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{});
-            } else if constexpr (t + 1 < C::SLICES) {
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{});
-            } else {
-                // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
-                // be outstanding.  The fence keeps the previous slice's MFMAs
-                // ahead of the barrier, where they run while the wave waits.
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
-                lds_barrier();
-                __builtin_amdgcn_sched_barrier(0);
-                slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{});
-            }
-        });
-    };
-    // acc = the sum over the current item's K-steps (steps are counted from
-    // the item's first one).
-
-    auto store_d = [&]() G18_INLINE {
-        if constexpr (EPI) {
-            auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
-            if constexpr (C::MF == 32)
-                store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
-                                           lane, vec_store, EpiFin{epi, N, vec_store});
-            else
-                store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
-                                             lane, vec_store, EpiFin{epi, N, vec_store});
-        } else if constexpr (C::MF == 32) {
-            store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                    vec_store);
-        } else {
-            store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                      vec_store);
-        }
-    };
-
-    // ---- stream-K epilogue helpers ----
-    // Hand-off between workgroups on different XCDs, whose L2 caches are not
-    // coherent with each other: partial sums and flags move with the sc1
-    // cache policy (coherent at device scope, like device-scope atomics), and
-    // a contributor's stores are complete (vmcnt 0) before its flag is
-    // raised.  No device-scope fence is used: on this part a fence writes
-    // back or invalidates a whole L2, which would evict every other
-    // workgroup's staged A and B lines.
-    constexpr int kSc1 = 16;    // cache-policy bits of a buffer access: sc1
-    // A partial slot holds each lane's accumulators in register order, 16
-    // bytes per lane per access: piece e of block q of wave v, lane l, is at
-    // byte (((v * NM + q) * P4 + e) * 64 + l) * 16, so every access is one
-    // fully coalesced 1 KB buffer access whose per-block part is a constant
-    // scalar offset (one lane offset in a VGPR for the whole slot).
-    constexpr int P4 = (int)(sizeof(typename C::acc_t) / 16);     // 16-byte pieces per block
-    auto slot_rsrc = [&](int wslot) G18_INLINE {
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(sk.partials + (int64_t)wslot * (C::BM * C::BN)), (short)0,
-            C::BM * C::BN * 4, kRsrcFlags);
-    };
-    auto slot_store = [&](__amdgpu_buffer_rsrc_t rs, int voff) G18_INLINE {
-        static_for<0, NM>([&](auto qc) G18_INLINE {
-            constexpr int q = decltype(qc)::value;
-            const auto &a = acc[q / C::TN][q % C::TN];
-#pragma unroll
-            for (int e = 0; e < P4; ++e) {
-                const f32x4 v = {a[4 * e], a[4 * e + 1], a[4 * e + 2], a[4 * e + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff,
-                                                       (q * P4 + e) * 1024, kSc1);
-            }
-            __builtin_amdgcn_sched_barrier(0);    // one block at a time: no register peak
-        });
-    };
-    // Owner: add the partial sums of slots w_first .. w_last, in that order.
-    // Loads are issued RB blocks at a time (the fragment registers are free
-    // here), so one memory latency covers RB KB per wave instead of one.
-    constexpr int RB = NM % 16 == 0 ? 16 : NM;
-    auto add_partials = [&](int w_first, int w_last, int voff) G18_INLINE {
-        for (int w2 = w_first; w2 <= w_last; ++w2) {
-            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(w2);
-            static_for<0, NM / RB>([&](auto bc) G18_INLINE {
-                constexpr int b0 = decltype(bc)::value * RB;
-                f32x4 pf[RB][P4];
-                static_for<0, RB>([&](auto gc) G18_INLINE {
-                    constexpr int q = b0 + decltype(gc)::value;
-#pragma unroll
-                    for (int e = 0; e < P4; ++e)
-                        pf[decltype(gc)::value][e] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rs, voff, (q * P4 + e) * 1024, kSc1));
-                });
-                static_for<0, RB>([&](auto gc) G18_INLINE {
-                    constexpr int q = b0 + decltype(gc)::value;
-                    auto &a = acc[q / C::TN][q % C::TN];
-#pragma unroll
-                    for (int e = 0; e < P4; ++e)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            a[4 * e + r] += pf[decltype(gc)::value][e][r];
-                });
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
-    };
-    // D for the current tile; ok == false (a contributor never arrived)
-    // writes NaN instead.
-    auto store_ok = [&](bool ok) G18_INLINE {
-        auto get = [&](int bi, int bj) G18_INLINE {
-            return ok ? acc[bi][bj] : typename C::acc_t{} + __builtin_nanf("");
-        };
-        if constexpr (C::MF == 32)
-            store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                       vec_store);
-        else
-            store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                         vec_store);
-    };
-
-    // The work loop: one pass (this workgroup's tile) for the one-tile-per-
-    // workgroup form; the persistent form walks its items.  The pipeline is
-    // written out here once, not wrapped in a lambda: wrapped, the register
-    // allocator moves accumulators and fragments between register files
-    // inside the K-loop.
-    const int w = blockIdx.x;
-    SkCursor cur = sk_begin(sk, w);
-    for (;;) {
-        SkItem it{};
-        if constexpr (SK) {
-            if (!sk_next(sk, nk, gridDim.x, cur, it))
-                break;
-            lds_barrier();             // every wave is done with the LDS stages
-            set_item(it.tile, it.s0, it.s1);
-        } else {
-            set_item(blockIdx.x, 0, nk);
-        }
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    setup_loads(ln);
-    setup_reads(ln);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = typename C::acc_t{};
-
-    // Prologue: steps 0 .. NSTAGE-2 and, with split loads, the first half of
-    // step NSTAGE-1 (its second half is issued by step 0's first slice, like
-    // every later step); otherwise all of step NSTAGE-1 too.
-    constexpr int PRO_LAST = C::SPLIT ? LHALF : C::LPS;
-    static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
-        constexpr int st = decltype(sc)::value;
-        static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
-            [&](auto qc) G18_INLINE { issue_one(st, sc, qc); });
-    });
-    wait_vmcnt<C::LPS * (C::NSTAGE - 2) + PRO_LAST>();
-    lds_barrier();
-    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], Z_{}, Z_{}, qc); });
-
-    // With two stages the step count is rounded up to even instead of
-    // guarding each step (a guard costs registers at the loop back-edge):
-    // an extra step multiplies the all-zero stage that the zero-length
-    // resource filled, and adding +0 leaves every accumulator unchanged (an
-    // fp32 sum that starts at +0 is never -0).
-    for (int u = 0; u < n; u += C::NSTAGE)
-        static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
-            if (C::NSTAGE <= 2 || u + decltype(sc)::value < n)
-                step_body(u + decltype(sc)::value, sc);
-        });
-    wait_vmcnt<0>();      // drain the zero-filling prefetches
-
-        if constexpr (!SK) {
-            store_d();
-            break;
-        } else {
-        const int s0 = it.s0;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int slot_voff = (wave * NM * P4 * 64 + ln) * 16;
-        if (s0 > 0) {
-            // Contributor: publish the partial sums, then the flag.
-            slot_store(slot_rsrc(w), slot_voff);
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            continue;
-        }
-        // Owner of a split tile (or a whole tile: an empty range): wait for
-        // the contributors' flags, add their partials, store D.
-        const int w_first = it.w_first, w_last = it.w_last;
-        bool ok = true;
-        if (w_first <= w_last) {
-            for (int w2 = w_first; w2 <= w_last && ok; ++w2) {
-                int got = 0;
-                for (int poll = 0; poll < kSpinLimit; ++poll) {
-                    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                            sk.flags + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-                        got = 1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(8);
-                }
-                ok = got != 0;
-            }
-        }
-        if (ok)
-            add_partials(w_first, w_last, slot_voff);
-        store_ok(ok);
-        if (w_first <= w_last && tid == 0)
-            for (int w2 = w_first; w2 <= w_last; ++w2)
-                __hip_atomic_store(sk.flags + w2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-}
-
-// K == 0 with the fused epilogue: D = alpha * (+0) + beta * C + bias.
-__global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M, int64_t N)
-{
-    const int64_t count = M * N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
-        float v = e.alpha * 0.0f;
-        if (e.beta != 0.0f)
-            v = v + e.beta * (float)e.C[i];
-        if (e.bias)
-            v = v + (float)e.bias[i % N];
-        D[i] = (_Float16)v;
-    }
-}
-
-// D = +0 everywhere (K == 0).
-__global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
-        D[i] = 0;
-}
-
-// ---------------------------------------------------------------------------
-// Host side.
-using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
-using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
-using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
-// 256 x 256: 4 waves of 128 x 128 on 16x16x32 MFMAs, two 64 KB stages, each
-// step's loads issued right after the barrier.  16x16x32 keeps half as many
-// accumulator registers busy per FLOP as 32x32x16, so the part draws less
-// power and holds a higher clock under its power limit.
-using BigDma = DmaCfg<256, 256, 2, 2, 64, 2, 16, 16, false>;
-// 128 x 128: 4 waves of 64 x 64 on 16x16x32 MFMAs, four 32 KB stages.
-using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
-// 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
-// eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
-using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
-// 4-byte loads (K even, operands 4-byte aligned): four times as many load
-// instructions per step, so fewer stages keep the waits encodable.
-using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 16, 4, true>;
-using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4, false>;
-using BigDma4 = DmaCfg<256, 256, 2, 2, 64, 2, 32, 4, true>;
-
-enum class Tile { kBig, kMid, kThin };
-
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Tile choice: the one with the smaller (waves of workgroups) x (time of one
-// tile), one workgroup per CU on MI355X's 256 CUs.  Tile times relative to a
-// 128 x 128 x K tile at the big tile's rate, measured on MI355X: a 256 x 256
-// tile costs 4.0 and a 128 x 128 tile 1.4 with 16-byte loads (the big tile's
-// pipeline is ~40 % faster per FLOP); with 4-byte loads (K % 8 != 0) 6.6 and
-// 2.25.  So 3000 x 5000 runs one wave of 240 big tiles rather than four of
-// 960 mid tiles, and 2048 x 2048 runs 256 mid tiles rather than 64 big ones.
-// The choice assumes operands aligned to 16 bytes.
-constexpr int kCUs = 256;
-
-Tile choose_tile(int64_t M, int64_t N, int64_t K)
-{
-    if (M <= 64 || N <= 64)
-        return Tile::kThin;
-    const bool wide = K % 8 == 0;
-    const double big_tile = wide ? 4.0 : 6.6, mid_tile = wide ? 1.4 : 2.25;
-    const int64_t big_waves = cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs);
-    const int64_t mid_waves = cdiv(cdiv(M, 128) * cdiv(N, 128), kCUs);
-    return big_waves * big_tile <= mid_waves * mid_tile ? Tile::kBig : Tile::kMid;
-}
-
-void tile_dims(Tile t, int &bm, int &bn)
-{
-    switch (t) {
-    case Tile::kBig: bm = Big::BM; bn = Big::BN; break;
-    case Tile::kMid: bm = Mid::BM; bn = Mid::BN; break;
-    default: bm = Thin::BM; bn = Thin::BN; break;
-    }
-}
-
-int validate(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K)
-{
-    const int64_t lim = INT32_MAX;
-    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > GEMM_MAX_K)
-        return GEMM_EINVAL;
-    const uint64_t a_bytes = (uint64_t)M * (uint64_t)K * 2u;
-    const uint64_t b_bytes = (uint64_t)N * (uint64_t)K * 2u;
-    const uint64_t d_bytes = (uint64_t)M * (uint64_t)N * 2u;
-    if ((a_bytes && !A) || (b_bytes && !B) || (d_bytes && !D))
-        return GEMM_EINVAL;
-    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 1u)
-        return GEMM_EINVAL;
-    auto overlap = [](const void *p, uint64_t pn, const void *q, uint64_t qn) {
-        const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-        return pn && qn && a < b + qn && b < a + pn;
-    };
-    if (overlap(D, d_bytes, A, a_bytes) || overlap(D, d_bytes, B, b_bytes))
-        return GEMM_EINVAL;
-    return GEMM_OK;
-}
-
-template <bool EPI>
-EpiArg<EPI> epi_arg(const Epi &e)
-{
-    if constexpr (EPI)
-        return e;
-    else
-        return NoEpi{};
-}
-
-template <class C, int LOADB, bool EPI, bool BF>
-void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
-                const Epi &epi)
-{
-    using T = typename Elem<BF>::T;
-    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    hipLaunchKernelGGL((gemm_nt_reg_kernel<C, LOADB, EPI, BF>), dim3((unsigned)(tm * tn)),
-                       dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm, tn,
-                       vec, epi_arg<EPI>(epi));
-}
-
-template <class C, bool SK, bool EPI, bool BF>
-void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
-                const SkPlan &sk, int grid, const Epi &epi)
-{
-    using T = typename Elem<BF>::T;
-    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    if (!SK)
-        grid = tm * tn;
-    if (K % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, SK, EPI, BF>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
-                           tn, vec, sk, epi_arg<EPI>(epi));
-    else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, SK, EPI, BF>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
-                           tn, vec, sk, epi_arg<EPI>(epi));
-}
-
-// CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
-// 4-byte loads; C: the register-staged kernel for whatever remains (odd K or
-// 2-byte aligned operands).
-// Bytes each lane moves per direct-to-LDS load for these operands: 16, 4,
-// or 0 when only the register-staged kernel can serve them.
-int load_bytes(const void *A, const void *B, int64_t K)
-{
-    const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
-    if (K % 8 == 0 && (ab & 15u) == 0)
-        return 16;
-    if (K % 2 == 0 && (ab & 3u) == 0)
-        return 4;
-    return 0;
-}
-
-// One workgroup per tile.  EPI: with the fused epilogue `epi`, whose C and
-// bias must then also be 8-byte aligned for vector accesses.
-template <class C, class CDma, class CDma4, bool EPI = false, bool BF = false>
-void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-                 const Epi &epi = Epi{})
-{
-    const uintptr_t dcb = (uintptr_t)D | (uintptr_t)epi.C | (uintptr_t)epi.bias;
-    const int vec = ((dcb & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    const SkPlan none{};
-    switch (load_bytes(A, B, K)) {
-    case 16: launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    case 4: launch_dma<CDma4, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    default: launch_cfg<C, 2, EPI, BF>(A, B, D, M, N, K, vec, s, epi);
-    }
-}
-
-// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
-void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-               const SkPlan &sk, int grid)
-{
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-    else
-        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-}
-
-
-// ---------------------------------------------------------------------------
-// Stream-K planning.  Measured on MI355X (TFLOPS, stream-K / one workgroup
-// per tile): 512x640x16384 312/135, 1024^2x16384 858/424, 768x1024x8192
-// 509/299, 900x1000x4098 234/142, 1024^2x4096 417/362; but 1024^2x2048
-// 238/312, 1280^2x8192 444/624, 1536^2x8192 684/792.  Stream-K runs on the
-// 128 x 128 tile when its tiles fill at most a quarter of the CUs and K
-// spans at least 64 K-steps: the partial-sum hand-off (one fp32 tile per
-// contributor through memory) then costs less than the idle CUs.  The
-// 256 x 256 tile is not used for it: its hand-off moves 256 KB per
-// contributor and its pipeline leaves no registers for the persistent loop.
-struct Plan {
-    Tile tile = Tile::kThin;
-    bool sk = false;
-    int grid = 0;
-    SkPlan split{};
-};
-
-// Stream-K split of `tiles` tiles of `steps` K-steps over P workgroups: if
-// there are fewer tiles than workgroups, every tile; otherwise the last
-// partial wave plus one full wave is split by steps (each workgroup then
-// gets between one and two tiles of work) and the rest run whole.
-SkPlan sk_split(int64_t tiles, int64_t steps, int P)
-{
-    SkPlan sp{};
-    sp.sk_tiles = (int)(tiles < P ? tiles : tiles % P + P);
-    sp.dp_tiles = (int)(tiles - sp.sk_tiles);
-    const int64_t total = (int64_t)sp.sk_tiles * steps;
-    sp.base = (int)(total / P);
-    sp.extra = (int)(total % P);
-    return sp;
-}
-
-// lb: 16 or 4 (0: the register-staged path, no stream-K).
-Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
-{
-    Plan pl;
-    pl.tile = choose_tile(M, N, K);
-    if (lb == 0 || pl.tile == Tile::kThin || K == 0)
-        return pl;
-    const int64_t steps = cdiv(K, 64);
-    const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
-    if (4 * tiles <= P && steps >= 64) {
-        pl.tile = Tile::kMid;
-        pl.sk = true;
-        pl.grid = P;
-        pl.split = sk_split(tiles, steps, P);
-    }
-    return pl;
-}
-
-int64_t flag_bytes(int P) { return cdiv((int64_t)P * 4, 256) * 256; }
-
-int64_t workspace_bytes(const Plan &pl)
-{
-    return pl.sk ? flag_bytes(pl.grid) + (int64_t)pl.grid * 128 * 128 * 4 : 0;
-}
-
-// Workgroups the stream-K grid may use on the current device: one per CU,
-// at most kCUs.  The count is read once per device.
-int device_cus()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return kCUs;
-    if (dev >= 0 && dev < 64 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0)
-        return cus;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return kCUs;
-    cus = cus < kCUs ? cus : kCUs;
-    if (dev >= 0 && dev < 64)
-        cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
-} // namespace
+// gemm_nt_f16.hip -- C entry points of the fp16 GEMM: gemm_nt_f16, its
+// stream-K form and the host-only introspection.
+// Kernels, tile choice and launch helpers are in gemm_kernels.h.
+#include "gemm_kernels.h"
 
 extern "C" {
-
 int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
                 hipStream_t stream)
 {
@@ -1348,6 +25,35 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
         }
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
+}
+
+const char *gemm_nt_f16_strerror(int code)
+{
+    switch (code) {
+    case GEMM_OK: return "success";
+    case GEMM_EINVAL: return "invalid argument (size out of range, NULL, misaligned or overlapping pointer)";
+    case GEMM_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+    }
+}
+
+int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk, int64_t *workgroups)
+{
+    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !bk || !workgroups)
+        return GEMM_EINVAL;
+    tile_dims(choose_tile(M, N, K), *bm, *bn);
+    *bk = kBK;
+    *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : cdiv(M, *bm) * cdiv(N, *bn);
+    return GEMM_OK;
+}
+
+int gemm_nt_f16_tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t *tile_m,
+                           int64_t *tile_n)
+{
+    if (tiles_m <= 0 || tiles_n <= 0 || wg < 0 || wg >= tiles_m * tiles_n || !tile_m || !tile_n)
+        return GEMM_EINVAL;
+    tile_coord(wg, tiles_m, tiles_n, *tile_m, *tile_n);
+    return GEMM_OK;
 }
 
 int64_t gemm_nt_f16_ws_size(int64_t M, int64_t N, int64_t K)
@@ -1429,111 +135,6 @@ int gemm_nt_f16_ws_items(int64_t M, int64_t N, int64_t K, int64_t wg, int64_t *i
         }
         ++*count;
     }
-    return GEMM_OK;
-}
-
-int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias, void *D,
-                   int64_t M, int64_t N, int64_t K, float alpha, float beta, hipStream_t stream)
-{
-    int rc = validate(A, B, D, M, N, K);
-    if (rc != GEMM_OK)
-        return rc;
-    const uint64_t d_bytes = (uint64_t)M * (uint64_t)N * 2u;
-    auto overlaps_d = [&](const void *p, uint64_t bytes) {
-        const uintptr_t a = (uintptr_t)p, d = (uintptr_t)D;
-        return bytes && d_bytes && a < d + d_bytes && d < a + bytes;
-    };
-    if (beta != 0.0f) {
-        if ((d_bytes && !C) || ((uintptr_t)C & 1u) || (C != D && overlaps_d(C, d_bytes)))
-            return GEMM_EINVAL;
-    } else {
-        C = nullptr;                      // not read
-    }
-    if (bias && (((uintptr_t)bias & 1u) || overlaps_d(bias, (uint64_t)N * 2u)))
-        return GEMM_EINVAL;
-    if (M == 0 || N == 0)
-        return GEMM_OK;
-    if (alpha == 1.0f && !C && !bias)
-        return gemm_nt_f16(A, B, D, M, N, K, stream);
-    const Epi epi{(const _Float16 *)C, (const _Float16 *)bias, alpha, beta};
-    if (K == 0) {
-        const int64_t count = M * N;
-        const int64_t blocks = cdiv(count, 256) < 4096 ? cdiv(count, 256) : 4096;
-        hipLaunchKernelGGL(epilogue_only_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (_Float16 *)D, epi, M, N);
-    } else {
-        switch (choose_tile(M, N, K)) {
-        case Tile::kBig:
-            launch_tile<Big, BigDma, BigDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
-            break;
-        case Tile::kMid:
-            launch_tile<Mid, MidDma, MidDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
-            break;
-        default:
-            launch_tile<Thin, ThinDma, ThinDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream,
-                                                       epi);
-            break;
-        }
-    }
-    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
-}
-
-int gemm_nt_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
-                 hipStream_t stream)
-{
-    const int rc = validate(A, B, D, M, N, K);
-    if (rc != GEMM_OK)
-        return rc;
-    if (M == 0 || N == 0)
-        return GEMM_OK;
-    if (K == 0) {
-        const int64_t count = M * N;
-        const int64_t blocks = cdiv(count, 256) < 4096 ? cdiv(count, 256) : 4096;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           (uint16_t *)D, count);
-    } else {
-        switch (choose_tile(M, N, K)) {
-        case Tile::kBig:
-            launch_tile<Big, BigDma, BigDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
-            break;
-        case Tile::kMid:
-            launch_tile<Mid, MidDma, MidDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
-            break;
-        default:
-            launch_tile<Thin, ThinDma, ThinDma4, false, true>(A, B, D, (int)M, (int)N, (int)K,
-                                                              stream);
-            break;
-        }
-    }
-    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
-}
-
-const char *gemm_nt_f16_strerror(int code)
-{
-    switch (code) {
-    case GEMM_OK: return "success";
-    case GEMM_EINVAL: return "invalid argument (size out of range, NULL, misaligned or overlapping pointer)";
-    case GEMM_ELAUNCH: return "kernel launch failed";
-    default: return "unknown error code";
-    }
-}
-
-int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk, int64_t *workgroups)
-{
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !bk || !workgroups)
-        return GEMM_EINVAL;
-    tile_dims(choose_tile(M, N, K), *bm, *bn);
-    *bk = kBK;
-    *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : cdiv(M, *bm) * cdiv(N, *bn);
-    return GEMM_OK;
-}
-
-int gemm_nt_f16_tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t *tile_m,
-                           int64_t *tile_n)
-{
-    if (tiles_m <= 0 || tiles_n <= 0 || wg < 0 || wg >= tiles_m * tiles_n || !tile_m || !tile_n)
-        return GEMM_EINVAL;
-    tile_coord(wg, tiles_m, tiles_n, *tile_m, *tile_n);
     return GEMM_OK;
 }
 

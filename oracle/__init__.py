@@ -67,6 +67,11 @@ def _load():
     lib.oracle_gemm_nt_bf16.restype = ctypes.c_int
     lib.oracle_gemm_nt_bf16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
     lib.oracle_gemm_nt_bf16_entries.restype = ctypes.c_int
+    lib.oracle_fp8_decode.argtypes = [p, p, i64, ctypes.c_int]
+    lib.oracle_fp8_decode.restype = None
+    lib.oracle_gemm_nt_fp8.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int]
+    lib.oracle_gemm_nt_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -211,6 +216,29 @@ def gemm_nt_bf16_entries(A: np.ndarray, B: np.ndarray, rows, cols, threads: int 
     _load().oracle_gemm_nt_bf16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c), r.size,
                                         _ptr(out), int(threads))
     return out
+
+
+def fp8_decode(bits: np.ndarray, e5m2: bool = False) -> np.ndarray:
+    """FP8 bit patterns (uint8, OCP E4M3 or E5M2) -> exact fp64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_fp8_decode(_ptr(b), _ptr(out), b.size, int(bool(e5m2)))
+    return out
+
+
+def gemm_nt_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, a_e5m2: bool = False,
+                b_e5m2: bool = False, threads: int = 0) -> np.ndarray:
+    """D = scale * A * B^T, A and B FP8 bit patterns (uint8), D fp16 bits."""
+    a = np.ascontiguousarray(A, dtype=np.uint8)
+    b = np.ascontiguousarray(B, dtype=np.uint8)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_fp8(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(bool(a_e5m2)),
+                               int(bool(b_e5m2)), float(np.float32(scale)), int(threads))
+    return d
 
 
 def threads_available() -> int:

@@ -45,6 +45,18 @@
  * half of an IEEE binary32), decoded exactly, summed in fp64 and rounded
  * once to bfloat16 with round to nearest, ties to even.
  *
+ * FP8 (oracle_gemm_nt_fp8): the GEMM-optimisation article at www.lqnn.cn
+ * (news/123226) names the two 8-bit formats, E4M3 and E5M2 (section 2.2),
+ * quantises with a scale kept in fp32 that maps the largest magnitude to
+ * 448 (section 4.2) and undoes it in the kernel's epilogue.  Readings
+ * taken: the formats are the OCP ones, E4M3 with bias 7, no infinities,
+ * S.1111.111 the only NaN, largest finite 448 (the article's own 448; its
+ * "range about 240" in section 2.2 does not fit that format), and E5M2 with
+ * bias 15 and IEEE-style infinities and NaNs; each operand is decoded
+ * exactly, the sum is taken in fp64, multiplied by one fp32 scale (the
+ * product of A's and B's per-tensor dequantisation scales) and rounded once
+ * to fp16.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
  */
@@ -345,5 +357,58 @@ int oracle_gemm_nt_bf16_entries(const uint16_t *A, const uint16_t *B,
         else
             out[i] = entry_bf(A + m * K, B + n * K, K);
     }
+    return nt;
+}
+
+/* ---- FP8 (OCP E4M3 and E5M2) --------------------------------------------
+ * E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent 0 is
+ * subnormal (fraction * 2^-9); S.1111.111 is NaN; no infinity.
+ * E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits; exponent 0 is
+ * subnormal (fraction * 2^-16); exponent 31 is infinity or NaN.           */
+static double fp8_decode(uint8_t v, int e5m2)
+{
+    int sign = v >> 7;
+    double x;
+    if (!e5m2) {
+        int e = (v >> 3) & 15, f = v & 7;
+        if (e == 15 && f == 7)
+            return NAN;
+        x = e ? ldexp((double)(8 + f), e - 10) : ldexp((double)f, -9);
+    } else {
+        int e = (v >> 2) & 31, f = v & 3;
+        if (e == 31)
+            return f ? NAN : (sign ? -INFINITY : INFINITY);
+        x = e ? ldexp((double)(4 + f), e - 17) : ldexp((double)f, -16);
+    }
+    return sign ? -x : x;
+}
+
+void oracle_fp8_decode(const uint8_t *in, double *out, int64_t n, int e5m2)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fp8_decode(in[i], e5m2);
+}
+
+/* Full D = scale * (A * B^T) with A, B in FP8 (a_e5m2 / b_e5m2 select E5M2
+ * over E4M3) and D in fp16. */
+int oracle_gemm_nt_fp8(const uint8_t *A, const uint8_t *B, uint16_t *D, int64_t M, int64_t N,
+                       int64_t K, int a_e5m2, int b_e5m2, float scale, int nthreads)
+{
+    double la[256], lb[256];
+    for (int v = 0; v < 256; ++v) {
+        la[v] = fp8_decode((uint8_t)v, a_e5m2);
+        lb[v] = fp8_decode((uint8_t)v, b_e5m2);
+    }
+    int nt = pick_threads(nthreads);
+    const double sc = (double)scale;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *ar = A + m * K, *br = B + n * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += la[ar[k]] * lb[br[k]];
+            D[m * N + n] = f16_encode_rne(sc * acc);
+        }
     return nt;
 }

@@ -5,8 +5,10 @@ mistake by a textual edit (a dropped term, a wrong sign, a transposed index,
 a detour through fp32, flushed subnormals, ties rounded away, a wrong zero
 sign, saturation instead of infinity; in the fused epilogue a bias per row,
 beta or alpha on the wrong term, a transposed C, a rounding before the
-epilogue), compiles the copy with gcc, points the oracle wrapper at it and runs
-the pin battery.  At least one pin must fail for every planted mistake.  All
+epilogue; in FP8 a wrong exponent bias, flushed subnormals, the other NaN
+convention, saturation in place of infinity, swapped formats, a rounding
+before the scale), compiles the copy with gcc, points the oracle wrapper at it
+and runs the pin battery.  At least one pin must fail for every planted mistake.  All
 of this runs on the CPU; the real oracle is not modified.
 """
 from __future__ import annotations
@@ -21,6 +23,7 @@ import pytest
 import oracle
 from tests import test_oracle_bf16_pins as bpins
 from tests import test_oracle_epilogue_pins as epins
+from tests import test_oracle_fp8_pins as fpins
 from tests import test_oracle_pins as pins
 
 SRC = Path(oracle.__file__).resolve().parent / "gemm_oracle.c"
@@ -57,6 +60,21 @@ MUTATIONS = {
                           "for (int64_t k = 1; k < K; ++k)\n        acc += g_lut_bf[arow[k]] * g_lut_bf[brow[k]];"),
     "bf16_via_fp32_rounding": ("    return bf16_encode_rne(acc);\n}",
                                "    return bf16_encode_rne((double)(float)acc);\n}"),
+    # FP8
+    "e4m3_exponent_bias": ("x = e ? ldexp((double)(8 + f), e - 10) : ldexp((double)f, -9);",
+                           "x = e ? ldexp((double)(8 + f), e - 11) : ldexp((double)f, -9);"),
+    "e4m3_flush_subnormals": ("x = e ? ldexp((double)(8 + f), e - 10) : ldexp((double)f, -9);",
+                              "x = e ? ldexp((double)(8 + f), e - 10) : 0.0 * f;"),
+    "e4m3_fnuz_nan": ("if (e == 15 && f == 7)\n            return NAN;",
+                      "if (v == 0x80)\n            return NAN;"),
+    "e5m2_inf_as_max": ("return f ? NAN : (sign ? -INFINITY : INFINITY);",
+                        "return f ? NAN : (sign ? -57344.0 : 57344.0);"),
+    "fp8_formats_swapped": ("lb[v] = fp8_decode((uint8_t)v, b_e5m2);",
+                            "lb[v] = fp8_decode((uint8_t)v, a_e5m2);"),
+    "fp8_round_before_scale": ("D[m * N + n] = f16_encode_rne(sc * acc);",
+                               "D[m * N + n] = f16_encode_rne(sc * g_lut[f16_encode_rne(acc)]);"),
+    "fp8_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];",
+                         "for (int64_t k = 1; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];"),
 }
 
 
@@ -92,6 +110,13 @@ def _battery():
         lambda: bpins.test_b3_brute_force(17, 62),
         lambda: bpins.test_b4_integer_exact_then_rounded(33, 20, 300),
         bpins.test_b5_ties_and_double_rounding,
+        fpins.test_f1_decode_exhaustive_against_torch,
+        fpins.test_f1_decode_defining_constants,
+        lambda: fpins.test_f2_brute_force(16, 84, 2.0 ** -7, False),
+        lambda: fpins.test_f2_brute_force(33, 85, 0.1, True),
+        lambda: fpins.test_f3_integer_exact(33, 20, 256, 0.5, False),
+        fpins.test_f4_scale_applied_once_after_the_sum,
+        fpins.test_f5_mixed_formats,
     ]
 
 
@@ -124,6 +149,10 @@ def _wrap(path: Path):
     lib.oracle_gemm_nt_bf16.restype = ctypes.c_int
     lib.oracle_gemm_nt_bf16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p, ctypes.c_int]
     lib.oracle_gemm_nt_bf16_entries.restype = ctypes.c_int
+    lib.oracle_fp8_decode.argtypes = [p, p, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_fp8.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int]
+    lib.oracle_gemm_nt_fp8.restype = ctypes.c_int
     return lib
 
 

@@ -16,11 +16,13 @@ GEMM_OK = 0
 GEMM_EINVAL = 1
 GEMM_ELAUNCH = 2
 GEMM_MAX_K = 4194303
+GEMM_FP8_E4M3 = 0
+GEMM_FP8_E5M2 = 1
 
 # Every symbol the header declares.
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
            "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
-           "gemm_nt_f16_ws_items")
+           "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_tile")
 
 
 class GemmError(RuntimeError):
@@ -73,6 +75,11 @@ def lib():
     L.gemm_nt_f16_ws_tile.restype = ctypes.c_int
     L.gemm_nt_f16_ws_items.argtypes = [i64, i64, i64, i64, lp, i64, lp]
     L.gemm_nt_f16_ws_items.restype = ctypes.c_int
+    L.gemm_nt_fp8.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                              ctypes.c_int, vp]
+    L.gemm_nt_fp8.restype = ctypes.c_int
+    L.gemm_nt_fp8_tile.argtypes = [i64, i64, i64, ctypes.c_int, ip, ip]
+    L.gemm_nt_fp8_tile.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -153,6 +160,24 @@ def gemm_nt_f16_ws_items(M: int, N: int, K: int, wg: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_ws_items")
     return [tuple(buf[5 * i:5 * i + 5]) for i in range(count.value)]
+
+
+def gemm_nt_fp8(A: int, B: int, D: int, M: int, N: int, K: int, scale: float = 1.0,
+                a_format: int = GEMM_FP8_E4M3, b_format: int = GEMM_FP8_E4M3,
+                stream: int = 0) -> int:
+    """Raw call of the FP8 form (A, B: FP8 bytes, D: fp16); returns the C
+    return code."""
+    return lib().gemm_nt_fp8(A or None, B or None, D or None, M, N, K, scale, a_format,
+                             b_format, stream or None)
+
+
+def gemm_nt_fp8_tile(M: int, N: int, K: int, aligned16: bool = True):
+    """(BM, BN) of the FP8 form's tile; (0, 0) for the plain kernel."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    rc = lib().gemm_nt_fp8_tile(M, N, K, int(bool(aligned16)), ctypes.byref(bm), ctypes.byref(bn))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_fp8_tile")
+    return bm.value, bn.value
 
 
 # ---- tensor-level convenience ----------------------------------------------

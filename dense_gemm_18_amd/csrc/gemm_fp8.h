@@ -1,0 +1,140 @@
+// gemm_fp8.h -- FP8 launch helpers shared by the two translation units of
+// gemm_nt_fp8 (split by B's format so that they compile in parallel).
+//
+//   D[m,n] = scale * sum_k A[m,k] * B[n,k]     A, B: OCP E4M3 or E5M2 bytes,
+//                                               D: fp16, fp32 accumulation
+//
+// FP8 operands with a per-tensor scale kept in fp32 and applied in the
+// epilogue follow the GEMM-optimisation article at www.lqnn.cn (news/123226),
+// sections 2.2 (the E4M3 and E5M2 formats) and 4.2-4.3 (quantisation scale,
+// fp32 accumulation).  The product runs on the 16-bit direct-to-LDS pipeline
+// with FP8 operands seen as 2-byte units (gemm_kernels.h) and the gfx950
+// f8f6f4 MFMA; the scale is the fused epilogue's alpha.
+#pragma once
+
+#include "gemm_kernels.h"
+
+// Launches the product for format pair F8 = 1 + fa + 2 * fb with fb = 1 (B in
+// E5M2); defined in gemm_nt_fp8_b5.hip.  Not exported from the library.
+__attribute__((visibility("hidden"))) void gemm18_fp8_launch_b5(
+    int f8, const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, float scale,
+    hipStream_t s);
+
+namespace {
+
+
+// 128 x 128 tile for FP8: the 16-bit mid tile's pipeline with each step's
+// loads issued after the barrier (an FP8 step is a single MFMA slice).
+using Mid8 = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, false>;
+// 4-byte loads (K % 4 == 0, operands 4-byte aligned): 32 load instructions
+// per step, so two stages keep the waits encodable.
+using Mid84 = DmaCfg<128, 128, 2, 2, 64, 2, 16, 4, false>;
+
+// Exact FP8 -> fp32 decode from the format definitions (every FP8 value is
+// an fp32 value).  E4M3: bias 7, 3 fraction bits, S.1111.111 is NaN, no
+// infinities.  E5M2: bias 15, 2 fraction bits, IEEE-style specials: it is
+// the upper byte of an fp16.
+template <int FMT>
+__device__ __forceinline__ float fp8_value(uint32_t v)
+{
+    if constexpr (FMT == 1) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(v << 8));
+    } else {
+        const uint32_t e = (v >> 3) & 15u, f = v & 7u;
+        float x = e ? __builtin_ldexpf((float)(8u + f), (int)e - 10) : __builtin_ldexpf((float)f, -9);
+        if (e == 15u && f == 7u)
+            x = __builtin_nanf("");
+        return (v & 0x80u) ? -x : x;
+    }
+}
+
+// Operands the direct-to-LDS pipeline cannot take (K % 4 != 0 or operands
+// not 4-byte aligned): one output per thread, fp32 sum in ascending k.
+template <int F8>
+__global__ void __launch_bounds__(256)
+gemm_nt_fp8_plain_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                         _Float16 *__restrict__ D, int64_t M, int64_t N, int64_t K, float scale)
+{
+    constexpr int fa = (F8 - 1) & 1, fb = (F8 - 1) >> 1;
+    const int64_t count = M * N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < count; idx += stride) {
+        const int64_t m = idx / N, n = idx - m * N;
+        const uint8_t *a = A + m * K, *b = B + n * K;
+        float acc = 0.0f;
+        for (int64_t k = 0; k < K; ++k)
+            acc = __builtin_fmaf(fp8_value<fa>(a[k]), fp8_value<fb>(b[k]), acc);
+        D[idx] = (_Float16)(acc * scale);
+    }
+}
+
+template <class C, int F8>
+void launch_fp8_dma(const void *A, const void *B, void *D, int M, int N, int Kp, int vec,
+                    hipStream_t s, const Epi &epi)
+{
+    using T = _Float16;
+    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
+    const SkPlan none{};
+    if (Kp % C::BK == 0)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, false, true, false, F8>),
+                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
+    else
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, false, true, false, F8>),
+                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
+}
+
+// Bytes each lane moves per direct-to-LDS load for FP8 operands with K
+// bytes per row: 16, 4, or 0 (the plain kernel).
+int fp8_load_bytes(const void *A, const void *B, int64_t K)
+{
+    const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
+    if (K % 16 == 0 && (ab & 15u) == 0)
+        return 16;
+    if (K % 4 == 0 && (ab & 3u) == 0)
+        return 4;
+    return 0;
+}
+
+// Tile of the FP8 product: the 16-bit choice on K / 2 byte pairs for 16-byte
+// loads (an FP8 step moves the same bytes and does twice the MFMA work);
+// with 4-byte loads the 128 x 128 tile (the 256 x 256 one would need more
+// loads in flight than the wait counter encodes) or the thin one.
+Tile fp8_tile(int64_t M, int64_t N, int64_t K, int lb)
+{
+    if (lb == 16)
+        return choose_tile(M, N, K / 2);
+    return (M <= 64 || N <= 64) ? Tile::kThin : Tile::kMid;
+}
+
+template <int F8>
+void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                float scale, hipStream_t s)
+{
+    const Epi epi{nullptr, nullptr, scale, 0.0f};
+    const int lb = fp8_load_bytes(A, B, K);
+    if (lb == 0) {
+        const int64_t blocks = cdiv(M * N, 256) < 8192 ? cdiv(M * N, 256) : 8192;
+        hipLaunchKernelGGL((gemm_nt_fp8_plain_kernel<F8>), dim3((unsigned)blocks), dim3(256), 0,
+                           s, (const uint8_t *)A, (const uint8_t *)B, (_Float16 *)D, M, N, K,
+                           scale);
+        return;
+    }
+    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    const int m = (int)M, n = (int)N, kp = (int)(K / 2);
+    const Tile t = fp8_tile(M, N, K, lb);
+    if (lb == 16) {
+        switch (t) {
+        case Tile::kBig: launch_fp8_dma<BigDma, F8>(A, B, D, m, n, kp, vec, s, epi); break;
+        case Tile::kMid: launch_fp8_dma<Mid8, F8>(A, B, D, m, n, kp, vec, s, epi); break;
+        default: launch_fp8_dma<ThinDma, F8>(A, B, D, m, n, kp, vec, s, epi); break;
+        }
+    } else if (t == Tile::kMid) {
+        launch_fp8_dma<Mid84, F8>(A, B, D, m, n, kp, vec, s, epi);
+    } else {
+        launch_fp8_dma<ThinDma4, F8>(A, B, D, m, n, kp, vec, s, epi);
+    }
+}
+
+} // namespace

@@ -60,6 +60,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Element type of A, B and D: fp16, or bfloat16 (BF).  Both are 2 bytes,
 // so loads, LDS layout and swizzle are shared; the MFMA, the fragment vector
@@ -102,6 +103,20 @@ __device__ __forceinline__ f32x16 mfma32(typename Elem<BF>::x8 b, typename Elem<
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+}
+
+// FP8 operands (OCP E4M3 or E5M2, one format per operand): F8 = 1 + fa +
+// 2 * fb with fa, fb the formats of A and B (0: E4M3, 1: E5M2, the codes of
+// the f8f6f4 MFMA's format fields); F8 = 0 for 16-bit operands.  The MFMA is
+// v_mfma_f32_16x16x128_f8f6f4 (32 bytes of K per lane and operand, no
+// block scales: the per-tensor scale is applied in the epilogue).  B is the
+// first operand as in mfma16; any assignment of K bytes to lanes gives the
+// same sum as long as A and B use the same one, which they do.
+template <int F8>
+__device__ __forceinline__ f32x4 mfma_f8(i32x8 b, i32x8 a, f32x4 c)
+{
+    constexpr int fa = (F8 - 1) & 1, fb = (F8 - 1) >> 1;
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, fb, fa, 0, 0, 0, 0);
 }
 
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
@@ -658,15 +673,23 @@ constexpr int kSpinLimit = 1 << 24;
 
 // KTAIL: K % BK != 0, so the last step is partial and every load carries a
 // per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
-// stream-K form; otherwise one workgroup per tile.
-template <class C, bool KTAIL, bool SK, bool EPI, bool BF>
+// stream-K form; otherwise one workgroup per tile.  F8 != 0: FP8 operands
+// (see mfma_f8), passed as 2-byte units: K counts byte pairs, so loads, LDS
+// layout, swizzle and K masks are those of the 16-bit path.  A K-step (a
+// 128-byte row) is one f8f6f4 MFMA per block; its two slices split the
+// blocks by rows instead of the K-step by halves, so the barrier, the loads
+// and the next step's fragment reads keep the 16-bit path's timing.
+template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                    const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
                    int M, int N, int K, int tiles_m, int tiles_n, int vec_store, SkPlan sk,
                    EpiArg<EPI> epi)
 {
-    using X8 = typename Elem<BF>::x8;
+    using X8 = typename std::conditional<F8 != 0, i32x8, typename Elem<BF>::x8>::type;
+    static_assert(F8 == 0 || (!BF && !SK && !C::SPLIT && C::MF == 16 && C::BK == 64 &&
+                              C::SLICES == 2 && C::NSTAGE % 2 == 0 && C::TM % 2 == 0),
+                  "FP8: 16x16 blocks, 128-byte rows, an even stage ring, loads after the barrier");
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -783,24 +806,40 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     X8 fr[2][C::TM + C::TN];
     auto read_one = [&](X8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
         constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
-        if constexpr (q < C::TM)
-            f[q] = *(const X8 *)(smem + a_addr[S][t] + C::MF * q * C::ROW_BYTES);
-        else
-            f[q] = *(const X8 *)(smem + b_addr[S][t] + C::MF * (q - C::TM) * C::ROW_BYTES);
+        constexpr int off = C::MF * (q < C::TM ? q : q - C::TM) * C::ROW_BYTES;
+        if constexpr (F8) {
+            // 32 bytes: the chunks of both 16-bit slices (t is always 0)
+            static_assert(t == 0, "an FP8 fragment spans the whole K-step");
+            const uint32_t p0 = q < C::TM ? a_addr[S][0] : b_addr[S][0];
+            const uint32_t p1 = q < C::TM ? a_addr[S][1] : b_addr[S][1];
+            const u32x4 lo = *(const u32x4 *)(smem + p0 + off);
+            const u32x4 hi = *(const u32x4 *)(smem + p1 + off);
+            f[q] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            f[q] = *(const X8 *)(smem + (q < C::TM ? a_addr[S][t] : b_addr[S][t]) + off);
+        }
     };
 
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
+    // MFMAs per slice: all blocks, or (FP8) half of the block rows.
+    constexpr int NMS = F8 ? NM / 2 : NM;
     constexpr int LHALF = C::LPS / 2;
     // Loads issued in one slice: half a step's or a whole step's.
     constexpr int LSL = C::SPLIT ? LHALF : C::LPS;
-    // Spacing of the loads over the NM MFMAs of a slice: one load every
+    // Spacing of the loads over the NMS MFMAs of a slice: one load every
     // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
     // than MFMAs (small tiles); the same for fragment reads (RPG).
-    constexpr int LSPACE = NM >= LSL ? NM / LSL : 1;
-    constexpr int LPG = NM >= LSL ? 1 : LSL / NM;
+    constexpr int LSPACE = NMS >= LSL ? NMS / LSL : 1;
+    constexpr int LPG = NMS >= LSL ? 1 : LSL / NMS;
     constexpr int RPG = (NR + NM - 1) / NM;
-    static_assert(C::LPS % 2 == 0 && (NM % LSL == 0 || LSL % NM == 0),
+    static_assert(C::LPS % 2 == 0 && (NMS % LSL == 0 || LSL % NMS == 0),
                   "loads split evenly over the slices that issue them");
+    // FP8 read schedule (second slice only), by the slice's MFMA index p:
+    // next-step A blocks of the first half-rows (dead since the first slice)
+    // after p = 0, 1, ...; A block i of the second half once row i is done;
+    // B block j (live to the end) spread from p = TM / 2 on.
+    constexpr int HR = C::TM / 2;
+    constexpr int BSTEP = (NMS - HR) / C::TN > 1 ? (NMS - HR) / C::TN : 1;
 
     // One slice: MFMA q of TM x TN, each followed by its share of fragment
     // reads for the next slice (stage RS, slice RT) and of the loads l0, l0+1,
@@ -808,23 +847,42 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // this issue order: with one wavefront per SIMD nothing else fills an
     // issue gap, and the four waves share the CU's load pipe (about 25 cycles
     // per 1 KB load), so loads are spread evenly rather than issued in a burst.
+    // FP8 fragments are twice as large and a K-step's are read in its second
+    // slice only; the A fragments are not double buffered (see the FP8 read
+    // schedule above), which keeps the 256 x 256 tile within the registers.
+    // h: (FP8) which half of the block rows this slice multiplies.
     auto slice = [&](const X8 (&cur)[C::TM + C::TN], X8 (&nxt)[C::TM + C::TN],
                      auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
-                     auto l0) G18_INLINE {
-        static_for<0, NM>([&](auto qc) G18_INLINE {
-            constexpr int q = decltype(qc)::value;
+                     auto l0, auto hc) G18_INLINE {
+        static_for<0, NMS>([&](auto pc) G18_INLINE {
+            constexpr int p = decltype(pc)::value;
+            constexpr int q = p + (F8 ? decltype(hc)::value * NMS : 0);
             constexpr int i = q / C::TN, j = q % C::TN;
-            if constexpr (C::MF == 32)
+            if constexpr (F8 != 0)
+                acc[i][j] = mfma_f8<F8>(cur[C::TM + j], cur[i], acc[i][j]);
+            else if constexpr (C::MF == 32)
                 acc[i][j] = mfma32<BF>(cur[C::TM + j], cur[i], acc[i][j]);
             else
                 acc[i][j] = mfma16<BF>(cur[C::TM + j], cur[i], acc[i][j]);
-            if constexpr (decltype(do_read)::value)
+            if constexpr (decltype(do_read)::value && F8 != 0) {
+                if constexpr (p < HR)
+                    read_one(nxt, rs, rt, std::integral_constant<int, p>{});
+                static_for<0, C::TN>([&](auto jc) G18_INLINE {
+                    constexpr int jb = decltype(jc)::value;
+                    constexpr int pb = HR + jb * BSTEP < NMS ? HR + jb * BSTEP : NMS - 1;
+                    if constexpr (p == pb)
+                        read_one(nxt, rs, rt, std::integral_constant<int, C::TM + jb>{});
+                });
+                if constexpr (j == C::TN - 1)
+                    read_one(nxt, rs, rt, std::integral_constant<int, i>{});
+            } else if constexpr (decltype(do_read)::value) {
                 static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
                     [&](auto rc) G18_INLINE { read_one(nxt, rs, rt, rc); });
-            if constexpr (decltype(do_load)::value && q % LSPACE == 0)
+            }
+            if constexpr (decltype(do_load)::value && p % LSPACE == 0)
                 static_for<0, LPG>([&](auto gc) G18_INLINE {
                     issue_one(lstep, ls,
-                              std::integral_constant<int, decltype(l0)::value + (q / LSPACE) * LPG +
+                              std::integral_constant<int, decltype(l0)::value + (p / LSPACE) * LPG +
                                                               decltype(gc)::value>{});
                 });
             __builtin_amdgcn_sched_barrier(0);
@@ -857,13 +915,18 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         using SN_ = std::integral_constant<int, (S + 1) % C::NSTAGE>;               // step u+1
         static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
             constexpr int t = decltype(tc)::value;
-            constexpr int c = t & 1;
+            // Fragment set of this slice: 16-bit slices alternate sets; FP8
+            // steps do (the ring has an even number of stages), and both
+            // slices of an FP8 step multiply the same set.
+            constexpr int c = F8 ? S & 1 : t & 1;
             using TN_ = std::integral_constant<int, t + 1>;
             if constexpr (t == 0 && C::SPLIT) {
                 // second half of step u - 1 + NSTAGE
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{});
+                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{}, tc);
             } else if constexpr (t + 1 < C::SLICES) {
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{});
+                // (FP8: nothing to read until the next step's stage is ready)
+                slice(fr[c], fr[c ^ 1], std::integral_constant<bool, F8 == 0>{}, S_{}, TN_{}, F_{},
+                      0, S_{}, Z_{}, tc);
             } else {
                 // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
                 // be outstanding.  The fence keeps the previous slice's MFMAs
@@ -872,7 +935,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
                 lds_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{});
+                slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, tc);
             }
         });
     };
@@ -1073,7 +1136,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 }
 
 // K == 0 with the fused epilogue: D = alpha * (+0) + beta * C + bias.
-__global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M, int64_t N)
+[[maybe_unused]] __global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M, int64_t N)
 {
     const int64_t count = M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1088,7 +1151,7 @@ __global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M,
 }
 
 // D = +0 everywhere (K == 0).
-__global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
+[[maybe_unused]] __global__ void fill_zero_kernel(uint16_t *__restrict__ D, int64_t count)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
@@ -1239,18 +1302,6 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
     default: launch_cfg<C, 2, EPI, BF>(A, B, D, M, N, K, vec, s, epi);
     }
 }
-
-// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
-void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-               const SkPlan &sk, int grid)
-{
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-    else
-        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-}
-
 
 // ---------------------------------------------------------------------------
 // Stream-K planning.  Measured on MI355X (TFLOPS, stream-K / one workgroup

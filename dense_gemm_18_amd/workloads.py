@@ -165,3 +165,45 @@ def bf16_integers(seed: int, M: int, N: int, K: int, lo: int = -2, hi: int = 2):
     rng = np.random.default_rng(seed)
     return (to_bf16_bits(rng.integers(lo, hi + 1, size=(M, K))),
             to_bf16_bits(rng.integers(lo, hi + 1, size=(N, K))))
+
+
+# FP8 inputs.  Format codes as in the C ABI: 0 = E4M3, 1 = E5M2.
+FP8_MAX = {0: 448.0, 1: 57344.0}
+
+
+def fp8_quantize(x: np.ndarray, fmt: int):
+    """Per-tensor FP8 quantisation (input preparation only): the scale maps
+    the largest magnitude to the format's largest finite value, and x / scale
+    is rounded to the nearest FP8 value by torch's float8 cast.  Returns the
+    FP8 bytes (uint8) and the fp32 dequantisation scale."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = np.float32(amax / FP8_MAX[fmt]) if amax > 0 else np.float32(1.0)
+    dt = torch.float8_e5m2 if fmt else torch.float8_e4m3fn
+    q = torch.from_numpy(x / scale).to(dt).view(torch.uint8).numpy().copy()
+    return q, scale
+
+
+def fp8_normal(seed: int, M: int, N: int, K: int, fa: int = 0, fb: int = 0):
+    """FP8 A [M, K] and B [N, K] quantised from standard normal values, each
+    with its own per-tensor scale; returns (A, B, scale) with scale the fp32
+    product of the two dequantisation scales."""
+    rng = np.random.default_rng(seed)
+    A, sa = fp8_quantize(rng.standard_normal((M, K), dtype=np.float32), fa)
+    B, sb = fp8_quantize(rng.standard_normal((N, K), dtype=np.float32), fb)
+    return A, B, float(np.float32(sa * sb))
+
+
+def fp8_integers(seed: int, M: int, N: int, K: int, fa: int = 0, fb: int = 0, lo: int = -4,
+                 hi: int = 4):
+    """FP8 A, B with integer entries in {lo..hi} (exact in both formats for
+    |v| <= 4)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    out = []
+    for rows, fmt in ((M, fa), (N, fb)):
+        v = rng.integers(lo, hi + 1, size=(rows, K)).astype(np.float32)
+        dt = torch.float8_e5m2 if fmt else torch.float8_e4m3fn
+        out.append(torch.from_numpy(v).to(dt).view(torch.uint8).numpy().copy())
+    return out[0], out[1]

@@ -78,6 +78,44 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
 int gemm_nt_bf16(const void *A, const void *B, void *D,
                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* FP8 operand formats (OCP 8-bit floating point). */
+#define GEMM_FP8_E4M3 0  /* 1 sign, 4 exponent (bias 7), 3 fraction bits; S.1111.111
+                            is NaN; no infinities; largest finite 448            */
+#define GEMM_FP8_E5M2 1  /* 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style
+                            infinities and NaNs; largest finite 57344             */
+
+/*
+ * FP8 product with a per-tensor scale (the GEMM-optimisation article at
+ * www.lqnn.cn, news/123226: section 2.2 names the E4M3 and E5M2 formats,
+ * sections 4.2-4.3 quantise each operand with a scale kept in fp32 and undo
+ * it after an fp32-accumulated product):
+ *
+ *     D[m,n] = scale * sum_{k<K} A[m,k] * B[n,k]
+ *
+ * A: M x K bytes in a_format, B: N x K bytes in b_format (GEMM_FP8_E4M3 or
+ *   GEMM_FP8_E5M2, chosen per operand), both row-major with no padding,
+ *   any alignment.  D: M x N fp16, 2-byte aligned.
+ * scale: fp32, normally the product of A's and B's dequantisation scales.
+ *   Products are exact and summed in fp32; the sum is multiplied by scale in
+ *   fp32 and rounded once to fp16 (round to nearest even).  K == 0 gives
+ *   scale * (+0).
+ * Fast path: K % 16 == 0 with A and B 16-byte aligned (then K % 4 == 0
+ *   with 4-byte alignment); anything else runs a plain per-output kernel.
+ *
+ * Returns as gemm_nt_f16 (sizes M, N, K in [0, 2^31 - 1], K <= GEMM_MAX_K),
+ * and GEMM_EINVAL also for an unknown format or D overlapping A or B.
+ */
+int gemm_nt_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                float scale, int a_format, int b_format, hipStream_t stream);
+
+/*
+ * Host-only: the output tile gemm_nt_fp8 uses for these sizes (aligned16:
+ * whether A and B are 16-byte aligned; 4-byte alignment is assumed
+ * otherwise).  *bm = *bn = 0 when the plain per-output kernel runs.
+ * GEMM_EINVAL for negative sizes or NULL outputs.
+ */
+int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn);
+
 /*
  * Fused epilogue, the standard GEMM form:
  *

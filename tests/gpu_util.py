@@ -218,3 +218,36 @@ def assert_bitexact(d_gpu, d_ref, what=""):
         i = diff[0]
         raise AssertionError(f"{what}: {diff.size} entries differ; first flat index {i}: "
                              f"gpu 0x{int(d_gpu.ravel()[i]):04x} ref 0x{int(d_ref.ravel()[i]):04x}")
+
+
+def run_gemm_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, fa: int = 0, fb: int = 0,
+                 a_off: int = 0, b_off: int = 0) -> np.ndarray:
+    """D = scale * A B^T through gemm_nt_fp8 (A, B: FP8 bytes, D: fp16 bit
+    patterns), canaries around D.  `*_off` start an operand that many bytes
+    past a 256-byte boundary."""
+    import torch
+    from dense_gemm_18_amd import binding
+
+    M, K = A.shape
+    N = B.shape[0]
+    dev = device()
+
+    def put(x, off):
+        flat = np.ascontiguousarray(x, dtype=np.uint8).ravel()
+        buf = torch.zeros(flat.size + off + 16, dtype=torch.uint8, device=dev)
+        if flat.size:
+            buf[off:off + flat.size].copy_(torch.from_numpy(flat.copy()).to(dev))
+        return buf, buf.data_ptr() + off
+
+    _ka, pa = put(A, a_off)
+    _kb, pb = put(B, b_off)
+    dbuf = torch.full((M * N + 2 * GUARD,), int(np.uint16(CANARY).view(np.int16)),
+                      dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = binding.gemm_nt_fp8(pa, pb, dbuf.data_ptr() + 2 * GUARD, M, N, K, scale, fa, fb, stream)
+    assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
+    torch.cuda.synchronize(dev)
+    host = dbuf.cpu().numpy().view(np.uint16)
+    assert np.all(host[:GUARD] == CANARY), "write before D"
+    assert np.all(host[GUARD + M * N:] == CANARY), "write after D"
+    return host[GUARD: GUARD + M * N].reshape(M, N).copy()

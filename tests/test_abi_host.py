@@ -166,3 +166,43 @@ def test_ex_validation_rejects_before_any_hip_call(C, bias, beta):
 
 def test_ex_empty_output_is_a_no_op():
     assert binding.gemm_nt_f16_ex(0, FAKE, 0, 0, 0, 0, 5, 5, 2.0, 1.0, 0) == binding.GEMM_OK
+
+
+E4, E5 = binding.GEMM_FP8_E4M3, binding.GEMM_FP8_E5M2
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, -1, 4, 4, 1.0, E4, E4),        # negative M
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, binding.GEMM_MAX_K + 1, 1.0, E4, E4),
+    (0, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, E4, E4),             # NULL A
+    (FAKE, 0, FAKE + 0x2000000, 4, 4, 4, 1.0, E4, E4),                         # NULL B
+    (FAKE, FAKE + 0x1000000, 0, 4, 4, 4, 1.0, E4, E4),                         # NULL D
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000001, 4, 4, 4, 1.0, E4, E4),          # odd D
+    (FAKE, FAKE + 0x1000000, FAKE + 8, 4, 4, 4, 1.0, E4, E4),                  # D overlaps A
+    (FAKE, FAKE + 0x1000000, FAKE + 0x1000000 - 8, 4, 4, 4, 1.0, E4, E4),      # D overlaps B
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, 2, E4),           # unknown format
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, E4, -1),
+])
+def test_fp8_validation_rejects_before_any_hip_call(args):
+    assert binding.gemm_nt_fp8(*args, 0) == binding.GEMM_EINVAL
+
+
+def test_fp8_accepts_odd_operand_addresses_and_empty_outputs():
+    # FP8 operands are bytes: odd A and B are valid (only M == 0 is called
+    # here, so nothing launches).
+    assert binding.gemm_nt_fp8(FAKE + 1, FAKE + 0x1000003, FAKE + 0x2000000, 0, 4, 4, 1.0,
+                               E4, E5, 0) == binding.GEMM_OK
+    assert binding.gemm_nt_fp8(0, 0, 0, 0, 0, 9, 2.0, E5, E5, 0) == binding.GEMM_OK
+
+
+@pytest.mark.parametrize("M,N,K,aligned,tile", [
+    (8192, 8192, 8192, True, (256, 256)),
+    (2048, 2048, 4096, True, (128, 128)),
+    (64, 4096, 4096, True, (64, 64)),
+    (8192, 8192, 8196, True, (128, 128)),    # K % 16 != 0: 4-byte loads, no 256 x 256 tile
+    (8192, 8192, 8192, False, (128, 128)),   # operands only 4-byte aligned
+    (40, 8192, 8196, True, (64, 64)),
+    (300, 200, 130, True, (0, 0)),           # K % 4 != 0: the plain kernel
+])
+def test_fp8_tile_choice(M, N, K, aligned, tile):
+    assert binding.gemm_nt_fp8_tile(M, N, K, aligned) == tile

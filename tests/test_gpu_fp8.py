@@ -1,0 +1,129 @@
+"""GPU parity of the FP8 product gemm_nt_fp8 against the oracle.
+
+Integer inputs (|v| <= 4, exact in both formats) with a power-of-two scale
+are bit-exact at any K: the products and their fp32 sum are exact on the GPU,
+the scale multiplies exactly, and both sides round the same exact value once
+to fp16.  Inputs quantised from normal values (per-tensor scales, the product
+scale applied in the epilogue) must satisfy the fp16 tolerance
+|D - D_ref| <= 2^-10 |D_ref| + 1e-3 sqrt(K): their dequantised values have
+unit spread, as the fp16 tests' inputs do, and the products are exact, so
+only the fp32 accumulation and the one rounding differ.
+
+Shapes cover the 256 x 256, 128 x 128 and 64 x 64 tiles, ragged M and N
+edges, K tails inside a step (16-byte loads), 4-byte loads (K % 16 != 0 or
+4-byte-aligned operands), the plain kernel (K % 4 != 0, odd addresses),
+every format pair, K = 0, special values and the full 8192^3 size on sampled
+rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_18_amd import binding
+from dense_gemm_18_amd import workloads as wl
+from tests.gpu_util import assert_bitexact, assert_tolerance, note, run_gemm_fp8
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = binding.GEMM_FP8_E4M3, binding.GEMM_FP8_E5M2
+
+# 256x256 (K tail inside a step), 128x128, 64x64, 128x128 with 4-byte loads,
+# 64x64 with 4-byte loads, the plain kernel (K % 4 == 2, K odd), one step
+SHAPES = [(2900, 4100, 400), (1100, 1100, 1024), (64, 300, 512), (700, 900, 4100),
+          (50, 300, 260), (300, 200, 130), (150, 97, 37), (256, 256, 128)]
+
+
+def _ref(A, B, scale, fa, fb):
+    return oracle.gemm_nt_fp8(A, B, scale, bool(fa), bool(fb))
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_integer_bitexact(M, N, K):
+    A, B = wl.fp8_integers(12000 + K, M, N, K)
+    bm = binding.gemm_nt_fp8_tile(M, N, K, True)
+    note(f"fp8 integer {M}x{N}x{K} tile {bm}")
+    for scale in (1.0, 0.25):
+        assert_bitexact(run_gemm_fp8(A, B, scale), _ref(A, B, scale, E4, E4),
+                        f"fp8 integer {M}x{N}x{K} scale {scale}")
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_random_tolerance(M, N, K):
+    A, B, s = wl.fp8_normal(12100 + K, M, N, K)
+    note(f"fp8 normal {M}x{N}x{K} scale {s}")
+    assert_tolerance(run_gemm_fp8(A, B, s), _ref(A, B, s, E4, E4), K, f"fp8 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E4, E5), (E5, E4), (E5, E5)])
+@pytest.mark.parametrize("M,N,K", [(1100, 1100, 1024), (300, 200, 130), (700, 900, 4100)])
+def test_fp8_format_pairs(fa, fb, M, N, K):
+    A, B, s = wl.fp8_normal(12200 + 7 * fa + 3 * fb, M, N, K, fa, fb)
+    note(f"fp8 formats {fa},{fb} {M}x{N}x{K}")
+    assert_tolerance(run_gemm_fp8(A, B, s, fa, fb), _ref(A, B, s, fa, fb), K,
+                     f"fp8 {fa},{fb} {M}x{N}x{K}")
+    Ai, Bi = wl.fp8_integers(12300 + fa + 2 * fb, M, N, K, fa, fb)
+    assert_bitexact(run_gemm_fp8(Ai, Bi, 0.5, fa, fb), _ref(Ai, Bi, 0.5, fa, fb),
+                    f"fp8 integer {fa},{fb} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("a_off,b_off", [(4, 0), (0, 12), (1, 0), (0, 3)])
+def test_fp8_misaligned_operands(a_off, b_off):
+    M, N, K = 500, 600, 1024
+    A, B = wl.fp8_integers(12400 + a_off, M, N, K)
+    note(f"fp8 offsets {a_off},{b_off}")
+    assert_bitexact(run_gemm_fp8(A, B, 1.0, a_off=a_off, b_off=b_off), _ref(A, B, 1.0, E4, E4),
+                    f"fp8 offsets {a_off},{b_off}")
+
+
+@pytest.mark.parametrize("scale", [1.0 / 3.0, -2.5, 1e-3])
+def test_fp8_scales(scale):
+    M, N, K = 1100, 1100, 1024
+    A, B = wl.fp8_integers(12500, M, N, K)
+    note(f"fp8 scale {scale}")
+    # exact sums; the fp32 product sum * scale is then the exact value
+    # rounded once to fp32 before the fp16 rounding: at most one fp16 step
+    assert_tolerance(run_gemm_fp8(A, B, scale), _ref(A, B, scale, E4, E4), 0,
+                     f"fp8 scale {scale}")
+
+
+def test_fp8_k_zero_and_empty():
+    note("fp8 K=0")
+    z = np.zeros((70, 0), np.uint8), np.zeros((90, 0), np.uint8)
+    assert np.all(run_gemm_fp8(*z, 2.0) == 0x0000)
+    assert np.all(run_gemm_fp8(*z, -2.0) == 0x8000)          # -2 * (+0) = -0
+    assert run_gemm_fp8(np.zeros((0, 16), np.uint8), np.zeros((5, 16), np.uint8)).size == 0
+
+
+def test_fp8_special_values():
+    M, N, K = 300, 260, 512
+    A, B = wl.fp8_integers(12600, M, N, K)
+    A[3, 100] = 0x7F                 # E4M3 NaN: row 3 of D is NaN
+    B[7, 9] = 0xFF                   # NaN: column 7 of D is NaN
+    A[10, :] = 0x7E                  # 448: row 10 overflows fp16 where it does not cancel
+    note("fp8 NaN and overflow")
+    d = run_gemm_fp8(A, B)
+    ref = _ref(A, B, 1.0, E4, E4)
+    g, r = d.view(np.float16), ref.view(np.float16)
+    assert np.array_equal(np.isnan(g), np.isnan(r))
+    assert np.isnan(g[3]).all() and np.isnan(g[:, 7]).all()
+    fin = ~np.isnan(r)
+    assert np.array_equal(d[fin], ref[fin])                 # infinities included
+    # E5M2 infinity times a positive value gives an infinity of that sign
+    A5, B5 = wl.fp8_integers(12601, 64, 64, 256, E5, E5, lo=1, hi=2)
+    A5[5, 17] = 0x7C                 # +inf
+    d5 = run_gemm_fp8(A5, B5, 1.0, E5, E5).view(np.float16)
+    assert np.all(d5[5] == np.inf)
+    assert np.isfinite(np.delete(d5, 5, axis=0)).all()
+
+
+def test_fp8_headline_size_sampled_rows():
+    M = N = K = 8192
+    A, B, s = wl.fp8_normal(12700, M, N, K)
+    note("fp8 8192^3 sampled rows")
+    d = run_gemm_fp8(A, B, s)
+    rows = np.unique(np.concatenate([wl.edge_lines(M, 256),
+                                     np.random.default_rng(12701).choice(M, 8, replace=False)]))
+    ref = _ref(A[rows], B, s, E4, E4)
+    assert_tolerance(d[rows], ref, K, "fp8 8192^3 rows")

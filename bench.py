@@ -1,16 +1,24 @@
-"""Throughput of the fp16 NT GEMM on one MI355X.
+"""Throughput of the NT GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--path f16|f16_ex|f16_ws|bf16|fp8]
 
-A step is one call of gemm_nt_f16 (the whole hot path) on the 8192 x 8192 x
-8192 workload: A [M,K] and B [N,K] fp16 drawn uniform[-1,1] from fixed seeds,
-fp32 accumulation, D [M,N] fp16, all resident in HBM before timing starts.
-Throughput is TFLOPS = 2*M*N*K / t (page "构建 Tiled GEMM", section "GEMM").
+A step is one call of the chosen entry point (the whole hot path): by
+default gemm_nt_f16 on the 8192 x 8192 x 8192 workload, A [M,K] and B [N,K]
+fp16 drawn uniform[-1,1] from fixed seeds, fp32 accumulation, D [M,N] fp16,
+all resident in HBM before timing starts.  Throughput is
+TFLOPS = 2*M*N*K / t (page "构建 Tiled GEMM", section "GEMM").
+
+The other paths time the library's other entry points on the same workload
+(or the one named): the fused epilogue (alpha 0.5, beta 1, with C and a
+bias), the stream-K form (default workload 1024 x 1024 x 16384), bfloat16
+storage, and FP8 E4M3 operands quantised from normal values with a
+per-tensor scale.
 
 Prints one JSON line with the metric, a roofline object for the GEMM kernel
 (achieved TFLOP/s from HIP events on the launch stream, against the MI355X
-dense fp16 MFMA peak) and a CPU baseline (the oracle, on a bounded sample of
-the same workload, on this host's cores).
+dense MFMA peak of the path's operand type) and a CPU baseline (the oracle,
+on a bounded sample of the same workload, on this host's cores).
 """
 from __future__ import annotations
 
@@ -26,13 +34,23 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-# MI355X dense fp16 MFMA peak: 256 CUs x 4096 FLOP/clock/CU x 2.4 GHz
-# (AMD's published 2.5 PFLOP/s dense fp16 figure).
+# MI355X dense MFMA peaks: 256 CUs x FLOP/clock/CU x 2.4 GHz; fp16 and
+# bf16 4096 FLOP/clock/CU (AMD's published 2.5 PFLOP/s dense figure), FP8
+# twice that (5.0 PFLOP/s).
 PEAK_FP16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_FP8_TFLOPS = 2 * PEAK_FP16_TFLOPS
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = [ROOT / "dense_gemm_18_amd" / "csrc" / "gemm_kernels.h",
-                  ROOT / "dense_gemm_18_amd" / "csrc" / "gemm_nt_f16.hip"]
-TRAFFIC_SUMMARY = ROOT / "profiles" / "gemm_nt_f16_square_8192_traffic.md"
+CSRC = ROOT / "dense_gemm_18_amd" / "csrc"
+# Sources of each path's kernels (their hash tells whether recorded counters
+# still describe the kernel).
+PATH_SOURCES = {
+    "f16": ["gemm_kernels.h", "gemm_nt_f16.hip"],
+    "f16_ws": ["gemm_kernels.h", "gemm_nt_f16.hip"],
+    "f16_ex": ["gemm_kernels.h", "gemm_nt_f16_ex.hip"],
+    "bf16": ["gemm_kernels.h", "gemm_nt_bf16.hip"],
+    "fp8": ["gemm_kernels.h", "gemm_fp8.h", "gemm_nt_fp8.hip"],
+}
+KERNEL_SOURCES = [CSRC / f for f in PATH_SOURCES["f16"]]
 
 
 def tflops(M: int, N: int, K: int, seconds: float) -> float:
@@ -40,36 +58,44 @@ def tflops(M: int, N: int, K: int, seconds: float) -> float:
     return 2.0 * M * N * K / (seconds * 1e12)
 
 
-def algorithmic_bytes(M: int, N: int, K: int) -> float:
-    """A and B read once, D written once, fp16."""
-    return 2.0 * (M * K + N * K + M * N)
+def algorithmic_bytes(M: int, N: int, K: int, elem: int = 2, extra: float = 0.0) -> float:
+    """A and B read once (elem bytes per element), D written once (2-byte),
+    plus `extra` bytes (the fused epilogue's C and bias)."""
+    return elem * (M * K + N * K) + 2.0 * M * N + extra
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel source's code: comments and whitespace are dropped,
-    so only a change to the code itself invalidates recorded counters."""
-    text = "\n".join(p.read_text() for p in KERNEL_SOURCES)
+def kernel_source_hash(path: str = "f16") -> str:
+    """Hash of a path's kernel sources' code: comments and whitespace are
+    dropped, so only a change to the code itself invalidates recorded
+    counters."""
+    text = "\n".join((CSRC / f).read_text() for f in PATH_SOURCES[path])
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     code = " ".join(text.split())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def recorded_traffic():
+def traffic_summary(path: str, workload: str) -> Path:
+    return ROOT / "profiles" / f"gemm_nt_{path}_{workload}_traffic.md"
+
+
+def recorded_traffic(path: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    if not TRAFFIC_SUMMARY.exists():
+    f = traffic_summary(path, workload)
+    if not f.exists():
         return None
-    text = TRAFFIC_SUMMARY.read_text()
+    text = f.read_text()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not b or h.group(1) != kernel_source_hash():
+    if not h or not b or h.group(1) != kernel_source_hash(path):
         return None
     return float(b.group(1))
 
 
-def cpu_baseline(A, B, M, N, K, budget_s: float = 12.0) -> dict:
-    """The oracle (untuned) on whole rows of D until ~budget_s of CPU work."""
+def cpu_baseline(rows_fn, M, N, K, budget_s: float = 12.0) -> dict:
+    """The oracle (untuned) on whole rows of D until ~budget_s of CPU work;
+    rows_fn(r0, r1, threads) computes rows r0 .. r1-1."""
     import oracle
     threads = oracle.threads_available()
     chunk = 64
@@ -77,7 +103,7 @@ def cpu_baseline(A, B, M, N, K, budget_s: float = 12.0) -> dict:
     t0 = time.perf_counter()
     while rows < M and time.perf_counter() - t0 < budget_s:
         r1 = min(M, rows + chunk)
-        oracle.gemm_nt_f16(A[rows:r1], B, threads=threads)
+        rows_fn(rows, r1, threads)
         rows = r1
     dt = time.perf_counter() - t0
     return {
@@ -101,6 +127,106 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> int:
     return 0
 
 
+def setup_path(path, w, torch, dev, binding, wl) -> dict:
+    """Inputs resident on the GPU and one step of the chosen entry point,
+    with what the report needs about it."""
+    import numpy as np
+
+    M, N, K = w.M, w.N, w.K
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    dD = torch.empty((M, N), dtype=torch.float16, device=dev)
+    pd = dD.data_ptr()
+    fp16_inputs = {"A": f"{w.a_dist} fp16, seed {w.seeds[0]}",
+                   "B": f"{w.b_dist} fp16, seed {w.seeds[1]}"}
+
+    def check(rc, what):
+        if rc != binding.GEMM_OK:
+            raise RuntimeError(f"{what}: {binding.gemm_nt_f16_strerror(rc)}")
+
+    keep = [dD]              # device buffers the steps use stay alive with P
+    P = {"keep": keep, "peak": PEAK_FP16_TFLOPS, "bytes": algorithmic_bytes(M, N, K),
+         "dtype": "fp16", "inputs": fp16_inputs, "tile": list(binding.gemm_nt_f16_tile(M, N, K)[:3])}
+    if path in ("f16", "f16_ws", "f16_ex"):
+        A, B = wl.random_inputs(w)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        pa, pb = dA.data_ptr(), dB.data_ptr()
+        P["tensors"] = (dA, dB)
+        keep += [dA, dB]
+    if path == "f16":
+        import oracle
+        P.update(entry="gemm_nt_f16",
+                 metric="fp16 GEMM TFLOPS (2MNK/t) at 8192^3; % of MI355X dense fp16 MFMA peak",
+                 step=lambda: check(binding.gemm_nt_f16(pa, pb, pd, M, N, K, sptr), "gemm_nt_f16"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_f16(A[r0:r1], B, threads=t))
+    elif path == "f16_ws":
+        import oracle
+        need = max(binding.gemm_nt_f16_ws_size(M, N, K), 256)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        keep.append(ws)
+        bm, bn, wg, skt = binding.gemm_nt_f16_ws_tile(M, N, K)
+        P.update(entry="gemm_nt_f16_ws", tile=[bm, bn, 64], stream_k_tiles=skt,
+                 metric=f"fp16 GEMM TFLOPS (2MNK/t), stream-K form, {M}x{N}x{K}",
+                 step=lambda: check(binding.gemm_nt_f16_ws(pa, pb, pd, M, N, K, ws.data_ptr(),
+                                                           need, sptr), "gemm_nt_f16_ws"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_f16(A[r0:r1], B, threads=t))
+        P["inputs"] = dict(fp16_inputs, workspace_bytes=need, stream_k_tiles=skt,
+                           workgroups=wg)
+    elif path == "f16_ex":
+        import oracle
+        rng = np.random.default_rng(w.seeds[0] + 77)
+        C = rng.uniform(-1.0, 1.0, size=(M, N)).astype(np.float16)
+        bias = rng.uniform(-1.0, 1.0, size=N).astype(np.float16)
+        dC, dbias = torch.from_numpy(C).to(dev), torch.from_numpy(bias).to(dev)
+        keep += [dC, dbias]
+        alpha, beta = 0.5, 1.0
+        P.update(entry="gemm_nt_f16_ex", bytes=algorithmic_bytes(M, N, K, extra=2.0 * (M * N + N)),
+                 metric=f"fp16 GEMM TFLOPS (2MNK/t) with fused alpha/beta/bias epilogue, "
+                        f"{M}x{N}x{K}",
+                 step=lambda: check(binding.gemm_nt_f16_ex(pa, pb, dC.data_ptr(), dbias.data_ptr(),
+                                                           pd, M, N, K, alpha, beta, sptr),
+                                    "gemm_nt_f16_ex"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_f16_ex(A[r0:r1], B, C[r0:r1], bias,
+                                                                  alpha, beta))
+        P["inputs"] = dict(fp16_inputs, C="uniform[-1,1] fp16", bias="uniform[-1,1] fp16",
+                           alpha=alpha, beta=beta)
+    elif path == "bf16":
+        import oracle
+        A, B = wl.bf16_uniform(w.seeds[0], M, N, K)
+        dA = torch.from_numpy(A.view(np.int16)).to(dev)
+        dB = torch.from_numpy(B.view(np.int16)).to(dev)
+        pa, pb = dA.data_ptr(), dB.data_ptr()
+        keep += [dA, dB]
+        P.update(entry="gemm_nt_bf16", dtype="bf16",
+                 metric=f"bf16 GEMM TFLOPS (2MNK/t), {M}x{N}x{K}; % of MI355X dense bf16 MFMA peak",
+                 step=lambda: check(binding.gemm_nt_bf16(pa, pb, pd, M, N, K, sptr), "gemm_nt_bf16"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_bf16(A[r0:r1], B, threads=t))
+        P["inputs"] = {"A": f"uniform[-1,1] bf16, seed {w.seeds[0]}",
+                       "B": f"uniform[-1,1] bf16, seed {w.seeds[0]} (second draw)"}
+    elif path == "fp8":
+        import oracle
+        A, B, scale = wl.fp8_normal(w.seeds[0], M, N, K)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        pa, pb = dA.data_ptr(), dB.data_ptr()
+        keep += [dA, dB]
+        e4 = binding.GEMM_FP8_E4M3
+        P.update(entry="gemm_nt_fp8", dtype="fp8_e4m3", peak=PEAK_FP8_TFLOPS,
+                 bytes=algorithmic_bytes(M, N, K, elem=1),
+                 tile=list(binding.gemm_nt_fp8_tile(M, N, K, True)) + [128],
+                 metric=f"FP8 E4M3 GEMM TFLOPS (2MNK/t), {M}x{N}x{K}, fp16 out; % of MI355X "
+                        "dense FP8 MFMA peak",
+                 step=lambda: check(binding.gemm_nt_fp8(pa, pb, pd, M, N, K, scale, e4, e4, sptr),
+                                    "gemm_nt_fp8"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_fp8(A[r0:r1], B, scale, threads=t))
+        P["inputs"] = {"A": f"standard normal quantised to E4M3 (per-tensor scale), seed "
+                            f"{w.seeds[0]}",
+                       "B": "standard normal quantised to E4M3 (per-tensor scale), same stream",
+                       "scale": scale}
+    else:
+        raise ValueError(path)
+    return P
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +236,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8192^3 GEMM)")
+    ap.add_argument("--path", default="f16", choices=sorted(PATH_SOURCES),
+                    help="entry point to time (default: gemm_nt_f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the "
@@ -137,23 +265,14 @@ def main() -> int:
 
     if not binding.library_path().exists():
         hip_build.build()
-    name = args.workload or wl.HEADLINE
+    path = args.path
+    name = args.workload or ("deep_1024x1024x16384" if path == "f16_ws" else wl.HEADLINE)
     w = wl.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
     dev = torch.device("cuda:0")
-
-    A, B = wl.random_inputs(w)
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
-    dD = torch.empty((M, N), dtype=torch.float16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream
-    pa, pb, pd = dA.data_ptr(), dB.data_ptr(), dD.data_ptr()
-
-    def step():
-        rc = binding.gemm_nt_f16(pa, pb, pd, M, N, K, sptr)
-        if rc != binding.GEMM_OK:
-            raise RuntimeError(binding.gemm_nt_f16_strerror(rc))
+    P = setup_path(path, w, torch, dev, binding, wl)
+    step = P["step"]
+    stream = torch.cuda.current_stream(dev)        # the stream every launch goes to
 
     for _ in range(args.warmup):
         step()
@@ -190,10 +309,11 @@ def main() -> int:
 
     value = tflops(M, N, K, wall / args.steps)
     achieved = tflops(M, N, K, avg_kernel_s)
-    traffic = recorded_traffic() if name == wl.HEADLINE else None
+    peak = P["peak"]
+    traffic = recorded_traffic(path, name)
     props = torch.cuda.get_device_properties(dev)
     out = {
-        "metric": "fp16 GEMM TFLOPS (2MNK/t) at 8192^3; % of MI355X dense fp16 MFMA peak",
+        "metric": P["metric"],
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -203,35 +323,36 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": P["dtype"],
         "data": "synthetic",
         "config": {
-            "workload": name, "M": M, "N": N, "K": K,
-            "A": f"{w.a_dist} fp16, seed {w.seeds[0]}", "B": f"{w.b_dist} fp16, seed {w.seeds[1]}",
+            "workload": name, "M": M, "N": N, "K": K, "entry_point": P["entry"],
+            **P["inputs"],
             "accumulate": "fp32", "layout": "A MxK, B NxK (D = A B^T), row-major",
-            "tile": list(binding.gemm_nt_f16_tile(M, N, K)[:3]),
+            "tile": P["tile"],
         },
-        "pct_of_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": round(PEAK_FP16_TFLOPS, 1),
+            "peak": round(peak, 1),
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_ms_avg": round(avg_kernel_s * 1e3, 5),
             "kernel_ms_median": round(median_ms, 5),
             "kernel_ms_min": round(min(kernel_ms), 5),
             "kernel_ms_max": round(max(kernel_ms), 5),
             "algorithmic_flops_per_launch": 2.0 * M * N * K,
-            "algorithmic_bytes_per_launch": algorithmic_bytes(M, N, K),
-            "hbm_gbs_at_algorithmic_bytes": round(algorithmic_bytes(M, N, K) / avg_kernel_s / 1e9, 1),
+            "algorithmic_bytes_per_launch": P["bytes"],
+            "hbm_gbs_at_algorithmic_bytes": round(P["bytes"] / avg_kernel_s / 1e9, 1),
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(path),
     }
-    if args.torch_context:
+    if args.torch_context and path == "f16":
+        dA, dB = P["tensors"]
         ts = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         lin = torch.nn.functional.linear          # A @ B^T with B stored [N, K]
         for _ in range(args.warmup):
@@ -244,7 +365,7 @@ def main() -> int:
         out["context_torch_linear_tflops"] = round(
             tflops(M, N, K, ts[0].elapsed_time(ts[1]) / args.steps / 1e3), 2)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K)
+        out["cpu_baseline"] = cpu_baseline(P["cpu_rows"], M, N, K)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -51,6 +51,9 @@ WORKLOADS = {
                  (4001, 4002), (4011, 4012)),
         Workload("square_8192", 8192, 8192, 8192, "uniform", "uniform",
                  (5001, 5002), (5011, 5012), sample_seed=5003),
+        # few output tiles, long K: the stream-K form's case
+        Workload("deep_1024x1024x16384", 1024, 1024, 16384, "uniform", "uniform",
+                 (6001, 6002), (6011, 6012)),
     )
 }
 

@@ -677,8 +677,7 @@ constexpr int kSpinLimit = 1 << 24;
 // (see mfma_f8), passed as 2-byte units: K counts byte pairs, so loads, LDS
 // layout, swizzle and K masks are those of the 16-bit path.  A K-step (a
 // 128-byte row) is one f8f6f4 MFMA per block; its two slices split the
-// blocks by rows instead of the K-step by halves, so the barrier, the loads
-// and the next step's fragment reads keep the 16-bit path's timing.
+// blocks by rows instead of the K-step by halves.
 template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
@@ -834,12 +833,13 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     constexpr int RPG = (NR + NM - 1) / NM;
     static_assert(C::LPS % 2 == 0 && (NMS % LSL == 0 || LSL % NMS == 0),
                   "loads split evenly over the slices that issue them");
-    // FP8 read schedule (second slice only), by the slice's MFMA index p:
-    // next-step A blocks of the first half-rows (dead since the first slice)
-    // after p = 0, 1, ...; A block i of the second half once row i is done;
-    // B block j (live to the end) spread from p = TM / 2 on.
+    // FP8 read schedule, by the slice's MFMA index p: the next step's B
+    // blocks (double-buffered) during the first slice, B block j after
+    // p = j * BSTEP; its A blocks (single-buffered) during the second: those
+    // of the first half-rows (dead since the first slice) after p = 0, 1, ...,
+    // A block i of the second half once row i is done with the current one.
     constexpr int HR = C::TM / 2;
-    constexpr int BSTEP = (NMS - HR) / C::TN > 1 ? (NMS - HR) / C::TN : 1;
+    constexpr int BSTEP = NMS / C::TN > 1 ? NMS / C::TN : 1;
 
     // One slice: MFMA q of TM x TN, each followed by its share of fragment
     // reads for the next slice (stage RS, slice RT) and of the loads l0, l0+1,
@@ -864,15 +864,16 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 acc[i][j] = mfma32<BF>(cur[C::TM + j], cur[i], acc[i][j]);
             else
                 acc[i][j] = mfma16<BF>(cur[C::TM + j], cur[i], acc[i][j]);
-            if constexpr (decltype(do_read)::value && F8 != 0) {
-                if constexpr (p < HR)
-                    read_one(nxt, rs, rt, std::integral_constant<int, p>{});
+            if constexpr (decltype(do_read)::value && F8 != 0 && decltype(hc)::value == 0) {
                 static_for<0, C::TN>([&](auto jc) G18_INLINE {
                     constexpr int jb = decltype(jc)::value;
-                    constexpr int pb = HR + jb * BSTEP < NMS ? HR + jb * BSTEP : NMS - 1;
+                    constexpr int pb = jb * BSTEP < NMS ? jb * BSTEP : NMS - 1;
                     if constexpr (p == pb)
                         read_one(nxt, rs, rt, std::integral_constant<int, C::TM + jb>{});
                 });
+            } else if constexpr (decltype(do_read)::value && F8 != 0) {
+                if constexpr (p < HR)
+                    read_one(nxt, rs, rt, std::integral_constant<int, p>{});
                 if constexpr (j == C::TN - 1)
                     read_one(nxt, rs, rt, std::integral_constant<int, i>{});
             } else if constexpr (decltype(do_read)::value) {
@@ -913,20 +914,31 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         using S_ = std::integral_constant<int, S>;
         using SP_ = std::integral_constant<int, (S + C::NSTAGE - 1) % C::NSTAGE>;   // step u-1+NSTAGE
         using SN_ = std::integral_constant<int, (S + 1) % C::NSTAGE>;               // step u+1
+        if constexpr (F8 != 0) {
+            // FP8: the barrier comes first (step u + 1 landed, step u's stage
+            // free); the first slice refills the stage with step u + NSTAGE
+            // and reads step u + 1's B blocks, the second reads its A blocks.
+            // LDS reads and DMA writes are then spread over the whole step,
+            // and each refill still has the step's second slice to land.
+            // Both slices multiply fragment set S & 1 (an even ring).
+            constexpr int c = S & 1;
+            using H1_ = std::integral_constant<int, 1>;
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, Z_{});
+            slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, F_{}, 0, S_{}, Z_{}, H1_{});
+        } else {
         static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
             constexpr int t = decltype(tc)::value;
-            // Fragment set of this slice: 16-bit slices alternate sets; FP8
-            // steps do (the ring has an even number of stages), and both
-            // slices of an FP8 step multiply the same set.
-            constexpr int c = F8 ? S & 1 : t & 1;
+            constexpr int c = t & 1;    // 16-bit slices alternate fragment sets
             using TN_ = std::integral_constant<int, t + 1>;
             if constexpr (t == 0 && C::SPLIT) {
                 // second half of step u - 1 + NSTAGE
                 slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{}, tc);
             } else if constexpr (t + 1 < C::SLICES) {
-                // (FP8: nothing to read until the next step's stage is ready)
-                slice(fr[c], fr[c ^ 1], std::integral_constant<bool, F8 == 0>{}, S_{}, TN_{}, F_{},
-                      0, S_{}, Z_{}, tc);
+                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{}, tc);
             } else {
                 // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
                 // be outstanding.  The fence keeps the previous slice's MFMAs
@@ -938,6 +950,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, tc);
             }
         });
+        }
     };
     // acc = the sum over the current item's K-steps (steps are counted from
     // the item's first one).

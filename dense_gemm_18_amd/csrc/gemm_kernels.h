@@ -341,6 +341,85 @@ __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M
     }
 }
 
+// Four fp16 values of row p at columns n .. n+3 (columns >= N read as 0),
+// raw: one 8-byte load when vec, else element loads.
+__device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec)
+{
+    if (vec)
+        return *(const f16x4 *)(p + n);
+    f16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        h[r] = n + r < N ? p[n + r] : (_Float16)0.0f;
+    return h;
+}
+
+// The fused epilogue on 16x16 blocks (same element map as store_blocks16)
+// in two phases: every C and bias value this lane needs is loaded first (in
+// registers as fp16, 2 VGPRs per group of four), then each group becomes
+// alpha * v + beta * C + bias in fp32 in that order and is stored.  All the
+// loads are in flight together instead of one load latency per group.
+template <int TM, int TN, class Get>
+__device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict__ D, int M,
+                                                   int N, int mbase, int nbase, int lane,
+                                                   int vec, const Epi &e)
+{
+    const int frow = lane & 15, fq = lane >> 4;
+    const bool has_c = e.beta != 0.0f, has_bias = e.bias != nullptr;
+    f16x4 cv[TM][TN], bv[TN];
+    if (has_bias) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bv[j] = load4h(e.bias, nbase + 16 * j + 4 * fq, N, vec);
+    }
+    if (has_c) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = mbase + 16 * i + frow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                cv[i][j] = m < M ? load4h(e.C + (int64_t)m * N, nbase + 16 * j + 4 * fq, N, vec)
+                                 : f16x4{};
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = mbase + 16 * i + frow;
+        _Float16 *drow = D + (int64_t)m * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const f32x4 v = get(i, j);
+            if (m >= M)
+                continue;
+            const int n = nbase + 16 * j + 4 * fq;
+            f32x4 u = v * e.alpha;
+            if (has_c) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    u[r] = u[r] + e.beta * (float)cv[i][j][r];
+            }
+            if (has_bias) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    u[r] = u[r] + (float)bv[j][r];
+            }
+            f16x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                h[r] = (_Float16)u[r];
+            if (vec) {
+                if (n < N)
+                    *(f16x4 *)(drow + n) = h;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        drow[n + r] = h[r];
+            }
+        }
+    }
+}
+
 template <int TM, int TN, class T>
 __device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], T *__restrict__ D,
                                             int M, int N, int mbase, int nbase, int lane,
@@ -715,7 +794,10 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                                                rows_a * K * 2, kRsrcFlags);
         rb = __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0,
                                                rows_b * K * 2, kRsrcFlags);
-        kb = s0 * C::BK;
+        // With a K tail the steps are aligned to K's end instead of its
+        // start: step 0 covers k in [-shift, BK - shift) and every later
+        // step is full, so only the first step's loads need a K mask.
+        kb = s0 * C::BK - (KTAIL ? nk * C::BK - K : 0);
         n = s1 - s0;
     };
 
@@ -758,26 +840,29 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // A rows, the rest B rows; each instruction fills 1024 contiguous LDS
     // bytes.  Rows past the tile's valid rows lie past the buffer range and
     // read as zero; steps past the end load through the zero-length
-    // resource; with KTAIL, chunks with k >= K get an out-of-range offset.
-    auto issue_one = [&](int step, auto sc, auto qc) G18_INLINE {
+    // resource.  FIRST (the prologue's first step only): with a K tail the
+    // item's first step may start before k = 0 (k0 < 0, uniform); chunks
+    // with k < 0 then get an out-of-range offset and the others carry k0 in
+    // their vector offset.  Loads inside the K-loop carry no mask, which
+    // keeps the loop's registers those of the untailed kernel.
+    auto issue_one = [&](int step, auto sc, auto qc, auto firstc) G18_INLINE {
         constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
         const int k0 = kb + step * C::BK;
         const bool live = step < n;
         char *stage = smem + S * C::STAGE_BYTES;
-        if constexpr (q < C::A_LOADS) {
-            uint32_t off = a_off[q];
-            if constexpr (KTAIL)
-                off = (k0 + a_k[q] < K) ? off : kOob;
-            char *dst = stage + (wave + C::NWAVES * q) * C::INST_BYTES;
-            load_lds<C::LB>(live ? ra : rz, dst, off, k0 * 2);
-        } else {
-            constexpr int i = q - C::A_LOADS;
-            uint32_t off = b_off[i];
-            if constexpr (KTAIL)
-                off = (k0 + b_k[i] < K) ? off : kOob;
-            char *dst = stage + C::BM * C::ROW_BYTES + (wave + C::NWAVES * i) * C::INST_BYTES;
-            load_lds<C::LB>(live ? rb : rz, dst, off, k0 * 2);
+        constexpr bool isa = q < C::A_LOADS;
+        constexpr int i = isa ? q : q - C::A_LOADS;
+        uint32_t off = isa ? a_off[i] : b_off[i];
+        uint32_t soff = (uint32_t)k0 * 2u;
+        if constexpr (KTAIL && decltype(firstc)::value) {
+            if (k0 < 0) {
+                const int kk = isa ? a_k[i] : b_k[i];
+                off = k0 + kk >= 0 ? off + soff : kOob;
+                soff = 0;
+            }
         }
+        char *dst = stage + (isa ? 0 : C::BM * C::ROW_BYTES) + (wave + C::NWAVES * i) * C::INST_BYTES;
+        load_lds<C::LB>(live ? (isa ? ra : rb) : rz, dst, off, soff);
     };
 
     typename C::acc_t acc[C::TM][C::TN];
@@ -884,7 +969,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 static_for<0, LPG>([&](auto gc) G18_INLINE {
                     issue_one(lstep, ls,
                               std::integral_constant<int, decltype(l0)::value + (p / LSPACE) * LPG +
-                                                              decltype(gc)::value>{});
+                                                              decltype(gc)::value>{},
+                              std::false_type{});
                 });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -962,8 +1048,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
                                            lane, vec_store, EpiFin{epi, N, vec_store});
             else
-                store_blocks16<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
-                                             lane, vec_store, EpiFin{epi, N, vec_store});
+                store_blocks16_epi<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
+                                                 lane, vec_store, epi);
         } else if constexpr (C::MF == 32) {
             store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
                                     vec_store);
@@ -1085,7 +1171,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
         constexpr int st = decltype(sc)::value;
         static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
-            [&](auto qc) G18_INLINE { issue_one(st, sc, qc); });
+            [&](auto qc) G18_INLINE {
+                issue_one(st, sc, qc, std::integral_constant<bool, st == 0>{});
+            });
     });
     wait_vmcnt<C::LPS * (C::NSTAGE - 2) + PRO_LAST>();
     lds_barrier();

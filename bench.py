@@ -323,6 +323,21 @@ def main() -> int:
     achieved = tflops(M, N, K, avg_kernel_s)
     peak = P["peak"]
     traffic = recorded_traffic(path, name)
+    # The kernel's bound: MFMA when its arithmetic intensity (algorithmic
+    # FLOP per algorithmic byte) is above the ridge point peak / HBM
+    # bandwidth, else HBM (the skinny linear-layer shapes).
+    intensity = 2.0 * M * N * K / P["bytes"]
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    else:
+        gbs = P["bytes"] / avg_kernel_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(achieved, 2),
+                "pct_of_mfma_peak": round(100.0 * achieved / peak, 2)}
+    roof["arithmetic_intensity_flop_per_byte"] = round(intensity, 1)
+    roof["ridge_flop_per_byte"] = round(ridge, 1)
     props = torch.cuda.get_device_properties(dev)
     out = {
         "metric": P["metric"],
@@ -345,11 +360,7 @@ def main() -> int:
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": round(peak, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            **roof,
             "traffic": traffic,
             "kernel_ms_avg": round(avg_kernel_s * 1e3, 5),
             "single_launch_ms_median": round(median_ms, 5),

@@ -8,8 +8,9 @@
 // Operation, storage types (fp16 in and out, fp32 accumulator) and the
 // NT layout follow page "构建 Tiled GEMM" ("Building a Tiled GEMM", mlc.ai
 // modern-gpu-programming-for-mlsys, chapter gemm_basics), section "GEMM".
-// The kernel design is gfx950's own; what it keeps from the pages is listed
-// next to each part.
+// The same kernels also serve bfloat16 storage, FP8 operands (2-byte units,
+// see mfma_f8) and the fused alpha/beta/bias epilogue.  The kernel design is
+// gfx950's own; what it keeps from the pages is listed next to each part.
 //
 // One workgroup computes one BM x BN output tile:
 //   * Tile -> workgroup map: an XCD-aware remap (consecutive workgroup ids
@@ -26,7 +27,8 @@
 //     the accesses are fully coalesced (page 1, "内核 1：共享内存分块", shows
 //     the cooperative coalesced tile copy).  The buffer resource of each
 //     workgroup spans only its valid rows, so rows past M or N read as zero
-//     in hardware; K tails are masked per load.
+//     in hardware; with a K tail the K-steps are aligned to K's end, so only
+//     the first step's loads carry a K mask.
 //   * LDS layout: rows of 64 fp16 (128 B = eight 16-byte chunks), chunk index
 //     XOR-swizzled by the row so that the MFMA fragment reader is free of
 //     bank conflicts (page 1, "为什么 swizzle 重要", explains the conflict
@@ -39,7 +41,8 @@
 //     accumulators hold 4 consecutive columns n of D for one row m and the
 //     epilogue writes 8-byte vectors.
 //   * Epilogue: fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even),
-//     masked at the M and N edges.
+//     masked at the M and N edges; the fused form loads C and bias first and
+//     forms alpha * acc + beta * C + bias in fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -550,17 +553,18 @@ gemm_nt_reg_kernel(const typename Elem<BF>::T *__restrict__ A,
 // gfx950's buffer_load_dwordx4 ... lds writes each lane's 16 bytes straight
 // into LDS, at M0 + 16 * lane: one instruction fills 1024 contiguous bytes
 // and needs no staging registers and no ds_write.  That leaves room for a
-// ring of NSTAGE LDS stages of BK = 32, so the loads for K-step u + NSTAGE - 1
-// are in flight while step u is multiplied (page 1, "内核 3：Warp 特化" and
+// ring of NSTAGE LDS stages of BK = 64, so the loads for later K-steps are
+// in flight while step u is multiplied (page 1, "内核 3：Warp 特化" and
 // "内核 4", overlaps loads with MMAs through a STAGES-deep ring; here one
 // wavefront both loads and multiplies, and the ring is tracked with vmcnt
 // and one workgroup barrier per K-step instead of full/empty events).
 //
-// LDS rows are BK fp16 (64 or 128 bytes, four or eight 16-byte chunks).  The
+// LDS rows are BK 2-byte elements (BK = 64 in every configuration: 128
+// bytes, eight 16-byte chunks; the template also takes BK = 32).  The
 // swizzle is applied on the global side: LDS slot (row, chunk) receives
-// global chunk chunk ^ swz_row(row) of that row.  Both swizzles were chosen
-// by measuring SQ_LDS_BANK_CONFLICT for the MFMA fragment read pattern
-// (32 rows x 16 bytes per half wave) on gfx950: zero conflicts.
+// global chunk chunk ^ swz_row(row) of that row.  The swizzles were chosen
+// by measuring SQ_LDS_BANK_CONFLICT for the MFMA fragment read patterns
+// (16 or 32 rows x 16 bytes per group of lanes) on gfx950: zero conflicts.
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -750,8 +754,9 @@ __host__ __device__ inline bool sk_next(const SkPlan &sk, int nk, int P, SkCurso
 // them before every read).
 constexpr int kSpinLimit = 1 << 24;
 
-// KTAIL: K % BK != 0, so the last step is partial and every load carries a
-// per-lane K mask; otherwise loads carry no mask at all.  SK: the persistent
+// KTAIL: K % BK != 0; the K-steps are then aligned to K's end, so the
+// first step starts before k = 0 and only its loads (in the prologue of the
+// tile's first work item) carry a per-lane K mask.  SK: the persistent
 // stream-K form; otherwise one workgroup per tile.  F8 != 0: FP8 operands
 // (see mfma_f8), passed as 2-byte units: K counts byte pairs, so loads, LDS
 // layout, swizzle and K masks are those of the 16-bit path.  A K-step (a

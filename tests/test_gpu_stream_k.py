@@ -25,6 +25,7 @@ SHAPES = [
     (768, 768, 8192),        # 36 tiles, pieces cross tile boundaries
     (512, 640, 16384),       # 20 tiles, up to 12 contributors each
     (900, 1000, 4098),       # ragged M, N; 4-byte loads and a K tail
+    (768, 1024, 8200),       # 16-byte loads and a K tail (only step 0 masked)
     (100, 8192, 32768),      # one tile row, K = 32768
 ]
 

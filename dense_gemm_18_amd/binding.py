@@ -182,16 +182,25 @@ def gemm_nt_fp8_tile(M: int, N: int, K: int, aligned16: bool = True):
 
 # ---- tensor-level convenience ----------------------------------------------
 
-def gemm_nt(A, B, out=None, stream=None):
-    """D = A @ B.T for fp16 CUDA (HIP) tensors A [M, K] and B [N, K].
+def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0):
+    """D = A @ B.T for CUDA (HIP) tensors A [M, K] and B [N, K].
 
-    ``out`` (optional) is a contiguous fp16 [M, N] tensor on the same device.
-    The call is enqueued on ``stream`` (default: the current stream).
+    float16 A and B call gemm_nt_f16 (D float16), bfloat16 call gemm_nt_bf16
+    (D bfloat16); float8_e4m3fn / float8_e5m2 operands (the two may differ)
+    call gemm_nt_fp8 with ``scale`` (D float16).  ``out`` (optional) is a
+    contiguous [M, N] tensor of D's dtype on the same device.  The call is
+    enqueued on ``stream`` (default: the current stream).
     """
     import torch
 
-    if A.dtype != torch.float16 or B.dtype != torch.float16:
-        raise TypeError("A and B must be float16")
+    fp8 = {torch.float8_e4m3fn: GEMM_FP8_E4M3, torch.float8_e5m2: GEMM_FP8_E5M2}
+    if A.dtype in fp8 and B.dtype in fp8:
+        out_dtype = torch.float16
+    elif A.dtype == B.dtype and A.dtype in (torch.float16, torch.bfloat16):
+        out_dtype = A.dtype
+    else:
+        raise TypeError(f"unsupported operand dtypes {A.dtype} and {B.dtype}: both float16, "
+                        "both bfloat16, or float8_e4m3fn / float8_e5m2")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError(f"shapes {tuple(A.shape)} and {tuple(B.shape)} are not [M,K] and [N,K]")
     if not (A.is_cuda and B.is_cuda) or A.device != B.device:
@@ -201,12 +210,21 @@ def gemm_nt(A, B, out=None, stream=None):
     M, K = A.shape
     N = B.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
-    elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif (out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous()
           or out.device != A.device):
-        raise ValueError("out must be a contiguous float16 [M, N] tensor on A's device")
+        raise ValueError(f"out must be a contiguous {out_dtype} [M, N] tensor on A's device")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    rc = gemm_nt_f16(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, s.cuda_stream)
+    pa, pb, pd = A.data_ptr(), B.data_ptr(), out.data_ptr()
+    if A.dtype in fp8:
+        name = "gemm_nt_fp8"
+        rc = gemm_nt_fp8(pa, pb, pd, M, N, K, scale, fp8[A.dtype], fp8[B.dtype], s.cuda_stream)
+    elif A.dtype == torch.bfloat16:
+        name = "gemm_nt_bf16"
+        rc = gemm_nt_bf16(pa, pb, pd, M, N, K, s.cuda_stream)
+    else:
+        name = "gemm_nt_f16"
+        rc = gemm_nt_f16(pa, pb, pd, M, N, K, s.cuda_stream)
     if rc != GEMM_OK:
-        raise GemmError(rc, "gemm_nt_f16")
+        raise GemmError(rc, name)
     return out

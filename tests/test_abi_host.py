@@ -206,3 +206,21 @@ def test_fp8_accepts_odd_operand_addresses_and_empty_outputs():
 ])
 def test_fp8_tile_choice(M, N, K, aligned, tile):
     assert binding.gemm_nt_fp8_tile(M, N, K, aligned) == tile
+
+
+def test_tensor_convenience_rejects_before_any_gpu_use():
+    import torch
+    h = torch.zeros((4, 8), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        binding.gemm_nt(h, h.to(torch.bfloat16))              # mixed 16-bit types
+    with pytest.raises(TypeError):
+        binding.gemm_nt(h.float(), h.float())                 # fp32 is not a storage type here
+    with pytest.raises(TypeError):
+        binding.gemm_nt(h, h.to(torch.float8_e4m3fn))         # 16-bit with FP8
+    with pytest.raises(ValueError):
+        binding.gemm_nt(h, torch.zeros((4, 9), dtype=torch.float16))   # K mismatch
+    with pytest.raises(ValueError):
+        binding.gemm_nt(h, h)                                 # CPU tensors
+    f8 = h.to(torch.float8_e4m3fn)
+    with pytest.raises(ValueError):
+        binding.gemm_nt(f8, h.to(torch.float8_e5m2))          # mixed FP8 formats are fine; CPU is not

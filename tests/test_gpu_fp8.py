@@ -127,3 +127,29 @@ def test_fp8_headline_size_sampled_rows():
                                      np.random.default_rng(12701).choice(M, 8, replace=False)]))
     ref = _ref(A[rows], B, s, E4, E4)
     assert_tolerance(d[rows], ref, K, "fp8 8192^3 rows")
+
+
+def test_tensor_convenience_every_dtype():
+    import torch
+    from dense_gemm_18_amd import binding
+    dev = torch.device("cuda:0")
+    M, N, K = 300, 260, 512
+    A, B = wl.fp8_integers(12800, M, N, K, E4, E5)
+    note("gemm_nt convenience fp8 / f16 / bf16")
+    dA = torch.from_numpy(A).to(dev).view(torch.float8_e4m3fn)
+    dB = torch.from_numpy(B).to(dev).view(torch.float8_e5m2)
+    d = binding.gemm_nt(dA, dB, scale=0.5)
+    torch.cuda.synchronize(dev)
+    assert d.dtype == torch.float16
+    assert_bitexact(d.cpu().numpy().view(np.uint16), _ref(A, B, 0.5, E4, E5), "gemm_nt fp8")
+    # the same integer operands in fp16 and bfloat16 (exact in both)
+    a16, b16 = oracle.fp8_decode(A).astype(np.float16), oracle.fp8_decode(B, True).astype(np.float16)
+    for dt, ref in ((torch.float16, oracle.gemm_nt_f16(a16, b16)),
+                    (torch.bfloat16, oracle.gemm_nt_bf16(wl.to_bf16_bits(a16), wl.to_bf16_bits(b16)))):
+        a = torch.from_numpy(a16).to(dev).to(dt)
+        b = torch.from_numpy(b16).to(dev).to(dt)
+        out = torch.empty((M, N), dtype=dt, device=dev)
+        r = binding.gemm_nt(a, b, out=out)
+        torch.cuda.synchronize(dev)
+        assert r is out and r.dtype == dt
+        assert_bitexact(r.cpu().view(torch.int16).numpy().view(np.uint16), ref, f"gemm_nt {dt}")

@@ -121,7 +121,7 @@ void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                            scale);
         return;
     }
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    const int vec = store_mode(D, N);
     const int m = (int)M, n = (int)N, kp = (int)(K / 2);
     const Tile t = fp8_tile(M, N, K, lb);
     if (lb == 16) {

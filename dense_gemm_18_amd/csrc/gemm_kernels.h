@@ -306,13 +306,57 @@ __device__ __forceinline__ void store_acc(const f32x16 (&acc)[TM][TN], T *__rest
                          vec_store);
 }
 
+// Staged epilogue of a wave's (16 TM) x (16 TN) output tile: the 16-bit
+// results are first written to the wave's own LDS buffer, rows of 32 TN
+// bytes whose 16-byte chunks are XOR-swizzled by the row (conflict-free for
+// the 16-rows-by-8-bytes writes of one MFMA block), then read back along
+// rows and written to D with 16-byte stores, each instruction covering whole
+// 128-byte lines of consecutive rows.  Written straight from the MFMA layout,
+// one store covers 32 bytes of each of 16 rows; when every CU finishes a
+// tile at once (the lock-step waves of a large GEMM) those partial-line
+// stores take several microseconds to drain, the staged ones about a third.
+// Used for tiles wholly inside D, with D 16-byte aligned and N % 8 == 0.
+template <int TM, int TN>
+struct Stage16 {
+    static constexpr int CPR = 2 * TN;            // 16-byte chunks per row
+    static constexpr int ROWB = 32 * TN;
+    static constexpr int BYTES = 16 * TM * ROWB;
+    // byte offset of the 8-byte group of columns n .. n+3 (n % 4 == 0) of row r
+    __device__ static int offset(int r, int n)
+    {
+        return r * ROWB + (((n >> 3) ^ (r % CPR)) << 4) + ((n >> 2) & 1) * 8;
+    }
+};
+
+// Read a wave's staged tile back row by row and store it at dtile (row
+// pitch N elements).  The caller's writes to `stage` are this wave's own, and
+// LDS operations of one wave complete in order.
+template <int TM, int TN, class T>
+__device__ __forceinline__ void flush_stage16(const char *stage, T *__restrict__ dtile, int N,
+                                              int lane)
+{
+    using S = Stage16<TM, TN>;
+    constexpr int RPI = 64 / S::CPR;              // rows per instruction
+    static_assert(64 % S::CPR == 0 && (16 * TM) % RPI == 0, "whole rows per instruction");
+    const int c = lane % S::CPR, r0 = lane / S::CPR;
+    T *dp = dtile + 8 * c;
+#pragma unroll
+    for (int it = 0; it < 16 * TM / RPI; ++it) {
+        const int r = it * RPI + r0;
+        const u32x4 v = *(const u32x4 *)(stage + r * S::ROWB + ((c ^ (r % S::CPR)) << 4));
+        *(u32x4 *)(dp + (int64_t)r * N) = v;
+    }
+}
+
 // Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
 // accumulator r of block (i, j) holds D[m][n] for
 //   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
+// stage != nullptr: the tile lies wholly inside D and its groups go to the
+// wave's staging buffer (flushed by the caller) instead of D.
 template <int TM, int TN, class T, class Get, class Fin = NoFin>
 __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M, int N,
                                                int mbase, int nbase, int lane, int vec_store,
-                                               Fin fin = Fin{})
+                                               Fin fin = Fin{}, char *stage = nullptr)
 {
     using X4 = typename Vec4<T>::type;
     const int frow = lane & 15, fq = lane >> 4;
@@ -331,7 +375,10 @@ __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 h[r] = (T)u[r];
-            if (vec_store) {
+            if (stage) {
+                *(u32x2 *)(stage + Stage16<TM, TN>::offset(16 * i + frow, 16 * j + 4 * fq)) =
+                    __builtin_bit_cast(u32x2, h);
+            } else if (vec_store) {
                 if (n < N)
                     *(X4 *)(drow + n) = h;
             } else {
@@ -362,13 +409,15 @@ __device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec
 // registers as fp16, 2 VGPRs per group of four), then each group becomes
 // alpha * v + beta * C + bias in fp32 in that order and is stored.  All the
 // loads are in flight together instead of one load latency per group.
-template <int TM, int TN, class Get>
+// WITH_C = false: the caller has established beta == 0 (C is never read),
+// which keeps the C registers out of the staged form.
+template <int TM, int TN, class Get, bool WITH_C = true>
 __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict__ D, int M,
                                                    int N, int mbase, int nbase, int lane,
-                                                   int vec, const Epi &e)
+                                                   int vec, const Epi &e, char *stage = nullptr)
 {
     const int frow = lane & 15, fq = lane >> 4;
-    const bool has_c = e.beta != 0.0f, has_bias = e.bias != nullptr;
+    const bool has_c = WITH_C && e.beta != 0.0f, has_bias = e.bias != nullptr;
     f16x4 cv[TM][TN], bv[TN];
     if (has_bias) {
 #pragma unroll
@@ -410,7 +459,10 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 h[r] = (_Float16)u[r];
-            if (vec) {
+            if (stage) {
+                *(u32x2 *)(stage + Stage16<TM, TN>::offset(16 * i + frow, 16 * j + 4 * fq)) =
+                    __builtin_bit_cast(u32x2, h);
+            } else if (vec) {
                 if (n < N)
                     *(f16x4 *)(drow + n) = h;
             } else {
@@ -1046,21 +1098,48 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // acc = the sum over the current item's K-steps (steps are counted from
     // the item's first one).
 
+    // 16x16 blocks of a tile wholly inside D, with D 16-byte aligned and
+    // N % 8 == 0 (vec_store == 2), go through LDS (store_blocks16's staged
+    // form); with the fused epilogue only for FP8 operands, whose epilogue
+    // is the scale alone (beta == 0).  (The 16-bit fused-epilogue kernel keeps
+    // the direct stores: next to its C registers the staging code makes the
+    // 256 x 256 kernel spill.)  The stages are free once every wave is past its
+    // last fragment read and its loads have landed (wait_vmcnt<0> before
+    // this, then the barrier); each wave then owns BM * BN * 2 / NWAVES
+    // bytes of them.
     auto store_d = [&]() G18_INLINE {
+        const int mb = m0 + wm * C::WTM, nb = n0 + wn * C::WTN;
+        if constexpr (C::MF == 16 && (!EPI || F8 != 0)) {
+            using St = Stage16<C::TM, C::TN>;
+            static_assert(St::BYTES * C::NWAVES <= C::LDS_BYTES, "staging fits the LDS stages");
+            bool staged = vec_store == 2 && m0 + C::BM <= M && n0 + C::BN <= N;
+            if constexpr (EPI)
+                staged = staged && epi.beta == 0.0f;
+            if (staged) {
+                lds_barrier();
+                char *stage = smem + wave * St::BYTES;
+                auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
+                if constexpr (EPI)
+                    store_blocks16_epi<C::TM, C::TN, decltype(get), false>(
+                        get, D, M, N, mb, nb, lane, vec_store, epi, stage);
+                else
+                    store_blocks16<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, NoFin{},
+                                                 stage);
+                flush_stage16<C::TM, C::TN>(stage, D + (int64_t)mb * N + nb, N, lane);
+                return;
+            }
+        }
         if constexpr (EPI) {
             auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
             if constexpr (C::MF == 32)
-                store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
-                                           lane, vec_store, EpiFin{epi, N, vec_store});
+                store_blocks<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store,
+                                           EpiFin{epi, N, vec_store});
             else
-                store_blocks16_epi<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN,
-                                                 lane, vec_store, epi);
+                store_blocks16_epi<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, epi);
         } else if constexpr (C::MF == 32) {
-            store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                    vec_store);
+            store_acc<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
         } else {
-            store_acc16<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                      vec_store);
+            store_acc16<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
         }
     };
 
@@ -1378,6 +1457,18 @@ void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int 
                            tn, vec, sk, epi_arg<EPI>(epi));
 }
 
+// The kernels' vec_store flag: 0 element stores; 1 D (and the epilogue's C
+// and bias, `other`) 8-byte aligned and N % 4 == 0: 8-byte stores and loads;
+// 2 also D 16-byte aligned and N % 8 == 0: whole tiles go through the LDS
+// staged epilogue (the direct-to-LDS kernels with 16x16 blocks).
+inline int store_mode(const void *D, int64_t N, uintptr_t other = 0)
+{
+    const uintptr_t d = (uintptr_t)D;
+    if (((d | other) & 7u) != 0 || N % 4 != 0)
+        return 0;
+    return ((d & 15u) == 0 && N % 8 == 0) ? 2 : 1;
+}
+
 // CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
 // 4-byte loads; C: the register-staged kernel for whatever remains (odd K or
 // 2-byte aligned operands).
@@ -1399,8 +1490,7 @@ template <class C, class CDma, class CDma4, bool EPI = false, bool BF = false>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
                  const Epi &epi = Epi{})
 {
-    const uintptr_t dcb = (uintptr_t)D | (uintptr_t)epi.C | (uintptr_t)epi.bias;
-    const int vec = ((dcb & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    const int vec = store_mode(D, N, (uintptr_t)epi.C | (uintptr_t)epi.bias);
     const SkPlan none{};
     switch (load_bytes(A, B, K)) {
     case 16: launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;

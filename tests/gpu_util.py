@@ -221,10 +221,11 @@ def assert_bitexact(d_gpu, d_ref, what=""):
 
 
 def run_gemm_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, fa: int = 0, fb: int = 0,
-                 a_off: int = 0, b_off: int = 0) -> np.ndarray:
+                 a_off: int = 0, b_off: int = 0, d_off: int = 0) -> np.ndarray:
     """D = scale * A B^T through gemm_nt_fp8 (A, B: FP8 bytes, D: fp16 bit
-    patterns), canaries around D.  `*_off` start an operand that many bytes
-    past a 256-byte boundary."""
+    patterns), canaries around D.  `a_off`, `b_off` start an operand that
+    many bytes past a 256-byte boundary; D starts `d_off` fp16 elements past
+    one."""
     import torch
     from dense_gemm_18_amd import binding
 
@@ -241,13 +242,14 @@ def run_gemm_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, fa: int = 0, 
 
     _ka, pa = put(A, a_off)
     _kb, pb = put(B, b_off)
-    dbuf = torch.full((M * N + 2 * GUARD,), int(np.uint16(CANARY).view(np.int16)),
+    g = GUARD + d_off
+    dbuf = torch.full((M * N + 2 * GUARD + d_off,), int(np.uint16(CANARY).view(np.int16)),
                       dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = binding.gemm_nt_fp8(pa, pb, dbuf.data_ptr() + 2 * GUARD, M, N, K, scale, fa, fb, stream)
+    rc = binding.gemm_nt_fp8(pa, pb, dbuf.data_ptr() + 2 * g, M, N, K, scale, fa, fb, stream)
     assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
     torch.cuda.synchronize(dev)
     host = dbuf.cpu().numpy().view(np.uint16)
-    assert np.all(host[:GUARD] == CANARY), "write before D"
-    assert np.all(host[GUARD + M * N:] == CANARY), "write after D"
-    return host[GUARD: GUARD + M * N].reshape(M, N).copy()
+    assert np.all(host[:g] == CANARY), "write before D"
+    assert np.all(host[g + M * N:] == CANARY), "write after D"
+    return host[g: g + M * N].reshape(M, N).copy()

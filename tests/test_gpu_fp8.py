@@ -77,6 +77,20 @@ def test_fp8_misaligned_operands(a_off, b_off):
                     f"fp8 offsets {a_off},{b_off}")
 
 
+@pytest.mark.parametrize("M,N,K,bm", [(4096, 4096, 128, 256), (1024, 1024, 512, 128),
+                                    (64, 2048, 1024, 64)])
+def test_fp8_staged_and_direct_epilogue(M, N, K, bm):
+    # Whole tiles with D 16-byte aligned and N % 8 == 0 are written through
+    # LDS; D only 8-byte aligned (d_off = 4) takes the direct stores.  Both
+    # bit-exact on integer inputs, on the 256 x 256, 128 x 128 and 64 x 64 tiles.
+    assert binding.gemm_nt_fp8_tile(M, N, K, True)[0] == bm
+    A, B = wl.fp8_integers(12500 + M + K, M, N, K)
+    ref = _ref(A, B, 0.5, E4, E4)
+    note(f"fp8 staged epilogue {M}x{N}x{K} tile {bm}")
+    assert_bitexact(run_gemm_fp8(A, B, 0.5), ref, f"fp8 {M}x{N}x{K} staged")
+    assert_bitexact(run_gemm_fp8(A, B, 0.5, d_off=4), ref, f"fp8 {M}x{N}x{K} direct")
+
+
 @pytest.mark.parametrize("scale", [1.0 / 3.0, -2.5, 1e-3])
 def test_fp8_scales(scale):
     M, N, K = 1100, 1100, 1024

@@ -282,8 +282,9 @@ def main() -> int:
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="only run the GEMM back to back for this many seconds (for sampling "
                          "clock and power with amd-smi); prints the achieved TFLOPS")
-    ap.add_argument("--torch-context", action="store_true",
-                    help="also time torch.nn.functional.linear on the same inputs (context only)")
+    ap.add_argument("--torch-context", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time torch.nn.functional.linear (hipBLASLt) on the same inputs "
+                         "(fp16 path only; context, never a reference)")
     args = ap.parse_args()
 
     if args.gpus != 1:

@@ -213,11 +213,14 @@ struct Epi {
     float alpha, beta;
 };
 
+// Four values of row p at columns n .. n+3 as fp32; columns >= N read as 0
+// and are never accessed.  vec: one 8-byte load (N % 4 == 0 and n % 4 == 0,
+// so the four columns are all valid or all past the end).
 __device__ __forceinline__ f32x4 load4(const _Float16 *p, int n, int N, int vec)
 {
     f32x4 v;
     if (vec) {
-        const f16x4 h = *(const f16x4 *)(p + n);
+        const f16x4 h = n < N ? *(const f16x4 *)(p + n) : f16x4{};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             v[r] = (float)h[r];
@@ -396,7 +399,7 @@ __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M
 __device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec)
 {
     if (vec)
-        return *(const f16x4 *)(p + n);
+        return n < N ? *(const f16x4 *)(p + n) : f16x4{};
     f16x4 h;
 #pragma unroll
     for (int r = 0; r < 4; ++r)

@@ -72,6 +72,9 @@ def _load():
     lib.oracle_gemm_nt_fp8.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_fp8.restype = ctypes.c_int
+    lib.oracle_gemm_nt_fp8_cs.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_float, p, ctypes.c_int]
+    lib.oracle_gemm_nt_fp8_cs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -238,6 +241,27 @@ def gemm_nt_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, a_e5m2: bool =
     d = np.empty((M, N), dtype=np.uint16)
     _load().oracle_gemm_nt_fp8(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(bool(a_e5m2)),
                                int(bool(b_e5m2)), float(np.float32(scale)), int(threads))
+    return d
+
+
+def gemm_nt_fp8_cs(A: np.ndarray, B: np.ndarray, a_scale: float, b_scale: np.ndarray,
+                   a_e5m2: bool = False, b_e5m2: bool = False, threads: int = 0) -> np.ndarray:
+    """D[m, n] = (a_scale * b_scale[n]) * (A B^T)[m, n], the per-column scale
+    formed in fp32; A and B FP8 bit patterns (uint8), b_scale N fp32 values
+    (one per row of B), D fp16 bits."""
+    a = np.ascontiguousarray(A, dtype=np.uint8)
+    b = np.ascontiguousarray(B, dtype=np.uint8)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    s = np.ascontiguousarray(b_scale, dtype=np.float32).ravel()
+    if s.size != N:
+        raise ValueError(f"b_scale has {s.size} values, B has {N} rows")
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_fp8_cs(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(bool(a_e5m2)),
+                                  int(bool(b_e5m2)), float(np.float32(a_scale)), _ptr(s),
+                                  int(threads))
     return d
 
 

@@ -57,6 +57,15 @@
  * product of A's and B's per-tensor dequantisation scales) and rounded once
  * to fp16.
  *
+ * FP8 with per-channel weight scales (oracle_gemm_nt_fp8_cs): the same
+ * article's weight quantisation (section 4.2, step 1) takes one scale per
+ * output channel, the largest magnitude of each weight row over 448, and the
+ * activation one scale per tensor from calibration (step 2).  In this layout
+ * a weight row is a row n of B, so column n of D takes the scale
+ * s_n = a_scale * b_scale[n].  Reading taken: s_n is formed in fp32 (one
+ * rounding, as both scales are fp32 values), then multiplies the exact sum
+ * before the one rounding to fp16.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
  */
@@ -409,6 +418,31 @@ int oracle_gemm_nt_fp8(const uint8_t *A, const uint8_t *B, uint16_t *D, int64_t 
             for (int64_t k = 0; k < K; ++k)
                 acc += la[ar[k]] * lb[br[k]];
             D[m * N + n] = f16_encode_rne(sc * acc);
+        }
+    return nt;
+}
+
+/* Per-channel form: D[m][n] = s_n * (A * B^T)[m][n] with s_n the fp32
+ * product a_scale * b_scale[n] (b_scale: N values, one per row of B). */
+int oracle_gemm_nt_fp8_cs(const uint8_t *A, const uint8_t *B, uint16_t *D, int64_t M, int64_t N,
+                          int64_t K, int a_e5m2, int b_e5m2, float a_scale,
+                          const float *b_scale, int nthreads)
+{
+    double la[256], lb[256];
+    for (int v = 0; v < 256; ++v) {
+        la[v] = fp8_decode((uint8_t)v, a_e5m2);
+        lb[v] = fp8_decode((uint8_t)v, b_e5m2);
+    }
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *ar = A + m * K, *br = B + n * K;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += la[ar[k]] * lb[br[k]];
+            const float sn = a_scale * b_scale[n];
+            D[m * N + n] = f16_encode_rne((double)sn * acc);
         }
     return nt;
 }

@@ -12,6 +12,13 @@ rounding to fp16).
      scale of 3 on a sum that a rounding of the unscaled sum first would send
      to a tie and the other neighbour, ties, and overflow to infinity;
   f5 mixed formats: A in E5M2 and B in E4M3 against the per-format decode.
+
+Per-channel weight scales (D[m, n] = fp32(a_scale * b_scale[n]) * sum):
+  f7 equal column scales reduce to the pinned per-tensor product;
+  f8 integer inputs with power-of-two scales that differ per column (and
+     M != N, so a scale taken per row would not match): exact;
+  f9 brute force on tiny shapes against exact rationals, the column scale
+     formed in fp32.
 """
 from __future__ import annotations
 
@@ -152,3 +159,49 @@ def test_f5_mixed_formats():
 def test_f6_shape_errors():
     with pytest.raises(ValueError):
         oracle.gemm_nt_fp8(np.zeros((2, 3), np.uint8), np.zeros((2, 4), np.uint8))
+
+
+def test_f7_column_scales_reduce_to_per_tensor():
+    A = _finite_fp8(111, (6, 40), False)
+    B = _finite_fp8(112, (9, 40), False)
+    for sa, sb in ((0.5, 0.25), (0.1, 3.0), (1.0 / 3.0, 7.0)):
+        want = oracle.gemm_nt_fp8(A, B, float(np.float32(sa) * np.float32(sb)))
+        got = oracle.gemm_nt_fp8_cs(A, B, sa, np.full(9, sb, np.float32))
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("e5m2", [False, True])
+def test_f8_column_scales_integer_exact(e5m2):
+    M, N, K = 13, 21, 64
+    A, B = _fp8_ints(121, (M, K), e5m2), _fp8_ints(122, (N, K), e5m2)
+    ai = oracle.fp8_decode(A, e5m2)
+    bi = oracle.fp8_decode(B, e5m2)
+    sb = (2.0 ** np.random.default_rng(123).integers(-6, 3, N)).astype(np.float32)
+    sa = 0.5
+    exact = (ai.astype(np.int64) @ bi.astype(np.int64).T) * (sa * sb.astype(np.float64))[None, :]
+    want = np.array([[nearest_f16(Fraction(float(v))) for v in row] for row in exact], np.uint16)
+    assert np.array_equal(oracle.gemm_nt_fp8_cs(A, B, sa, sb, e5m2, e5m2), want)
+
+
+@pytest.mark.parametrize("K,seed", [(7, 131), (24, 132)])
+def test_f9_column_scales_brute_force(K, seed):
+    rng = np.random.default_rng(seed)
+    M, N = 3, 4
+    A = _finite_fp8(seed * 10 + 1, (M, K), False)
+    B = _finite_fp8(seed * 10 + 2, (N, K), True)
+    sa = np.float32(rng.uniform(0.01, 2.0))
+    sb = rng.uniform(0.01, 2.0, N).astype(np.float32)
+    a = [[Fraction(float(v)) for v in r] for r in oracle.fp8_decode(A, False)]
+    b = [[Fraction(float(v)) for v in r] for r in oracle.fp8_decode(B, True)]
+    want = np.empty((M, N), np.uint16)
+    for n in range(N):
+        sn = Fraction(float(np.float32(sa * sb[n])))          # the product rounded to fp32
+        for m in range(M):
+            want[m, n] = nearest_f16(sn * sum((x * y for x, y in zip(a[m], b[n])), Fraction(0)))
+    assert np.array_equal(oracle.gemm_nt_fp8_cs(A, B, float(sa), sb, False, True), want)
+
+
+def test_f9_column_scale_count_checked():
+    with pytest.raises(ValueError):
+        oracle.gemm_nt_fp8_cs(np.zeros((2, 3), np.uint8), np.zeros((4, 3), np.uint8), 1.0,
+                              np.ones(3, np.float32))

@@ -7,7 +7,8 @@ sign, saturation instead of infinity; in the fused epilogue a bias per row,
 beta or alpha on the wrong term, a transposed C, a rounding before the
 epilogue; in FP8 a wrong exponent bias, flushed subnormals, the other NaN
 convention, saturation in place of infinity, swapped formats, a rounding
-before the scale), compiles the copy with gcc, points the oracle wrapper at it
+before the scale; with per-channel scales a scale per row, a dropped
+activation scale, a rounding before the scale), compiles the copy with gcc, points the oracle wrapper at it
 and runs the pin battery.  At least one pin must fail for every planted mistake.  All
 of this runs on the CPU; the real oracle is not modified.
 """
@@ -69,12 +70,21 @@ MUTATIONS = {
                       "if (v == 0x80)\n            return NAN;"),
     "e5m2_inf_as_max": ("return f ? NAN : (sign ? -INFINITY : INFINITY);",
                         "return f ? NAN : (sign ? -57344.0 : 57344.0);"),
-    "fp8_formats_swapped": ("lb[v] = fp8_decode((uint8_t)v, b_e5m2);",
-                            "lb[v] = fp8_decode((uint8_t)v, a_e5m2);"),
+    "fp8_formats_swapped": ("lb[v] = fp8_decode((uint8_t)v, b_e5m2);\n    }\n    int nt = pick_threads(nthreads);\n    const double sc",
+                            "lb[v] = fp8_decode((uint8_t)v, a_e5m2);\n    }\n    int nt = pick_threads(nthreads);\n    const double sc"),
+    "fp8_cs_formats_swapped": ("lb[v] = fp8_decode((uint8_t)v, b_e5m2);\n    }\n    int nt = pick_threads(nthreads);\n#pragma",
+                               "lb[v] = fp8_decode((uint8_t)v, a_e5m2);\n    }\n    int nt = pick_threads(nthreads);\n#pragma"),
     "fp8_round_before_scale": ("D[m * N + n] = f16_encode_rne(sc * acc);",
                                "D[m * N + n] = f16_encode_rne(sc * g_lut[f16_encode_rne(acc)]);"),
-    "fp8_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];",
-                         "for (int64_t k = 1; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];"),
+    "fp8_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];\n            D[m * N + n] = f16_encode_rne(sc * acc);",
+                         "for (int64_t k = 1; k < K; ++k)\n                acc += la[ar[k]] * lb[br[k]];\n            D[m * N + n] = f16_encode_rne(sc * acc);"),
+    # FP8 with per-channel weight scales
+    "fp8_cs_scale_per_row": ("const float sn = a_scale * b_scale[n];",
+                             "const float sn = a_scale * b_scale[m % N];"),
+    "fp8_cs_activation_scale_dropped": ("const float sn = a_scale * b_scale[n];",
+                                        "const float sn = b_scale[n];"),
+    "fp8_cs_round_before_scale": ("D[m * N + n] = f16_encode_rne((double)sn * acc);",
+                                  "D[m * N + n] = f16_encode_rne((double)sn * g_lut[f16_encode_rne(acc)]);"),
 }
 
 
@@ -117,6 +127,11 @@ def _battery():
         lambda: fpins.test_f3_integer_exact(33, 20, 256, 0.5, False),
         fpins.test_f4_scale_applied_once_after_the_sum,
         fpins.test_f5_mixed_formats,
+        fpins.test_f7_column_scales_reduce_to_per_tensor,
+        lambda: fpins.test_f8_column_scales_integer_exact(False),
+        lambda: fpins.test_f8_column_scales_integer_exact(True),
+        lambda: fpins.test_f9_column_scales_brute_force(7, 131),
+        lambda: fpins.test_f9_column_scales_brute_force(24, 132),
     ]
 
 
@@ -153,6 +168,9 @@ def _wrap(path: Path):
     lib.oracle_gemm_nt_fp8.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_fp8.restype = ctypes.c_int
+    lib.oracle_gemm_nt_fp8_cs.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_float, p, ctypes.c_int]
+    lib.oracle_gemm_nt_fp8_cs.restype = ctypes.c_int
     return lib
 
 

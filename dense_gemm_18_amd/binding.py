@@ -22,7 +22,7 @@ GEMM_FP8_E5M2 = 1
 # Every symbol the header declares.
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
            "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
-           "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_tile")
+           "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_cs", "gemm_nt_fp8_tile")
 
 
 class GemmError(RuntimeError):
@@ -78,6 +78,9 @@ def lib():
     L.gemm_nt_fp8.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                               ctypes.c_int, vp]
     L.gemm_nt_fp8.restype = ctypes.c_int
+    L.gemm_nt_fp8_cs.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_float, vp, ctypes.c_int,
+                                 ctypes.c_int, vp]
+    L.gemm_nt_fp8_cs.restype = ctypes.c_int
     L.gemm_nt_fp8_tile.argtypes = [i64, i64, i64, ctypes.c_int, ip, ip]
     L.gemm_nt_fp8_tile.restype = ctypes.c_int
     _lib = L
@@ -169,6 +172,15 @@ def gemm_nt_fp8(A: int, B: int, D: int, M: int, N: int, K: int, scale: float = 1
     return code."""
     return lib().gemm_nt_fp8(A or None, B or None, D or None, M, N, K, scale, a_format,
                              b_format, stream or None)
+
+
+def gemm_nt_fp8_cs(A: int, B: int, D: int, M: int, N: int, K: int, a_scale: float,
+                   b_scale: int, a_format: int = GEMM_FP8_E4M3, b_format: int = GEMM_FP8_E4M3,
+                   stream: int = 0) -> int:
+    """Raw call of the FP8 form with per-channel weight scales (b_scale: device
+    address of N fp32 values, one per row of B); returns the C return code."""
+    return lib().gemm_nt_fp8_cs(A or None, B or None, D or None, M, N, K, a_scale,
+                                b_scale or None, a_format, b_format, stream or None)
 
 
 def gemm_nt_fp8_tile(M: int, N: int, K: int, aligned16: bool = True):

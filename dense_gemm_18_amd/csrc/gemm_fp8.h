@@ -3,6 +3,7 @@
 //
 //   D[m,n] = scale * sum_k A[m,k] * B[n,k]     A, B: OCP E4M3 or E5M2 bytes,
 //                                               D: fp16, fp32 accumulation
+//   (or scale * col_scale[n] per column: per-channel weight scales)
 //
 // FP8 operands with a per-tensor scale kept in fp32 and applied in the
 // epilogue follow the GEMM-optimisation article at www.lqnn.cn (news/123226),
@@ -18,7 +19,7 @@
 // E5M2); defined in gemm_nt_fp8_b5.hip.  Not exported from the library.
 __attribute__((visibility("hidden"))) void gemm18_fp8_launch_b5(
     int f8, const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, float scale,
-    hipStream_t s);
+    const float *col_scale, hipStream_t s);
 
 namespace {
 
@@ -49,11 +50,13 @@ __device__ __forceinline__ float fp8_value(uint32_t v)
 }
 
 // Operands the direct-to-LDS pipeline cannot take (K % 4 != 0 or operands
-// not 4-byte aligned): one output per thread, fp32 sum in ascending k.
+// not 4-byte aligned): one output per thread, fp32 sum in ascending k, times
+// scale (or scale * col_scale[n], formed in fp32, with column scales).
 template <int F8>
 __global__ void __launch_bounds__(256)
 gemm_nt_fp8_plain_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
-                         _Float16 *__restrict__ D, int64_t M, int64_t N, int64_t K, float scale)
+                         _Float16 *__restrict__ D, int64_t M, int64_t N, int64_t K, float scale,
+                         const float *__restrict__ col_scale)
 {
     constexpr int fa = (F8 - 1) & 1, fb = (F8 - 1) >> 1;
     const int64_t count = M * N;
@@ -64,7 +67,7 @@ gemm_nt_fp8_plain_kernel(const uint8_t *__restrict__ A, const uint8_t *__restric
         float acc = 0.0f;
         for (int64_t k = 0; k < K; ++k)
             acc = __builtin_fmaf(fp8_value<fa>(a[k]), fp8_value<fb>(b[k]), acc);
-        D[idx] = (_Float16)(acc * scale);
+        D[idx] = (_Float16)(acc * (col_scale ? scale * col_scale[n] : scale));
     }
 }
 
@@ -110,15 +113,15 @@ Tile fp8_tile(int64_t M, int64_t N, int64_t K, int lb)
 
 template <int F8>
 void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
-                float scale, hipStream_t s)
+                float scale, const float *col_scale, hipStream_t s)
 {
-    const Epi epi{nullptr, nullptr, scale, 0.0f};
+    const Epi epi{nullptr, nullptr, scale, 0.0f, col_scale};
     const int lb = fp8_load_bytes(A, B, K);
     if (lb == 0) {
         const int64_t blocks = cdiv(M * N, 256) < 8192 ? cdiv(M * N, 256) : 8192;
         hipLaunchKernelGGL((gemm_nt_fp8_plain_kernel<F8>), dim3((unsigned)blocks), dim3(256), 0,
                            s, (const uint8_t *)A, (const uint8_t *)B, (_Float16 *)D, M, N, K,
-                           scale);
+                           scale, col_scale);
         return;
     }
     const int vec = store_mode(D, N);

@@ -211,6 +211,9 @@ struct Epi {
     const _Float16 *C;
     const _Float16 *bias;
     float alpha, beta;
+    // FP8 only: N per-column scales; column n is scaled by alpha * col_scale[n]
+    // (formed in fp32) instead of alpha.  Null everywhere else.
+    const float *col_scale;
 };
 
 // Four values of row p at columns n .. n+3 as fp32; columns >= N read as 0
@@ -413,8 +416,10 @@ __device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec
 // alpha * v + beta * C + bias in fp32 in that order and is stored.  All the
 // loads are in flight together instead of one load latency per group.
 // WITH_C = false: the caller has established beta == 0 (C is never read),
-// which keeps the C registers out of the staged form.
-template <int TM, int TN, class Get, bool WITH_C = true>
+// which keeps the C registers out of the staged form.  COLS: per-column
+// scales may be present (FP8 kernels only; the 16-bit fused epilogue is
+// compiled without them).
+template <int TM, int TN, class Get, bool WITH_C = true, bool COLS = false>
 __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict__ D, int M,
                                                    int N, int mbase, int nbase, int lane,
                                                    int vec, const Epi &e, char *stage = nullptr)
@@ -422,6 +427,20 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
     const int frow = lane & 15, fq = lane >> 4;
     const bool has_c = WITH_C && e.beta != 0.0f, has_bias = e.bias != nullptr;
     f16x4 cv[TM][TN], bv[TN];
+    // per-column factors alpha * col_scale[n .. n+3] (columns >= N not read)
+    f32x4 sv[COLS ? TN : 1];
+    const bool has_cs = COLS && e.col_scale != nullptr;
+    if constexpr (COLS) {
+        if (has_cs) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = nbase + 16 * j + 4 * fq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sv[j][r] = e.alpha * (n + r < N ? e.col_scale[n + r] : 0.0f);
+            }
+        }
+    }
     if (has_bias) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -447,7 +466,12 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
             if (m >= M)
                 continue;
             const int n = nbase + 16 * j + 4 * fq;
-            f32x4 u = v * e.alpha;
+            f32x4 u;
+            if constexpr (COLS) {
+                u = has_cs ? v * sv[j] : v * e.alpha;
+            } else {
+                u = v * e.alpha;
+            }
             if (has_c) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -1123,7 +1147,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 char *stage = smem + wave * St::BYTES;
                 auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
                 if constexpr (EPI)
-                    store_blocks16_epi<C::TM, C::TN, decltype(get), false>(
+                    store_blocks16_epi<C::TM, C::TN, decltype(get), false, (F8 != 0)>(
                         get, D, M, N, mb, nb, lane, vec_store, epi, stage);
                 else
                     store_blocks16<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, NoFin{},
@@ -1138,7 +1162,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 store_blocks<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store,
                                            EpiFin{epi, N, vec_store});
             else
-                store_blocks16_epi<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, epi);
+                store_blocks16_epi<C::TM, C::TN, decltype(get), true, (F8 != 0)>(
+                    get, D, M, N, mb, nb, lane, vec_store, epi);
         } else if constexpr (C::MF == 32) {
             store_acc<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
         } else {
@@ -1323,13 +1348,15 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     }
 }
 
-// K == 0 with the fused epilogue: D = alpha * (+0) + beta * C + bias.
+// K == 0 with the fused epilogue: D = alpha * (+0) + beta * C + bias (with FP8
+// column scales, alpha * col_scale[n] in place of alpha).
 [[maybe_unused]] __global__ void epilogue_only_kernel(_Float16 *__restrict__ D, Epi e, int64_t M, int64_t N)
 {
     const int64_t count = M * N;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
-        float v = e.alpha * 0.0f;
+        const float s = e.col_scale ? e.alpha * e.col_scale[i % N] : e.alpha;
+        float v = s * 0.0f;
         if (e.beta != 0.0f)
             v = v + e.beta * (float)e.C[i];
         if (e.bias)

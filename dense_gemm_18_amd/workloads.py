@@ -198,6 +198,26 @@ def fp8_normal(seed: int, M: int, N: int, K: int, fa: int = 0, fb: int = 0):
     return A, B, float(np.float32(sa * sb))
 
 
+def fp8_channelwise(seed: int, M: int, N: int, K: int, fa: int = 0, fb: int = 0):
+    """Inputs of the per-channel FP8 product (input preparation only), after
+    the GEMM-optimisation article at www.lqnn.cn, section 4.2: A (activations,
+    standard normal) quantised with one per-tensor scale, B (weights,
+    N(0, 0.02^2) with per-row magnitudes spread over [0.25, 4] so that the
+    channel scales differ) with one scale per row mapping that row's largest
+    magnitude to the format's largest finite value.  Returns (A, B, a_scale,
+    b_scale) with b_scale N fp32 values."""
+    import torch
+    rng = np.random.default_rng(seed)
+    A, sa = fp8_quantize(rng.standard_normal((M, K), dtype=np.float32), fa)
+    W = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+         * rng.uniform(0.25, 4.0, (N, 1)).astype(np.float32))
+    amax = np.abs(W).max(axis=1) if K else np.zeros(N, np.float32)
+    sb = np.where(amax > 0, amax / np.float32(FP8_MAX[fb]), 1.0).astype(np.float32)
+    dt = torch.float8_e5m2 if fb else torch.float8_e4m3fn
+    B = torch.from_numpy(np.ascontiguousarray(W / sb[:, None])).to(dt).view(torch.uint8).numpy().copy()
+    return A, B, float(sa), sb
+
+
 def fp8_integers(seed: int, M: int, N: int, K: int, fa: int = 0, fb: int = 0, lo: int = -4,
                  hi: int = 4):
     """FP8 A, B with integer entries in {lo..hi} (exact in both formats for

@@ -109,6 +109,29 @@ int gemm_nt_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                 float scale, int a_format, int b_format, hipStream_t stream);
 
 /*
+ * FP8 product with per-channel weight scales (the same article, section 4.2:
+ * weights are quantised with one scale per output channel, the largest
+ * magnitude of each weight row over 448, activations with one scale per
+ * tensor).  B holds the weights, so row n of B is output channel n:
+ *
+ *     D[m,n] = (a_scale * b_scale[n]) * sum_{k<K} A[m,k] * B[n,k]
+ *
+ * A, B, D, formats and the fast path as gemm_nt_fp8.
+ * a_scale: fp32, A's dequantisation scale.  b_scale: device pointer to N
+ *   fp32 values (B's per-row dequantisation scales), 4-byte aligned, read
+ *   only, owned by the caller; it may be NULL only when M or N is 0.  The
+ *   factor a_scale * b_scale[n] is formed in fp32 (round to nearest even),
+ *   then multiplies the fp32 sum, and the result is rounded once to fp16.
+ *   K == 0 gives (a_scale * b_scale[n]) * (+0).
+ *
+ * Returns as gemm_nt_fp8, and GEMM_EINVAL also for a NULL or misaligned
+ * b_scale, or D overlapping b_scale.
+ */
+int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                   float a_scale, const float *b_scale, int a_format, int b_format,
+                   hipStream_t stream);
+
+/*
  * Host-only: the output tile gemm_nt_fp8 uses for these sizes (aligned16:
  * whether A and B are 16-byte aligned; 4-byte alignment is assumed
  * otherwise).  *bm = *bn = 0 when the plain per-output kernel runs.

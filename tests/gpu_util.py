@@ -253,3 +253,33 @@ def run_gemm_fp8(A: np.ndarray, B: np.ndarray, scale: float = 1.0, fa: int = 0, 
     assert np.all(host[:g] == CANARY), "write before D"
     assert np.all(host[g + M * N:] == CANARY), "write after D"
     return host[g: g + M * N].reshape(M, N).copy()
+
+
+def run_gemm_fp8_cs(A: np.ndarray, B: np.ndarray, a_scale: float, b_scale: np.ndarray,
+                    fa: int = 0, fb: int = 0, d_off: int = 0) -> np.ndarray:
+    """D = (a_scale * b_scale[n]) * A B^T through gemm_nt_fp8_cs (A, B: FP8
+    bytes, b_scale: N fp32 values copied to the device, D: fp16 bit
+    patterns), canaries around D; D starts `d_off` fp16 elements past a
+    256-byte boundary."""
+    import torch
+    from dense_gemm_18_amd import binding
+
+    M, K = A.shape
+    N = B.shape[0]
+    dev = device()
+    dA = torch.from_numpy(np.ascontiguousarray(A, dtype=np.uint8).copy()).to(dev)
+    dB = torch.from_numpy(np.ascontiguousarray(B, dtype=np.uint8).copy()).to(dev)
+    dS = torch.from_numpy(np.ascontiguousarray(b_scale, dtype=np.float32).copy()).to(dev)
+    g = GUARD + d_off
+    dbuf = torch.full((M * N + 2 * GUARD + d_off,), int(np.uint16(CANARY).view(np.int16)),
+                      dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = binding.gemm_nt_fp8_cs(dA.data_ptr() if A.size else 0, dB.data_ptr() if B.size else 0,
+                                dbuf.data_ptr() + 2 * g, M, N, K, a_scale, dS.data_ptr(), fa, fb,
+                                stream)
+    assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
+    torch.cuda.synchronize(dev)
+    host = dbuf.cpu().numpy().view(np.uint16)
+    assert np.all(host[:g] == CANARY), "write before D"
+    assert np.all(host[g + M * N:] == CANARY), "write after D"
+    return host[g: g + M * N].reshape(M, N).copy()

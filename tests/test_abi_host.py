@@ -195,6 +195,26 @@ def test_fp8_accepts_odd_operand_addresses_and_empty_outputs():
     assert binding.gemm_nt_fp8(0, 0, 0, 0, 0, 9, 2.0, E5, E5, 0) == binding.GEMM_OK
 
 
+S0 = FAKE + 0x3000000    # a column-scale address
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, -1, 4, 4, 1.0, S0, E4, E4),     # negative M
+    (0, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, S0, E4, E4),         # NULL A
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, 0, E4, E4),       # NULL b_scale
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, S0 + 2, E4, E4),  # misaligned
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, FAKE + 0x2000008, E4, E4),  # D overlaps
+    (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, 4, 4, 4, 1.0, S0, E4, 3),       # unknown format
+])
+def test_fp8_cs_validation_rejects_before_any_hip_call(args):
+    assert binding.gemm_nt_fp8_cs(*args, 0) == binding.GEMM_EINVAL
+
+
+def test_fp8_cs_empty_output_needs_no_scales():
+    assert binding.gemm_nt_fp8_cs(0, FAKE, 0, 0, 5, 4, 1.0, 0, E4, E4, 0) == binding.GEMM_OK
+    assert binding.gemm_nt_fp8_cs(FAKE, 0, 0, 5, 0, 4, 1.0, 0, E4, E5, 0) == binding.GEMM_OK
+
+
 @pytest.mark.parametrize("M,N,K,aligned,tile", [
     (8192, 8192, 8192, True, (256, 256)),
     (2048, 2048, 4096, True, (128, 128)),

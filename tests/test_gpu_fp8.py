@@ -23,7 +23,8 @@ import pytest
 import oracle
 from dense_gemm_18_amd import binding
 from dense_gemm_18_amd import workloads as wl
-from tests.gpu_util import assert_bitexact, assert_tolerance, note, run_gemm_fp8
+from tests.gpu_util import (assert_bitexact, assert_tolerance, note, run_gemm_fp8,
+                            run_gemm_fp8_cs)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +168,74 @@ def test_tensor_convenience_every_dtype():
         torch.cuda.synchronize(dev)
         assert r is out and r.dtype == dt
         assert_bitexact(r.cpu().view(torch.int16).numpy().view(np.uint16), ref, f"gemm_nt {dt}")
+
+
+# ---- per-channel weight scales (gemm_nt_fp8_cs) ------------------------------
+
+def _ref_cs(A, B, sa, sb, fa=E4, fb=E4):
+    return oracle.gemm_nt_fp8_cs(A, B, sa, sb, bool(fa), bool(fb))
+
+
+def _pow2_scales(seed, N):
+    return (2.0 ** np.random.default_rng(seed).integers(-3, 3, N)).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_cs_integer_bitexact(M, N, K):
+    # power-of-two column scales that differ per column: exact on every tile,
+    # load width and the plain kernel
+    A, B = wl.fp8_integers(13000 + K, M, N, K)
+    sb = _pow2_scales(13001 + N, N)
+    note(f"fp8 column scales integer {M}x{N}x{K}")
+    assert_bitexact(run_gemm_fp8_cs(A, B, 0.5, sb), _ref_cs(A, B, 0.5, sb),
+                    f"fp8 cs integer {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_cs_channelwise_quantised(M, N, K):
+    A, B, sa, sb = wl.fp8_channelwise(13100 + K, M, N, K)
+    note(f"fp8 channel-wise {M}x{N}x{K}")
+    assert_tolerance(run_gemm_fp8_cs(A, B, sa, sb), _ref_cs(A, B, sa, sb), K,
+                     f"fp8 cs {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E5), (E5, E4)])
+def test_fp8_cs_format_pairs_and_direct_stores(fa, fb):
+    # mixed formats; D only 8-byte aligned takes the direct stores
+    A, B = wl.fp8_integers(13200 + fa, 1024, 1024, 512, fa, fb)
+    sb = _pow2_scales(13201, 1024)
+    ref = _ref_cs(A, B, 2.0, sb, fa, fb)
+    note(f"fp8 column scales formats {fa},{fb}")
+    assert_bitexact(run_gemm_fp8_cs(A, B, 2.0, sb, fa, fb), ref, "staged")
+    assert_bitexact(run_gemm_fp8_cs(A, B, 2.0, sb, fa, fb, d_off=4), ref, "direct")
+
+
+def test_fp8_cs_equal_scales_match_per_tensor():
+    # equal column scales give the per-tensor product with the fp32 product
+    # of the two scales, bit for bit on the GPU too
+    A, B, s = wl.fp8_normal(13300, 1000, 1032, 1024)
+    sa, sbv = np.float32(0.37), np.float32(s / 0.37)
+    sb = np.full(1032, sbv, np.float32)
+    note("fp8 equal column scales")
+    assert np.array_equal(run_gemm_fp8_cs(A, B, float(sa), sb),
+                          run_gemm_fp8(A, B, float(np.float32(sa * sbv))))
+
+
+def test_fp8_cs_k_zero_and_signs():
+    # K = 0: (a_scale * b_scale[n]) * (+0), so columns with a negative scale
+    # hold -0
+    sb = np.array([1.0, -2.0, 0.5, -0.25, 3.0], np.float32)
+    A = np.zeros((3, 0), np.uint8)
+    B = np.zeros((5, 0), np.uint8)
+    note("fp8 column scales K = 0")
+    assert_bitexact(run_gemm_fp8_cs(A, B, 1.5, sb), _ref_cs(A, B, 1.5, sb), "K = 0")
+
+
+def test_fp8_cs_headline_size_sampled_rows():
+    M = N = K = 8192
+    A, B, sa, sb = wl.fp8_channelwise(13400, M, N, K)
+    note("fp8 column scales 8192^3 sampled rows")
+    d = run_gemm_fp8_cs(A, B, sa, sb)
+    rows = np.unique(np.concatenate([wl.edge_lines(M, 256),
+                                     np.random.default_rng(13401).choice(M, 8, replace=False)]))
+    assert_tolerance(d[rows], _ref_cs(A[rows], B, sa, sb), K, "fp8 cs 8192^3 rows")

@@ -1,7 +1,7 @@
 """Throughput of the NT GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--path f16|f16_ex|f16_ws|bf16|fp8]
+                    [--path f16|f16_ex|f16_ws|bf16|fp8|fp8_cs]
 
 A step is one call of the chosen entry point (the whole hot path): by
 default gemm_nt_f16 on the 8192 x 8192 x 8192 workload, A [M,K] and B [N,K]
@@ -12,8 +12,8 @@ TFLOPS = 2*M*N*K / t (page "构建 Tiled GEMM", section "GEMM").
 The other paths time the library's other entry points on the same workload
 (or the one named): the fused epilogue (alpha 0.5, beta 1, with C and a
 bias), the stream-K form (default workload 1024 x 1024 x 16384), bfloat16
-storage, and FP8 E4M3 operands quantised from normal values with a
-per-tensor scale.
+storage, FP8 E4M3 operands quantised from normal values with a per-tensor
+scale, and FP8 with per-channel weight scales.
 
 Prints one JSON line with the metric, a roofline object for the GEMM kernel
 (achieved TFLOP/s from HIP events on the launch stream, against the MI355X
@@ -49,6 +49,7 @@ PATH_SOURCES = {
     "f16_ex": ["gemm_kernels.h", "gemm_nt_f16_ex.hip"],
     "bf16": ["gemm_kernels.h", "gemm_nt_bf16.hip"],
     "fp8": ["gemm_kernels.h", "gemm_fp8.h", "gemm_nt_fp8.hip"],
+    "fp8_cs": ["gemm_kernels.h", "gemm_fp8.h", "gemm_nt_fp8.hip"],
 }
 KERNEL_SOURCES = [CSRC / f for f in PATH_SOURCES["f16"]]
 
@@ -259,6 +260,27 @@ def setup_path(path, w, torch, dev, binding, wl) -> dict:
                             f"{w.seeds[0]}",
                        "B": "standard normal quantised to E4M3 (per-tensor scale), same stream",
                        "scale": scale}
+    elif path == "fp8_cs":
+        import oracle
+        A, B, sa, sb = wl.fp8_channelwise(w.seeds[0], M, N, K)
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        dS = torch.from_numpy(sb).to(dev)
+        pa, pb, ps = dA.data_ptr(), dB.data_ptr(), dS.data_ptr()
+        keep += [dA, dB, dS]
+        e4 = binding.GEMM_FP8_E4M3
+        P.update(entry="gemm_nt_fp8_cs", dtype="fp8_e4m3", peak=PEAK_FP8_TFLOPS,
+                 bytes=algorithmic_bytes(M, N, K, elem=1, extra=4.0 * N),
+                 tile=list(binding.gemm_nt_fp8_tile(M, N, K, True)) + [128],
+                 metric=f"FP8 E4M3 GEMM TFLOPS (2MNK/t) with per-channel weight scales, "
+                        f"{M}x{N}x{K}, fp16 out; % of MI355X dense FP8 MFMA peak",
+                 step=lambda: check(binding.gemm_nt_fp8_cs(pa, pb, pd, M, N, K, sa, ps, e4, e4,
+                                                           sptr), "gemm_nt_fp8_cs"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_fp8_cs(A[r0:r1], B, sa, sb, threads=t))
+        P["inputs"] = {"A": f"standard normal quantised to E4M3 (per-tensor scale), seed "
+                            f"{w.seeds[0]}",
+                       "B": "N(0, 0.02^2) weights, rows scaled by U[0.25, 4], quantised to E4M3 "
+                            "with one scale per row, same stream",
+                       "a_scale": sa}
     else:
         raise ValueError(path)
     return P

@@ -194,12 +194,14 @@ def gemm_nt_fp8_tile(M: int, N: int, K: int, aligned16: bool = True):
 
 # ---- tensor-level convenience ----------------------------------------------
 
-def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0):
+def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0, b_scale=None):
     """D = A @ B.T for CUDA (HIP) tensors A [M, K] and B [N, K].
 
     float16 A and B call gemm_nt_f16 (D float16), bfloat16 call gemm_nt_bf16
     (D bfloat16); float8_e4m3fn / float8_e5m2 operands (the two may differ)
-    call gemm_nt_fp8 with ``scale`` (D float16).  ``out`` (optional) is a
+    call gemm_nt_fp8 with ``scale`` (D float16), or, given ``b_scale`` (a
+    contiguous float32 tensor of N per-row scales of B on the same device),
+    gemm_nt_fp8_cs with a_scale = ``scale``.  ``out`` (optional) is a
     contiguous [M, N] tensor of D's dtype on the same device.  The call is
     enqueued on ``stream`` (default: the current stream).
     """
@@ -228,7 +230,17 @@ def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0):
         raise ValueError(f"out must be a contiguous {out_dtype} [M, N] tensor on A's device")
     s = stream if stream is not None else torch.cuda.current_stream(A.device)
     pa, pb, pd = A.data_ptr(), B.data_ptr(), out.data_ptr()
-    if A.dtype in fp8:
+    if b_scale is not None:
+        if A.dtype not in fp8:
+            raise TypeError("b_scale applies to FP8 operands only")
+        if (b_scale.dtype != torch.float32 or b_scale.numel() != N or not b_scale.is_contiguous()
+                or b_scale.device != A.device):
+            raise ValueError("b_scale must be a contiguous float32 tensor of N values on A's device")
+    if A.dtype in fp8 and b_scale is not None:
+        name = "gemm_nt_fp8_cs"
+        rc = gemm_nt_fp8_cs(pa, pb, pd, M, N, K, scale, b_scale.data_ptr(), fp8[A.dtype],
+                            fp8[B.dtype], s.cuda_stream)
+    elif A.dtype in fp8:
         name = "gemm_nt_fp8"
         rc = gemm_nt_fp8(pa, pb, pd, M, N, K, scale, fp8[A.dtype], fp8[B.dtype], s.cuda_stream)
     elif A.dtype == torch.bfloat16:

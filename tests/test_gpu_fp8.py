@@ -157,6 +157,12 @@ def test_tensor_convenience_every_dtype():
     torch.cuda.synchronize(dev)
     assert d.dtype == torch.float16
     assert_bitexact(d.cpu().numpy().view(np.uint16), _ref(A, B, 0.5, E4, E5), "gemm_nt fp8")
+    # per-channel scales of B's rows
+    sb = _pow2_scales(12801, N)
+    d = binding.gemm_nt(dA, dB, scale=0.5, b_scale=torch.from_numpy(sb).to(dev))
+    torch.cuda.synchronize(dev)
+    assert_bitexact(d.cpu().numpy().view(np.uint16), _ref_cs(A, B, 0.5, sb, E4, E5),
+                    "gemm_nt fp8 column scales")
     # the same integer operands in fp16 and bfloat16 (exact in both)
     a16, b16 = oracle.fp8_decode(A).astype(np.float16), oracle.fp8_decode(B, True).astype(np.float16)
     for dt, ref in ((torch.float16, oracle.gemm_nt_f16(a16, b16)),

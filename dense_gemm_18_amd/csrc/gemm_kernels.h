@@ -415,30 +415,28 @@ __device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec
 // registers as fp16, 2 VGPRs per group of four), then each group becomes
 // alpha * v + beta * C + bias in fp32 in that order and is stored.  All the
 // loads are in flight together instead of one load latency per group.
-// WITH_C = false: the caller has established beta == 0 (C is never read),
-// which keeps the C registers out of the staged form.  COLS: per-column
-// scales may be present (FP8 kernels only; the 16-bit fused epilogue is
-// compiled without them).
-template <int TM, int TN, class Get, bool WITH_C = true, bool COLS = false>
+// WITH_C / WITH_BIAS = false: the caller has established that C (beta == 0)
+// or the bias is absent, which keeps their registers and code out (the FP8
+// kernels, whose epilogue is a scale alone).  COLS: e.col_scale is present
+// (FP8 with per-channel scales; the caller branches on it once, so that no
+// form computes the other's arithmetic).
+template <int TM, int TN, class Get, bool WITH_C = true, bool COLS = false, bool WITH_BIAS = true>
 __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict__ D, int M,
                                                    int N, int mbase, int nbase, int lane,
                                                    int vec, const Epi &e, char *stage = nullptr)
 {
     const int frow = lane & 15, fq = lane >> 4;
-    const bool has_c = WITH_C && e.beta != 0.0f, has_bias = e.bias != nullptr;
+    const bool has_c = WITH_C && e.beta != 0.0f, has_bias = WITH_BIAS && e.bias != nullptr;
     f16x4 cv[TM][TN], bv[TN];
     // per-column factors alpha * col_scale[n .. n+3] (columns >= N not read)
     f32x4 sv[COLS ? TN : 1];
-    const bool has_cs = COLS && e.col_scale != nullptr;
     if constexpr (COLS) {
-        if (has_cs) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int n = nbase + 16 * j + 4 * fq;
+        for (int j = 0; j < TN; ++j) {
+            const int n = nbase + 16 * j + 4 * fq;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sv[j][r] = e.alpha * (n + r < N ? e.col_scale[n + r] : 0.0f);
-            }
+            for (int r = 0; r < 4; ++r)
+                sv[j][r] = e.alpha * (n + r < N ? e.col_scale[n + r] : 0.0f);
         }
     }
     if (has_bias) {
@@ -467,11 +465,10 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
                 continue;
             const int n = nbase + 16 * j + 4 * fq;
             f32x4 u;
-            if constexpr (COLS) {
-                u = has_cs ? v * sv[j] : v * e.alpha;
-            } else {
+            if constexpr (COLS)
+                u = v * sv[j];
+            else
                 u = v * e.alpha;
-            }
             if (has_c) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -1146,9 +1143,14 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 lds_barrier();
                 char *stage = smem + wave * St::BYTES;
                 auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
-                if constexpr (EPI)
-                    store_blocks16_epi<C::TM, C::TN, decltype(get), false, (F8 != 0)>(
-                        get, D, M, N, mb, nb, lane, vec_store, epi, stage);
+                if constexpr (EPI) {     // FP8: the scale alone, or per-column scales
+                    if (epi.col_scale)
+                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, true, false>(
+                            get, D, M, N, mb, nb, lane, vec_store, epi, stage);
+                    else
+                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, false, false>(
+                            get, D, M, N, mb, nb, lane, vec_store, epi, stage);
+                }
                 else
                     store_blocks16<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, NoFin{},
                                                  stage);
@@ -1161,9 +1163,16 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             if constexpr (C::MF == 32)
                 store_blocks<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store,
                                            EpiFin{epi, N, vec_store});
-            else
-                store_blocks16_epi<C::TM, C::TN, decltype(get), true, (F8 != 0)>(
-                    get, D, M, N, mb, nb, lane, vec_store, epi);
+            else if constexpr (F8 != 0) {
+                if (epi.col_scale)
+                    store_blocks16_epi<C::TM, C::TN, decltype(get), false, true, false>(
+                        get, D, M, N, mb, nb, lane, vec_store, epi);
+                else
+                    store_blocks16_epi<C::TM, C::TN, decltype(get), false, false, false>(
+                        get, D, M, N, mb, nb, lane, vec_store, epi);
+            } else {
+                store_blocks16_epi<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, epi);
+            }
         } else if constexpr (C::MF == 32) {
             store_acc<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
         } else {

@@ -357,9 +357,10 @@ __device__ __forceinline__ void flush_stage16(const char *stage, T *__restrict__
 // Same for v_mfma_f32_16x16x32_f16 blocks (B as the first operand):
 // accumulator r of block (i, j) holds D[m][n] for
 //   m = mbase + 16 i + lane % 16,  n = nbase + 16 j + 4 (lane / 16) + r.
-// stage != nullptr: the tile lies wholly inside D and its groups go to the
-// wave's staging buffer (flushed by the caller) instead of D.
-template <int TM, int TN, class T, class Get, class Fin = NoFin>
+// STAGED: the tile lies wholly inside D (no row or column checks) and its
+// groups go to the wave's staging buffer `stage` (flushed by the caller)
+// instead of D.
+template <int TM, int TN, class T, class Get, class Fin = NoFin, bool STAGED = false>
 __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M, int N,
                                                int mbase, int nbase, int lane, int vec_store,
                                                Fin fin = Fin{}, char *stage = nullptr)
@@ -373,15 +374,17 @@ __device__ __forceinline__ void store_blocks16(Get get, T *__restrict__ D, int M
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const f32x4 v = get(i, j);
-            if (m >= M)
-                continue;
+            if constexpr (!STAGED) {
+                if (m >= M)
+                    continue;
+            }
             const int n = nbase + 16 * j + 4 * fq;
             const f32x4 u = fin(v, m, n);
             X4 h;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 h[r] = (T)u[r];
-            if (stage) {
+            if constexpr (STAGED) {
                 *(u32x2 *)(stage + Stage16<TM, TN>::offset(16 * i + frow, 16 * j + 4 * fq)) =
                     __builtin_bit_cast(u32x2, h);
             } else if (vec_store) {
@@ -420,7 +423,8 @@ __device__ __forceinline__ f16x4 load4h(const _Float16 *p, int n, int N, int vec
 // kernels, whose epilogue is a scale alone).  COLS: e.col_scale is present
 // (FP8 with per-channel scales; the caller branches on it once, so that no
 // form computes the other's arithmetic).
-template <int TM, int TN, class Get, bool WITH_C = true, bool COLS = false, bool WITH_BIAS = true>
+template <int TM, int TN, class Get, bool WITH_C = true, bool COLS = false, bool WITH_BIAS = true,
+          bool STAGED = false>
 __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict__ D, int M,
                                                    int N, int mbase, int nbase, int lane,
                                                    int vec, const Epi &e, char *stage = nullptr)
@@ -461,8 +465,10 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const f32x4 v = get(i, j);
-            if (m >= M)
-                continue;
+            if constexpr (!STAGED) {
+                if (m >= M)
+                    continue;
+            }
             const int n = nbase + 16 * j + 4 * fq;
             f32x4 u;
             if constexpr (COLS)
@@ -483,7 +489,7 @@ __device__ __forceinline__ void store_blocks16_epi(Get get, _Float16 *__restrict
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 h[r] = (_Float16)u[r];
-            if (stage) {
+            if constexpr (STAGED) {
                 *(u32x2 *)(stage + Stage16<TM, TN>::offset(16 * i + frow, 16 * j + 4 * fq)) =
                     __builtin_bit_cast(u32x2, h);
             } else if (vec) {
@@ -1145,15 +1151,15 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
                 if constexpr (EPI) {     // FP8: the scale alone, or per-column scales
                     if (epi.col_scale)
-                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, true, false>(
+                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, true, false, true>(
                             get, D, M, N, mb, nb, lane, vec_store, epi, stage);
                     else
-                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, false, false>(
+                        store_blocks16_epi<C::TM, C::TN, decltype(get), false, false, false, true>(
                             get, D, M, N, mb, nb, lane, vec_store, epi, stage);
                 }
                 else
-                    store_blocks16<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store, NoFin{},
-                                                 stage);
+                    store_blocks16<C::TM, C::TN, typename Elem<BF>::T, decltype(get), NoFin, true>(
+                        get, D, M, N, mb, nb, lane, vec_store, NoFin{}, stage);
                 flush_stage16<C::TM, C::TN>(stage, D + (int64_t)mb * N + nb, N, lane);
                 return;
             }

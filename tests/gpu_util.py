@@ -152,9 +152,10 @@ def run_gemm_ex(A: np.ndarray, B: np.ndarray, C=None, bias=None, alpha=1.0, beta
     return host[GUARD: GUARD + M * N].reshape(M, N).copy()
 
 
-def run_gemm_bf16(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+def run_gemm_bf16(A: np.ndarray, B: np.ndarray, d_off: int = 0) -> np.ndarray:
     """bfloat16 D = A B^T through gemm_nt_bf16 (uint16 bit patterns in and
-    out), canaries around D."""
+    out), canaries around D; D starts `d_off` elements past a 256-byte
+    boundary."""
     import torch
     from dense_gemm_18_amd import binding
 
@@ -163,17 +164,18 @@ def run_gemm_bf16(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     dev = device()
     dA = torch.from_numpy(np.ascontiguousarray(A, np.uint16).view(np.int16).copy()).to(dev)
     dB = torch.from_numpy(np.ascontiguousarray(B, np.uint16).view(np.int16).copy()).to(dev)
-    dbuf = torch.full((M * N + 2 * GUARD,), int(np.uint16(CANARY).view(np.int16)),
+    g = GUARD + d_off
+    dbuf = torch.full((M * N + 2 * GUARD + d_off,), int(np.uint16(CANARY).view(np.int16)),
                       dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = binding.gemm_nt_bf16(dA.data_ptr(), dB.data_ptr(), dbuf.data_ptr() + 2 * GUARD, M, N, K,
+    rc = binding.gemm_nt_bf16(dA.data_ptr(), dB.data_ptr(), dbuf.data_ptr() + 2 * g, M, N, K,
                               stream)
     assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
     torch.cuda.synchronize(dev)
     host = dbuf.cpu().numpy().view(np.uint16)
-    assert np.all(host[:GUARD] == CANARY), "write before D"
-    assert np.all(host[GUARD + M * N:] == CANARY), "write after D"
-    return host[GUARD: GUARD + M * N].reshape(M, N).copy()
+    assert np.all(host[:g] == CANARY), "write before D"
+    assert np.all(host[g + M * N:] == CANARY), "write after D"
+    return host[g: g + M * N].reshape(M, N).copy()
 
 
 def f16val(bits: np.ndarray) -> np.ndarray:

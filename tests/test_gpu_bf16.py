@@ -44,6 +44,19 @@ def test_bf16_integer_bitexact(M, N, K):
     assert diff.size == 0, f"{diff.size} entries differ, first {diff[:5]}"
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 64), (1000, 1032, 192), (64, 4096, 512)])
+def test_bf16_staged_and_direct_epilogue(M, N, K):
+    # whole tiles with D 16-byte aligned and N % 8 == 0 go through LDS; with D
+    # only 8-byte aligned (d_off = 4) the same tiles take the direct stores
+    A, B = wl.bf16_integers(9900 + M + K, M, N, K)
+    ref = oracle.gemm_nt_bf16(A, B)
+    note(f"bf16 staged epilogue {M}x{N}x{K}")
+    for d_off in (0, 4):
+        d = run_gemm_bf16(A, B, d_off=d_off)
+        diff = np.flatnonzero(d != ref)
+        assert diff.size == 0, f"d_off {d_off}: {diff.size} entries differ, first {diff[:5]}"
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_bf16_random_tolerance(M, N, K):
     A, B = wl.bf16_uniform(9800 + K, M, N, K)

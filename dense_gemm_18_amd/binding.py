@@ -22,7 +22,8 @@ GEMM_FP8_E5M2 = 1
 # Every symbol the header declares.
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
            "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
-           "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_cs", "gemm_nt_fp8_tile")
+           "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_cs", "gemm_nt_fp8_tile",
+           "gemm_nt_f16_kernel")
 
 
 class GemmError(RuntimeError):
@@ -60,6 +61,8 @@ def lib():
     lp = ctypes.POINTER(ctypes.c_int64)
     L.gemm_nt_f16_tile.argtypes = [i64, i64, i64, ip, ip, ip, lp]
     L.gemm_nt_f16_tile.restype = ctypes.c_int
+    L.gemm_nt_f16_kernel.argtypes = [vp, vp, vp, i64, i64, i64, ip, ip, ip, ip]
+    L.gemm_nt_f16_kernel.restype = ctypes.c_int
     L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
     L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
     L.gemm_nt_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -107,6 +110,17 @@ def gemm_nt_f16_tile(M: int, N: int, K: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_tile")
     return bm.value, bn.value, bk.value, wg.value
+
+
+def gemm_nt_f16_kernel(A: int, B: int, D: int, M: int, N: int, K: int):
+    """(BM, BN, load_bytes, store_mode) of the kernel a gemm_nt_f16 call with
+    these device addresses and sizes takes (host-only, nothing is read)."""
+    bm, bn, lb, st = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().gemm_nt_f16_kernel(A or None, B or None, D or None, M, N, K, ctypes.byref(bm),
+                                  ctypes.byref(bn), ctypes.byref(lb), ctypes.byref(st))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_kernel")
+    return bm.value, bn.value, lb.value, st.value
 
 
 def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):

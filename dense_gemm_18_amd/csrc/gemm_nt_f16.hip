@@ -61,6 +61,18 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk,
     return GEMM_OK;
 }
 
+int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, int64_t N,
+                       int64_t K, int *bm, int *bn, int *lbytes, int *store)
+{
+    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !lbytes || !store)
+        return GEMM_EINVAL;
+    tile_dims(choose_tile(M, N, K), *bm, *bn);
+    const int lb = load_bytes(A, B, K);
+    *lbytes = lb ? lb : 2;
+    *store = store_mode(D, N);
+    return GEMM_OK;
+}
+
 int gemm_nt_f16_tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t *tile_m,
                            int64_t *tile_n)
 {

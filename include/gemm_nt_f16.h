@@ -72,8 +72,11 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
 /*
  * The same operation on bfloat16 storage: A, B and D hold bfloat16 (1 sign,
  * 8 exponent, 7 fraction bits), products are accumulated in fp32 and the sum
- * is converted to bfloat16 with round-to-nearest-even.  Arguments, layout,
- * ownership, degenerate sizes and errors exactly as gemm_nt_f16.
+ * is converted to bfloat16 with round-to-nearest-even.  The GEMM-optimisation
+ * article at www.lqnn.cn (news/123226), section 2.2, defines the format (8
+ * exponent and 7 fraction bits, FP32's range) and the bf16 x bf16 product
+ * accumulated in FP32.  Arguments, layout, ownership, degenerate sizes and
+ * errors exactly as gemm_nt_f16.
  */
 int gemm_nt_bf16(const void *A, const void *B, void *D,
                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -140,7 +143,10 @@ int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, 
 int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn);
 
 /*
- * Fused epilogue, the standard GEMM form:
+ * Fused epilogue, the standard GEMM form (the GEMM-optimisation article at
+ * www.lqnn.cn, news/123226, section 2.1, writes GEMM as C = alpha*A*B +
+ * beta*C; its section 3.4 builds the same alpha/beta combination into the
+ * kernel's epilogue; the per-column bias is a linear layer's):
  *
  *     D[m,n] = alpha * sum_{k<K} A[m,k] * B[n,k] + beta * C[m,n] + bias[n]
  *
@@ -245,6 +251,22 @@ const char *gemm_nt_f16_strerror(int code);
  */
 int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
                      int *bm, int *bn, int *bk, int64_t *workgroups);
+
+/*
+ * Host-only introspection (no HIP call) of the kernel a gemm_nt_f16 call
+ * with these pointers and sizes takes (gemm_nt_bf16 and gemm_nt_f16_ex take
+ * the same one): the output tile *bm x *bn; *load_bytes, the width of one
+ * operand load per lane (16: K % 8 == 0 and A, B 16-byte aligned; 4: K even
+ * and A, B 4-byte aligned; 2: the register-staged kernel for odd K or
+ * 2-byte aligned operands); *store, the epilogue's store form (0: element
+ * stores; 1: 8-byte stores, D 8-byte aligned and N % 4 == 0; 2: whole tiles
+ * staged through LDS and written with 16-byte stores, D 16-byte aligned and
+ * N % 8 == 0).  The pointers are only inspected, never dereferenced.
+ * Returns GEMM_OK or GEMM_EINVAL (negative size or NULL output).
+ */
+int gemm_nt_f16_kernel(const void *A, const void *B, const void *D,
+                       int64_t M, int64_t N, int64_t K,
+                       int *bm, int *bn, int *load_bytes, int *store);
 
 /*
  * Host-only introspection (no HIP call): the output tile (tile_m, tile_n)

@@ -244,3 +244,29 @@ def test_tensor_convenience_rejects_before_any_gpu_use():
     f8 = h.to(torch.float8_e4m3fn)
     with pytest.raises(ValueError):
         binding.gemm_nt(f8, h.to(torch.float8_e5m2))          # mixed FP8 formats are fine; CPU is not
+
+
+@pytest.mark.parametrize("M,N,K,offs,want", [
+    (8192, 8192, 8192, (0, 0, 0), (256, 256, 16, 2)),
+    (3000, 5000, 2050, (0, 0, 0), (256, 256, 4, 2)),
+    (2900, 4100, 97, (0, 0, 0), (256, 256, 2, 1)),       # N % 8 == 4: 8-byte stores
+    (2900, 4100, 64, (2, 0, 0), (256, 256, 2, 1)),       # A only 2-byte aligned
+    (2900, 4100, 64, (4, 0, 0), (256, 256, 4, 1)),       # A only 4-byte aligned
+    (2900, 4096, 64, (0, 0, 8), (256, 256, 16, 1)),      # D 8-byte aligned: direct stores
+    (2900, 4096, 64, (0, 0, 2), (256, 256, 16, 0)),      # D 2-byte aligned: element stores
+    (1100, 1100, 99, (0, 0, 0), (128, 128, 2, 1)),
+    (64, 300, 37, (0, 0, 0), (64, 64, 2, 1)),
+    (64, 302, 37, (0, 0, 0), (64, 64, 2, 0)),            # N % 4 != 0: element stores
+])
+def test_kernel_introspection(M, N, K, offs, want):
+    # the tile, operand load width and store form a call would take; the
+    # addresses are only inspected
+    a, b, d = (FAKE + offs[0], FAKE + 0x4000000 + offs[1], FAKE + 0x8000000 + offs[2])
+    assert binding.gemm_nt_f16_kernel(a, b, d, M, N, K) == want
+    bm, bn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
+    assert (bm, bn) == want[:2]
+
+
+def test_kernel_introspection_rejects_negative_sizes():
+    with pytest.raises(binding.GemmError):
+        binding.gemm_nt_f16_kernel(FAKE, FAKE, FAKE, -1, 4, 4)

@@ -131,6 +131,142 @@ def host_cpu() -> dict:
             "affinity": len(os.sched_getaffinity(0))}
 
 
+class ClockSampler:
+    """Shader clock and socket power while the benchmark runs.
+
+    amd-smi runs as a child process in watch mode (one sample of every XCD's
+    GFX clock and the socket power per second), started before this process
+    touches the GPU and stopped (its process group) once the GPU work is
+    done.  A reader thread stamps each line with the time it arrived, so the
+    samples that fall inside the loaded part of the run can be picked out.
+    The power limit comes from `amd-smi static --limit`, run first by the
+    same child."""
+
+    CMD = "amd-smi static -g 0 --limit; echo __METRIC__; amd-smi metric -g 0 -c -p -w 1"
+
+    def __init__(self):
+        import subprocess
+        import threading
+        self.lines = []
+        self.error = None
+        self.proc = None
+        env = dict(os.environ, PYTHONUNBUFFERED="1")
+        try:
+            self.proc = subprocess.Popen(["bash", "-c", self.CMD], stdout=subprocess.PIPE,
+                                         stderr=subprocess.STDOUT, text=True, env=env,
+                                         start_new_session=True)
+        except OSError as e:
+            self.error = f"amd-smi not started: {e}"
+            return
+        self.reader = threading.Thread(target=self._read, daemon=True)
+        self.reader.start()
+
+    def _read(self):
+        for line in self.proc.stdout:
+            self.lines.append((time.monotonic(), line.rstrip("\n")))
+
+    def stop(self):
+        import signal
+        if self.proc is None or self.proc.returncode is not None:
+            return
+        try:
+            os.killpg(self.proc.pid, signal.SIGTERM)
+        except OSError:
+            pass
+        try:
+            self.proc.wait(timeout=10)
+        except Exception:
+            os.killpg(self.proc.pid, signal.SIGKILL)
+            self.proc.wait(timeout=10)
+        self.reader.join(timeout=5)
+
+    def parse(self):
+        """[{"t", "gfx": [MHz per XCD], "power": W}] per watch sample, and
+        the power limits (name -> W) from the static query."""
+        samples, limits = [], {}
+        cur, section, ppt, in_metric = None, "", "", False
+        for t, line in self.lines:
+            s = line.strip()
+            if s == "__METRIC__":
+                in_metric = True
+                continue
+            if not in_metric:
+                m = re.match(r"^(PPT\d+):", s)
+                if m:
+                    ppt = m.group(1)
+                m = re.match(r"^(\w*POWER\w*):\s*([0-9.]+)\s*W\b", s)
+                if m:
+                    limits[f"{ppt}.{m.group(1)}" if ppt else m.group(1)] = float(m.group(2))
+                continue
+            if re.match(r"^GPU:\s*\d+", s):
+                if cur is not None:
+                    samples.append(cur)
+                cur = {"t": t, "gfx": [], "power": None}
+                continue
+            if cur is None:
+                continue
+            m = re.match(r"^(GFX_\d+):\s*(.*)$", s)
+            if m:
+                section = m.group(1)
+                m2 = re.match(r"CLK:\s*([0-9.]+)\s*MHz", m.group(2))
+                if m2:
+                    cur["gfx"].append(float(m2.group(1)))
+                    section = ""
+                continue
+            if re.match(r"^[A-Z0-9_]+:\s*$", s):
+                section = ""
+                continue
+            m = re.match(r"^CLK:\s*([0-9.]+)\s*MHz", s)
+            if m and section.startswith("GFX_"):
+                cur["gfx"].append(float(m.group(1)))
+                cur["t"] = t
+                section = ""
+                continue
+            m = re.match(r"^SOCKET_POWER:\s*([0-9.]+)\s*W", s)
+            if m:
+                cur["power"] = float(m.group(1))
+        if cur is not None:
+            samples.append(cur)
+        return [x for x in samples if x["gfx"] or x["power"] is not None], limits
+
+    def report(self, t0: float, t1: float, peak: float, value: float) -> dict:
+        """Clock and power over the samples read between t0 and t1 (the
+        loaded part of the run), and the value as a fraction of the peak at
+        the mean clock held there."""
+        rocm = ""
+        try:
+            rocm = Path("/opt/rocm/.info/version").read_text().strip()
+        except OSError:
+            pass
+        out = {"source": "amd-smi metric -g 0 -c -p -w 1, a child process started before the "
+                         "GPU was first used", "rocm": rocm}
+        if self.error:
+            out["error"] = self.error
+            return out
+        samples, limits = self.parse()
+        out["power_limits_w"] = limits
+        inside = [x for x in samples if t0 <= x["t"] <= t1 and x["gfx"]]
+        out["samples_total"] = len(samples)
+        out["samples_under_load"] = len(inside)
+        if not inside:
+            out["error"] = "no amd-smi sample fell inside the loaded part of the run"
+            out["raw_tail"] = [ln for _, ln in self.lines[-6:]]
+            return out
+        clks = [c for x in inside for c in x["gfx"]]
+        pw = [x["power"] for x in inside if x["power"] is not None]
+        mean = sum(clks) / len(clks)
+        out.update({
+            "gfx_mhz_mean": round(mean, 1), "gfx_mhz_min": min(clks), "gfx_mhz_max": max(clks),
+            "gfx_mhz_per_xcd_last": inside[-1]["gfx"],
+            "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None,
+            "socket_power_w_max": max(pw) if pw else None,
+            "spec_mhz": 2400,
+            "peak_at_held_clock": round(peak * mean / 2400.0, 1),
+            "frac_of_peak_at_held_clock": round(value / (peak * mean / 2400.0), 4),
+        })
+        return out
+
+
 def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3) -> int:
     """A plain copy of known size: each launch reads and writes `nbytes`."""
     dev = torch.device("cuda:0")
@@ -298,6 +434,13 @@ def main() -> int:
     ap.add_argument("--path", default="f16", choices=sorted(PATH_SOURCES),
                     help="entry point to time (default: gemm_nt_f16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm", type=float, default=3.0,
+                    help="seconds of back-to-back launches before the warm-up steps, so that "
+                         "the clock reaches the level it holds under this load (the first "
+                         "~0.1 s run slower); not part of the timed region")
+    ap.add_argument("--clock", action=argparse.BooleanOptionalAction, default=True,
+                    help="sample the shader clock and socket power with amd-smi (a child "
+                         "process started before the GPU is touched); off under profilers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -314,6 +457,16 @@ def main() -> int:
               "single-GPU and has no multi-GPU mode.", file=sys.stderr)
         return 2
 
+    # The sampler starts before torch touches the GPU, and is always stopped.
+    sampler = ClockSampler() if args.clock and not args.copy_calibration else None
+    try:
+        return run(args, sampler)
+    finally:
+        if sampler is not None:
+            sampler.stop()
+
+
+def run(args, sampler) -> int:
     import torch
 
     if args.copy_calibration:
@@ -334,6 +487,14 @@ def main() -> int:
     step = P["step"]
     stream = torch.cuda.current_stream(dev)        # the stream every launch goes to
 
+    t_load = time.monotonic()
+    prewarm_calls = 0
+    if args.prewarm > 0 and args.sustain <= 0:
+        while time.monotonic() - t_load < args.prewarm:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize(dev)
+            prewarm_calls += 20
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
@@ -378,6 +539,7 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     median_ms = kernel_ms[len(kernel_ms) // 2]
+    t_unload = time.monotonic()
 
     value = tflops(M, N, K, wall / args.steps)
     achieved = tflops(M, N, K, avg_kernel_s)
@@ -433,6 +595,7 @@ def main() -> int:
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
         "kernel_source_sha256_16": kernel_source_hash(path),
+        "prewarm": {"seconds": args.prewarm, "launches": prewarm_calls},
     }
     if args.torch_context and path == "f16":
         dA, dB = P["tensors"]
@@ -447,6 +610,11 @@ def main() -> int:
         torch.cuda.synchronize(dev)
         out["context_torch_linear_tflops"] = round(
             tflops(M, N, K, ts[0].elapsed_time(ts[1]) / args.steps / 1e3), 2)
+    if sampler is not None:
+        sampler.stop()
+        # samples from 1 s into the load (the clock settles) to the end of the
+        # GPU work; amd-smi reports each sample averaged over its interval
+        out["clock"] = sampler.report(t_load + 1.0, t_unload + 1.0, peak, value)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(P["cpu_rows"], M, N, K)
     print(json.dumps(out), flush=True)

@@ -769,13 +769,26 @@ struct DmaCfg {
 // runs the tile's first step: every other contributor starts its range inside
 // that tile, writes its fp32 partial sums to its own slot and raises its flag;
 // the owner adds the slots in ascending workgroup order (so results do not
-// depend on timing), rounds once to fp16, and lowers the flags again.
+// depend on timing) and rounds once to fp16.
+//
+// Flags carry the call's epoch instead of a fixed value, so a flag left by an
+// earlier call never reads as raised: every workgroup reads the epoch word
+// e at its start and the call uses e + 1 (0 skipped); the last workgroup to
+// finish (a done counter) stores e + 1 back and zeroes the counter, ready for
+// the next call on the stream.  A zero-filled workspace is a valid start.
 struct SkPlan {
     int dp_tiles, sk_tiles;
     int base, extra;
-    uint32_t *flags;      // P words; zero before the call, zero after it
+    uint32_t *hdr;        // kSkHdrWords words: epoch, done counter, error word
+    uint32_t *flags;      // P words
     float *partials;      // P slots of BM * BN floats
 };
+// Workspace header: word 0 the last completed call's epoch, word 1 the count
+// of workgroups done in the running call (0 between calls), word 2 nonzero
+// once an owner gave up waiting for a contributor (sticky; the caller clears
+// it).  The header is 256 bytes, followed by the flags and the slots.
+constexpr int kSkHdrWords = 64;
+constexpr int kSkErrWord = 2;
 
 // One work item of workgroup w: K-steps [s0, s1) of `tile`.  s0 > 0: w is a
 // contributor to that tile.  Otherwise w writes the tile, adding the partial
@@ -1271,6 +1284,12 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // inside the K-loop.
     const int w = blockIdx.x;
     SkCursor cur = sk_begin(sk, w);
+    uint32_t epoch = 0;
+    if constexpr (SK) {
+        const uint32_t e0 = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(sk.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        epoch = e0 + 1u ? e0 + 1u : 1u;
+    }
     for (;;) {
         SkItem it{};
         if constexpr (SK) {
@@ -1327,12 +1346,17 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         asm volatile("" : "+v"(ln));
         const int slot_voff = (wave * NM * P4 * 64 + ln) * 16;
         if (s0 > 0) {
-            // Contributor: publish the partial sums, then the flag.
+            // Contributor: publish the partial sums, then the flag.  The
+            // stores are device-coherent (sc1) and complete (vmcnt 0) in
+            // every wave before the barrier; the compiler barriers keep the
+            // flag store after them in program order.
             slot_store(slot_rsrc(w), slot_voff);
             wait_vmcnt<0>();
             __syncthreads();
+            asm volatile("" ::: "memory");
             if (tid == 0)
-                __hip_atomic_store(sk.flags + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sk.flags + w, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::: "memory");
             continue;
         }
         // Owner of a split tile (or a whole tile: an empty range): wait for
@@ -1344,7 +1368,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 int got = 0;
                 for (int poll = 0; poll < kSpinLimit; ++poll) {
                     if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                            sk.flags + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                            sk.flags + w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == epoch) {
                         got = 1;
                         break;
                     }
@@ -1353,12 +1377,27 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 ok = got != 0;
             }
         }
+        // The slot loads below must not move above the polls: the flag's
+        // value is needed (s_waitcnt) before the loop exits, and this
+        // compiler barrier keeps the loads after it in program order.
+        asm volatile("" ::: "memory");
         if (ok)
             add_partials(w_first, w_last, slot_voff);
+        else if (tid == 0)
+            __hip_atomic_store(sk.hdr + kSkErrWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         store_ok(ok);
-        if (w_first <= w_last && tid == 0)
-            for (int w2 = w_first; w2 <= w_last; ++w2)
-                __hip_atomic_store(sk.flags + w2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if constexpr (SK) {
+        // The last workgroup to finish publishes the epoch for the next call.
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t done = __hip_atomic_fetch_add(sk.hdr + 1, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (done + 1u == gridDim.x) {
+                __hip_atomic_store(sk.hdr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sk.hdr, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
@@ -1595,10 +1634,30 @@ inline Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
 }
 
 inline int64_t flag_bytes(int P) { return cdiv((int64_t)P * 4, 256) * 256; }
+constexpr int64_t kSkHdrBytes = kSkHdrWords * 4;
 
 inline int64_t workspace_bytes(const Plan &pl)
 {
-    return pl.sk ? flag_bytes(pl.grid) + (int64_t)pl.grid * 128 * 128 * 4 : 0;
+    return pl.sk ? kSkHdrBytes + flag_bytes(pl.grid) + (int64_t)pl.grid * 128 * 128 * 4 : 0;
+}
+
+// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
+inline void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
+                      const SkPlan &sk, int grid)
+{
+    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
+    if (load_bytes(A, B, K) == 16)
+        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+    else
+        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+}
+
+// Header, flags and slots of a stream-K plan inside workspace `ws`.
+inline void bind_workspace(SkPlan &sp, void *ws, int grid)
+{
+    sp.hdr = (uint32_t *)ws;
+    sp.flags = (uint32_t *)((char *)ws + kSkHdrBytes);
+    sp.partials = (float *)((char *)ws + kSkHdrBytes + flag_bytes(grid));
 }
 
 // Workgroups the stream-K grid may use on the current device: one per CU,

@@ -3,20 +3,6 @@
 // Kernels, tile choice and launch helpers are in gemm_kernels.h.
 #include "gemm_kernels.h"
 
-namespace {
-// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
-void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-               const SkPlan &sk, int grid)
-{
-    const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-    else
-        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-}
-
-} // namespace
-
 extern "C" {
 int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
                 hipStream_t stream)
@@ -115,8 +101,7 @@ int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, 
     if (!pl.sk || need > ws_bytes)
         return gemm_nt_f16(A, B, D, M, N, K, stream);
     SkPlan sp = pl.split;
-    sp.flags = (uint32_t *)workspace;
-    sp.partials = (float *)((char *)workspace + flag_bytes(pl.grid));
+    bind_workspace(sp, workspace, pl.grid);
     launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }

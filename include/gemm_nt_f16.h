@@ -187,19 +187,23 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
  *
  * workspace: device memory of at least gemm_nt_f16_ws_size(M, N, K) bytes,
  *   256-byte aligned, not overlapping A, B or D, owned by the caller.  It
- *   must be zero-filled before its first use; every call that completes
- *   leaves it ready for the next one (its flag words zero again), so it is
- *   reused without clearing, for any shape.  Calls that share a workspace
- *   must not run concurrently (order them on one stream).
+ *   must be zero-filled before its first use; every call leaves it ready for
+ *   the next one, so it is reused without clearing, for any shape.  Its first
+ *   256 bytes are a header: the 32-bit word at byte offset 0 counts calls
+ *   (each call's flags carry that call's number, so a flag left by an earlier
+ *   call never counts as raised), the word at offset 4 is zero between
+ *   calls, and the word at offset 8 becomes nonzero when a wait timed out
+ *   (below); it stays set until the caller zeroes it.  Calls that share a
+ *   workspace must not run concurrently (order them on one stream).
  * ws_bytes: its size in bytes.  When the shape does not benefit from
  *   stream-K, or ws_bytes is too small for the plan, the call runs exactly
  *   as gemm_nt_f16 (workspace unused; it may then be NULL with ws_bytes 0).
  *
  * All workgroups of the grid must be resident at once: the call expects the
  * GPU's CUs not to be held by other long-running work.  A workgroup that
- * waits more than ~5 s for another writes its tile as NaN (0x7E00) and
- * ends, so the kernel always terminates; the workspace must then be zeroed
- * again.
+ * waits more than ~5 s for another writes its tile as NaN (0x7E00), sets the
+ * header's error word and ends, so the kernel always terminates; the
+ * workspace stays valid for later calls.
  *
  * Returns GEMM_OK, GEMM_EINVAL (as gemm_nt_f16, or ws_bytes < 0, a NULL or
  * misaligned workspace with ws_bytes > 0, or a workspace overlapping A, B or

@@ -94,7 +94,8 @@ def test_plan_choice(M, N, K, bm, sk):
     assert (got[0], got[3]) == (bm, sk)
     need = binding.gemm_nt_f16_ws_size(M, N, K)
     if sk:
-        assert need == 1024 + 256 * 128 * 128 * 4  # 256 flag words, 256 fp32 128x128 slots
+        # a 256-byte header, 256 flag words, 256 fp32 128x128 slots
+        assert need == 256 + 1024 + 256 * 128 * 128 * 4
     else:
         assert need == 0 and binding.gemm_nt_f16_ws_items(M, N, K, 0) == []
 

@@ -15,6 +15,7 @@ _lib = None
 GEMM_OK = 0
 GEMM_EINVAL = 1
 GEMM_ELAUNCH = 2
+GEMM_ESCRATCH = 3
 GEMM_MAX_K = 4194303
 GEMM_FP8_E4M3 = 0
 GEMM_FP8_E5M2 = 1
@@ -23,7 +24,7 @@ GEMM_FP8_E5M2 = 1
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
            "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
            "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_cs", "gemm_nt_fp8_tile",
-           "gemm_nt_f16_kernel")
+           "gemm_nt_f16_kernel", "gemm_nt_f16_ws_noalloc")
 
 
 class GemmError(RuntimeError):
@@ -72,6 +73,8 @@ def lib():
     L.gemm_nt_f16_ex.restype = ctypes.c_int
     L.gemm_nt_f16_ws.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp]
     L.gemm_nt_f16_ws.restype = ctypes.c_int
+    L.gemm_nt_f16_ws_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_nt_f16_ws_noalloc.restype = ctypes.c_int
     L.gemm_nt_f16_ws_size.argtypes = [i64, i64, i64]
     L.gemm_nt_f16_ws_size.restype = i64
     L.gemm_nt_f16_ws_tile.argtypes = [i64, i64, i64, ip, ip, lp, lp]
@@ -149,6 +152,13 @@ def gemm_nt_f16_ws(A: int, B: int, D: int, M: int, N: int, K: int, workspace: in
     """Raw call of the stream-K form; returns the C return code."""
     return lib().gemm_nt_f16_ws(A or None, B or None, D or None, M, N, K, workspace or None,
                                 ws_bytes, stream or None)
+
+
+def gemm_nt_f16_ws_noalloc(A: int, B: int, D: int, M: int, N: int, K: int,
+                           stream: int = 0) -> int:
+    """Raw call of the stream-K form on the library's static scratch (no
+    allocation); returns the C return code."""
+    return lib().gemm_nt_f16_ws_noalloc(A or None, B or None, D or None, M, N, K, stream or None)
 
 
 def gemm_nt_f16_ws_size(M: int, N: int, K: int) -> int:

@@ -33,6 +33,7 @@ const char *gemm_nt_f16_strerror(int code)
     case GEMM_OK: return "success";
     case GEMM_EINVAL: return "invalid argument (size out of range, NULL, misaligned or overlapping pointer)";
     case GEMM_ELAUNCH: return "kernel launch failed";
+    case GEMM_ESCRATCH: return "the call needs more scratch memory than the library's static buffer holds";
     default: return "unknown error code";
     }
 }

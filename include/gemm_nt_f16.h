@@ -47,6 +47,7 @@ typedef struct ihipStream_t *hipStream_t;
 #define GEMM_OK 0       /* work enqueued (or nothing to do)                    */
 #define GEMM_EINVAL 1   /* argument rejected; nothing enqueued                 */
 #define GEMM_ELAUNCH 2  /* the HIP runtime reported an error at kernel launch  */
+#define GEMM_ESCRATCH 3 /* the call needs more than the library's static scratch */
 
 /* Largest K accepted: a 256-row operand panel must span fewer than 2^31
  * bytes, the range one buffer resource addresses. */
@@ -212,6 +213,30 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
 int gemm_nt_f16_ws(const void *A, const void *B, void *D,
                    int64_t M, int64_t N, int64_t K,
                    void *workspace, int64_t ws_bytes, hipStream_t stream);
+
+/*
+ * gemm_nt_f16_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what gemm_nt_f16_ws
+ * computes, with the same plan, kernels and results, and calls no allocating
+ * routine: the workspace is a static device array of the library (16 MiB +
+ * 1.25 KiB per GPU, loaded with the library's code and held until the
+ * process ends), looked up once per device on the first call, which also
+ * enqueues a small kernel that zeroes its header and flags.
+ *
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or different threads, without ordering) race and give
+ * wrong results; order them on one stream.  A wait that times out behaves as
+ * in gemm_nt_f16_ws (NaN tile; the error word is in the static array, not
+ * readable by the caller).
+ *
+ * Arguments as gemm_nt_f16.  Returns GEMM_OK, GEMM_EINVAL (as gemm_nt_f16),
+ * GEMM_ESCRATCH (the plan needs more workspace than the static array holds;
+ * not reached on GPUs of up to 256 CUs) or GEMM_ELAUNCH (also when the
+ * array's device address cannot be obtained).
+ */
+int gemm_nt_f16_ws_noalloc(const void *A, const void *B, void *D,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
  * Host-only (no HIP call): bytes of workspace gemm_nt_f16_ws needs for this

@@ -107,7 +107,7 @@ int fp8_load_bytes(const void *A, const void *B, int64_t K)
 Tile fp8_tile(int64_t M, int64_t N, int64_t K, int lb)
 {
     if (lb == 16)
-        return choose_tile(M, N, K / 2);
+        return choose_tile(M, N, K / 2, false);
     return (M <= 64 || N <= 64) ? Tile::kThin : Tile::kMid;
 }
 

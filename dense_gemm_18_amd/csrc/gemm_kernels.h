@@ -1455,22 +1455,33 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Tile choice: the one with the smaller (waves of workgroups) x (time of one
 // tile), one workgroup per CU on MI355X's 256 CUs.  Tile times relative to a
 // 128 x 128 x K tile at the big tile's rate, measured on MI355X: a 256 x 256
-// tile costs 4.0 and a 128 x 128 tile 1.4 with 16-byte loads (the big tile's
-// pipeline is ~40 % faster per FLOP); with 4-byte loads (K % 8 != 0) 6.6 and
-// 2.25.  So 3000 x 5000 runs one wave of 240 big tiles rather than four of
-// 960 mid tiles, and 2048 x 2048 runs 256 mid tiles rather than 64 big ones.
-// The choice assumes operands aligned to 16 bytes.
+// tile costs 4.0, a 128 x 128 tile 1.4 and a 64 x 64 tile 0.85 with 16-byte
+// loads (the big tile's pipeline is ~40 % faster per FLOP; the 64 x 64 tile
+// moves more bytes per FLOP but fills four times as many CUs); with 4-byte
+// loads (K % 8 != 0) 6.6, 2.25 and 1.3.  So 3000 x 5000 runs one wave of 240
+// big tiles rather than four of 960 mid tiles, 2048 x 2048 runs 256 mid tiles
+// rather than 64 big ones, and 1024 x 1024 runs 256 thin tiles rather than
+// 64 mid ones (5.5 against 8.1 us at K = 1024).  The choice assumes operands
+// aligned to 16 bytes.
 constexpr int kCUs = 256;
 
-inline Tile choose_tile(int64_t M, int64_t N, int64_t K)
+// thin_ok = false (FP8, whose 64 x 64 tile cost is not measured): the thin
+// tile only when M or N is at most 64.
+inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
 {
     if (M <= 64 || N <= 64)
         return Tile::kThin;
     const bool wide = K % 8 == 0;
     const double big_tile = wide ? 4.0 : 6.6, mid_tile = wide ? 1.4 : 2.25;
-    const int64_t big_waves = cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs);
-    const int64_t mid_waves = cdiv(cdiv(M, 128) * cdiv(N, 128), kCUs);
-    return big_waves * big_tile <= mid_waves * mid_tile ? Tile::kBig : Tile::kMid;
+    const double thin_tile = wide ? 0.85 : 1.3;
+    const double big = cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs) * big_tile;
+    const double mid = cdiv(cdiv(M, 128) * cdiv(N, 128), kCUs) * mid_tile;
+    const double thin = cdiv(cdiv(M, 64) * cdiv(N, 64), kCUs) * thin_tile;
+    if (!thin_ok)
+        return big <= mid ? Tile::kBig : Tile::kMid;
+    if (big <= mid && big <= thin)
+        return Tile::kBig;
+    return mid <= thin ? Tile::kMid : Tile::kThin;
 }
 
 inline void tile_dims(Tile t, int &bm, int &bn)
@@ -1584,15 +1595,17 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
 }
 
 // ---------------------------------------------------------------------------
-// Stream-K planning.  Measured on MI355X (TFLOPS, stream-K / one workgroup
-// per tile): 512x640x16384 312/135, 1024^2x16384 858/424, 768x1024x8192
-// 509/299, 900x1000x4098 234/142, 1024^2x4096 417/362; but 1024^2x2048
-// 238/312, 1280^2x8192 444/624, 1536^2x8192 684/792.  Stream-K runs on the
-// 128 x 128 tile when its tiles fill at most a quarter of the CUs and K
-// spans at least 64 K-steps: the partial-sum hand-off (one fp32 tile per
-// contributor through memory) then costs less than the idle CUs.  The
-// 256 x 256 tile is not used for it: its hand-off moves 256 KB per
-// contributor and its pipeline leaves no registers for the persistent loop.
+// Stream-K planning.  Measured on MI355X (TFLOPS, stream-K / 128 x 128 tiles
+// / 64 x 64 tiles, one workgroup per tile): 1024^2x16384 833/433/740,
+// 512x640x16384 307/136/273, 1024^2x8192 613/407/676, 768x1024x8192
+// 494/314/559, 1024^2x4100 322/220/379; and earlier 1280^2x8192 444/624,
+// 1536^2x8192 684/792 (stream-K / 128 x 128).  Stream-K runs on the 128 x 128
+// tile when those tiles fill at most a quarter of the CUs and K spans at
+// least 192 K-steps: the partial-sum hand-off (one fp32 tile per contributor
+// through memory) then costs less than the 64 x 64 tiles' extra loads, which
+// win below that.  The 256 x 256 tile is not used for it: its hand-off moves
+// 256 KB per contributor and its pipeline leaves no registers for the
+// persistent loop.
 struct Plan {
     Tile tile = Tile::kThin;
     bool sk = false;
@@ -1615,16 +1628,18 @@ inline SkPlan sk_split(int64_t tiles, int64_t steps, int P)
     return sp;
 }
 
+constexpr int64_t kSkMinSteps = 192;
+
 // lb: 16 or 4 (0: the register-staged path, no stream-K).
 inline Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
 {
     Plan pl;
     pl.tile = choose_tile(M, N, K);
-    if (lb == 0 || pl.tile == Tile::kThin || K == 0)
+    if (lb == 0 || M <= 64 || N <= 64 || K == 0)
         return pl;
     const int64_t steps = cdiv(K, 64);
     const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
-    if (4 * tiles <= P && steps >= 64) {
+    if (4 * tiles <= P && steps >= kSkMinSteps) {
         pl.tile = Tile::kMid;
         pl.sk = true;
         pl.grid = P;

@@ -180,7 +180,7 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
  * calls are bitwise identical.
  *
  * When the problem's 128 x 128 output tiles fill at most a quarter of the
- * GPU's CUs and K spans at least 64 steps of 64 (K > 4032), a persistent
+ * GPU's CUs and K spans at least 192 steps of 64 (K > 12224), a persistent
  * grid of one workgroup per CU (at most 256) splits the K-steps of the
  * tiles evenly over all workgroups; a tile split over several workgroups
  * is summed in fp32 through `workspace` and rounded to fp16 once.  Other

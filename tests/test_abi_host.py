@@ -96,7 +96,11 @@ def test_tile_introspection():
     (2048, 2048, 8192, 128),    # 64 big tiles would leave 3/4 of the CUs idle
     (2560, 2560, 4096, 128),    # 100 big tiles vs 400 mid tiles (2 waves)
     (2048, 2048, 8194, 128),
-    (1024, 1024, 1024, 128),
+    (1024, 1024, 1024, 64),     # 256 thin tiles (1 wave) beat 64 mid tiles
+    (2048, 1024, 1024, 128),    # 128 mid tiles (1 wave) beat 512 thin tiles (2 waves)
+    (1100, 1100, 1024, 128),    # 81 mid tiles vs 324 thin tiles (2 waves)
+    (1024, 1024, 1026, 64),     # 4-byte loads
+    (2048, 1024, 1026, 128),
     (64, 16384, 8192, 64),      # M <= 64: the thin tile
     (16384, 33, 128, 64),
 ])

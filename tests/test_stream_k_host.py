@@ -17,14 +17,14 @@ from dense_gemm_18_amd import binding
 FAKE = 0x10000000
 
 SK_SHAPES = [
-    (1024, 1024, 8192),      # 64 tiles, 4 pieces each: 3 contributors
-    (768, 768, 8192),        # 36 tiles, pieces cross tile boundaries
+    (1024, 1024, 12288),     # 64 tiles, 4 pieces each: 3 contributors
+    (768, 768, 12288),       # 36 tiles, pieces cross tile boundaries
     (512, 640, 16384),       # 20 tiles of 256 steps: up to 13 workgroups per tile
-    (900, 1000, 4098),       # ragged M, N; 4-byte loads and a K tail
-    (1024, 1024, 4096),
+    (900, 1000, 12290),      # ragged M, N; 4-byte loads and a K tail
+    (1024, 1024, 16384),
     (100, 8192, 32768),      # one tile row
-    (65, 300, 4096),         # one tile row of 3 tiles, ragged
-    (64 * 128, 65, 8192),    # a tall single column of tiles
+    (65, 300, 12288),        # one tile row of 3 tiles, ragged
+    (64 * 128, 65, 12288),   # a tall single column of tiles
 ]
 
 
@@ -80,14 +80,14 @@ def test_schedule_covers_each_step_once(M, N, K):
 @pytest.mark.parametrize("M,N,K,bm,sk", [
     (8192, 8192, 8192, 256, 0),      # whole waves: plain launch
     (3072, 3072, 3072, 256, 0),      # 576 128x128 tiles: more than a quarter of the CUs
-    (1280, 1280, 8192, 128, 0),      # 100 tiles
-    (1024, 1024, 2048, 128, 0),      # only 32 K-steps
-    (1024, 1024, 4032, 128, 0),      # 63 K-steps
-    (1024, 1024, 4096, 128, 64),
-    (1024, 1024, 8192, 128, 64),
-    (900, 1000, 4098, 128, 64),      # 4-byte loads
+    (1280, 1280, 16384, 128, 0),     # 100 tiles
+    (1024, 1024, 4096, 64, 0),       # only 64 K-steps: the 64x64 tiles
+    (1024, 1024, 12224, 64, 0),      # 191 K-steps
+    (1024, 1024, 12288, 128, 64),
+    (1024, 1024, 16384, 128, 64),
+    (900, 1000, 12290, 128, 64),     # 4-byte loads
     (64, 16384, 8192, 64, 0),        # thin tiles never split
-    (1024, 1024, 8191, 128, 0),      # odd K: register-staged path, no stream-K
+    (1024, 1024, 16383, 64, 0),      # odd K: register-staged path, no stream-K
 ])
 def test_plan_choice(M, N, K, bm, sk):
     got = binding.gemm_nt_f16_ws_tile(M, N, K)
@@ -122,6 +122,6 @@ def test_ws_validation_rejects_before_any_hip_call(ws, ws_bytes):
 
 def test_ws_items_rejects_bad_arguments():
     with pytest.raises(binding.GemmError):
-        binding.gemm_nt_f16_ws_items(1024, 1024, 8192, 256)      # outside the 256 workgroups
+        binding.gemm_nt_f16_ws_items(1024, 1024, 12288, 256)     # outside the 256 workgroups
     with pytest.raises(binding.GemmError):
         binding.gemm_nt_f16_ws_items(0, 1024, 8192, 0)

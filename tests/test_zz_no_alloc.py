@@ -39,7 +39,7 @@ def _run_noalloc(A, B):
 
 
 # Two stream-K shapes (the second smaller), then one the plain kernel serves.
-SHAPES = [(1024, 1024, 16384), (512, 640, 8192)]
+SHAPES = [(1024, 1024, 16384), (512, 640, 12288)]
 
 
 def test_noalloc_matches_workspace_form_two_calls():

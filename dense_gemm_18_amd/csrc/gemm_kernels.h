@@ -21,14 +21,16 @@
 //     blocks; page 1 ("内核 4：生产级调优") notes that a larger M tile
 //     improves L2 reuse of B.
 //   * Global -> LDS staging: A and B are both K-contiguous, so one loader
-//     serves both.  Each lane moves 16-byte chunks (8 fp16 along K), or
-//     4-byte pieces of them when K is not a multiple of 8, with buffer loads
-//     that write LDS directly; 8 lanes cover one 128-byte row of a K-step, so
-//     the accesses are fully coalesced (page 1, "内核 1：共享内存分块", shows
-//     the cooperative coalesced tile copy).  The buffer resource of each
-//     workgroup spans only its valid rows, so rows past M or N read as zero
-//     in hardware; with a K tail the K-steps are aligned to K's end, so only
-//     the first step's loads carry a K mask.
+//     serves both.  Each lane moves 16-byte chunks (8 fp16 along K); 8 lanes
+//     cover one 128-byte row of a K-step, so the accesses are fully
+//     coalesced (page 1, "内核 1：共享内存分块", shows the cooperative
+//     coalesced tile copy).  With K % 8 == 0 and 16-byte aligned operands
+//     the chunks go straight to LDS (buffer loads that write LDS); otherwise
+//     they are loaded into registers at whatever alignment the rows have and
+//     written to the same LDS bytes.  The buffer resource of each workgroup
+//     spans only its valid rows, so rows past M or N read as zero in
+//     hardware; with a K tail the K-steps are aligned to K's end, so only the
+//     first step's loads carry a K mask.
 //   * LDS layout: rows of 64 fp16 (128 B = eight 16-byte chunks), chunk index
 //     XOR-swizzled by the row so that the MFMA fragment reader is free of
 //     bank conflicts (page 1, "为什么 swizzle 重要", explains the conflict
@@ -155,52 +157,6 @@ __host__ __device__ inline void tile_coord(int64_t wg, int64_t tiles_m, int64_t 
 // consecutive lanes touches every bank once, whether the LDS serves 128 or
 // 256 bytes per clock.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// ---------------------------------------------------------------------------
-// Tile configuration.
-template <int BM_, int BN_, int WM_, int WN_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int THREADS = WM * WN * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;      // wave tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32;      // MFMA blocks per wave
-    static constexpr int CA = BM * 8 / THREADS;             // A chunks per thread per K-step
-    static constexpr int CB = BN * 8 / THREADS;
-    static constexpr int STAGE = (BM + BN) * kBK;           // fp16 elements per LDS stage
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
-    static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "chunks must split evenly");
-    static_assert(THREADS % 8 == 0, "8 lanes per LDS row");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
-};
-
-// Load one chunk (8 fp16 along K) of a row panel.  `off` is the byte offset
-// of the chunk's first element, `k` its K index.  LOADB is the width of one
-// load: 16 (K % 8 == 0, 16-byte aligned panel), 4 (K even, 4-byte aligned)
-// or 2 (anything).  Elements with k >= K read as zero; rows past the panel's
-// valid rows lie past the buffer range and read as zero in hardware.
-template <int LOADB>
-__device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off, int k, int K)
-{
-    u32x4 v;
-    if constexpr (LOADB == 16) {
-        v = __builtin_amdgcn_raw_buffer_load_b128(rs, k < K ? off : kOob, 0, 0);
-    } else if constexpr (LOADB == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            v[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, k + 2 * j < K ? off + 4 * j : kOob, 0, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, k + 2 * j < K ? off + 4 * j : kOob, 0, 0);
-            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, k + 2 * j + 1 < K ? off + 4 * j + 2 : kOob, 0, 0);
-            v[j] = lo | (hi << 16);
-        }
-    }
-    return v;
-}
 
 // Fused epilogue of gemm_nt_f16_ex: the four consecutive columns n .. n+3
 // of row m become alpha * v + beta * C[m][n..] + bias[n..], formed in fp32
@@ -514,121 +470,6 @@ __device__ __forceinline__ void store_acc16(const f32x4 (&acc)[TM][TN], T *__res
                            vec_store);
 }
 
-template <class C, int LOADB, bool EPI, bool BF>
-__global__ void __launch_bounds__(C::THREADS, 1)
-gemm_nt_reg_kernel(const typename Elem<BF>::T *__restrict__ A,
-                   const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
-                   int M, int N, int K, int tiles_m, int tiles_n, int vec_store, EpiArg<EPI> epi)
-{
-    using X8 = typename Elem<BF>::x8;
-    __shared__ __attribute__((aligned(16))) _Float16 smem[2 * C::STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave % C::WM, wn = wave / C::WM;
-
-    int64_t tm64, tn64;
-    tile_coord(blockIdx.x, tiles_m, tiles_n, tm64, tn64);
-    const int m0 = (int)tm64 * C::BM, n0 = (int)tn64 * C::BN;
-    const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
-
-    // Buffer resources spanning only this tile's valid rows.
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + (int64_t)m0 * K), (short)0, rows_a * K * 2, kRsrcFlags);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(B + (int64_t)n0 * K), (short)0, rows_b * K * 2, kRsrcFlags);
-
-    // Loader mapping: thread t moves chunk (t & 7) of rows (t >> 3) + i * THREADS/8.
-    const int lrow = tid >> 3, lch = tid & 7;
-    constexpr int ROWS_PER_PASS = C::THREADS / 8;
-    const uint32_t row_bytes = (uint32_t)K * 2;
-
-    u32x4 stA[C::CA], stB[C::CB];
-    auto load_tiles = [&](int k0) {
-        const int k = k0 + lch * 8;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i)
-            stA[i] = load_chunk<LOADB>(ra, (uint32_t)(lrow + i * ROWS_PER_PASS) * row_bytes + (uint32_t)k * 2, k, K);
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i)
-            stB[i] = load_chunk<LOADB>(rb, (uint32_t)(lrow + i * ROWS_PER_PASS) * row_bytes + (uint32_t)k * 2, k, K);
-    };
-    auto store_tiles = [&](int stage) {
-        _Float16 *sa = smem + stage * C::STAGE;
-        _Float16 *sb = sa + C::BM * kBK;
-#pragma unroll
-        for (int i = 0; i < C::CA; ++i) {
-            const int row = lrow + i * ROWS_PER_PASS;
-            *(u32x4 *)(sa + row * kBK + ((lch ^ swz(row)) << 3)) = stA[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::CB; ++i) {
-            const int row = lrow + i * ROWS_PER_PASS;
-            *(u32x4 *)(sb + row * kBK + ((lch ^ swz(row)) << 3)) = stB[i];
-        }
-    };
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = f32x16{};
-
-    // MFMA fragment rows of this lane (same pattern for A and B: both are
-    // K-contiguous).  Lane l supplies row l % 32 and K chunk 2s + l / 32 of
-    // each 16-wide K slice s.
-    const int frow = lane & 31, fhi = lane >> 5;
-    const int a_row0 = wm * C::WTM + frow;
-    const int b_row0 = wn * C::WTN + frow;
-    const int fsw = swz(frow);   // rows differ from frow by multiples of 32
-
-    auto compute = [&](int stage) {
-        const _Float16 *sa = smem + stage * C::STAGE;
-        const _Float16 *sb = sa + C::BM * kBK;
-#pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            const int ch = ((2 * s + fhi) ^ fsw) << 3;
-            X8 af[C::TM], bf[C::TN];
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-                af[i] = *(const X8 *)(sa + (a_row0 + 32 * i) * kBK + ch);
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                bf[j] = *(const X8 *)(sb + (b_row0 + 32 * j) * kBK + ch);
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = mfma32<BF>(bf[j], af[i], acc[i][j]);
-        }
-    };
-
-    const int nk = (K + kBK - 1) / kBK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more)
-            load_tiles((kt + 1) * kBK);
-        compute(cur);
-        if (more)
-            store_tiles(cur ^ 1);
-        __syncthreads();
-    }
-
-    if constexpr (EPI)
-        store_blocks<C::TM, C::TN>([&](int i, int j) { return acc[i][j]; }, D, M, N,
-                                   m0 + wm * C::WTM, n0 + wn * C::WTN, lane, vec_store,
-                                   EpiFin{epi, N, vec_store});
-    else
-        store_acc<C::TM, C::TN>(acc, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
-                                vec_store);
-}
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS kernel (fast path: K % 8 == 0, A and B 16-byte aligned).
 //
@@ -714,12 +555,24 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_, bool SPLIT_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_, bool SPLIT_,
+          bool REG_ = false>
 struct DmaCfg {
     // LB: bytes one lane moves per load: 16 (buffer_load_dwordx4 ... lds,
     // needs K % 8 == 0 and 16-byte aligned operands) or 4 (buffer_load_dword
     // ... lds, needs K even and 4-byte aligned operands).
     static constexpr int LB = LB_;
+    // REG: the same 16-byte chunks, loaded into registers at any alignment
+    // (gfx950's vector memory loads take unaligned addresses) and written to
+    // LDS with ds_write_b128 at the byte the direct-to-LDS load would fill;
+    // serves any K and any 2-byte-aligned operands.  Each chunk is loaded
+    // one step ahead of its LDS write, and the register is reloaded right
+    // after the write, so every load has a full step to land wherever the
+    // write sits in the step.  The writes of a step are spread evenly over
+    // one step's worth of slices: a group in the slice after the barrier
+    // that frees their stage, the other groups in the next step's slices
+    // before its barrier.
+    static constexpr bool REG = REG_;
     // SPLIT: a step's loads are issued half in the slice after the barrier
     // and half in the next step's first slice; otherwise all of them in the
     // slice after the barrier (which gives every load the longest time to
@@ -758,6 +611,8 @@ struct DmaCfg {
     static_assert(SLICES % 2 == 0, "slice 0 of every step uses fragment set 0");
     static_assert(SPLIT || LPS * (NSTAGE - 1) < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+    static_assert(!REG || (LB == 16 && NSTAGE == 2 && BK == 64 && !SPLIT && LPS % SLICES == 0),
+                  "register staging: 16-byte chunks, two stages, writes in every slice");
 };
 
 // Stream-K work split of a persistent grid of P workgroups (one per CU, all
@@ -945,8 +800,64 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // with k < 0 then get an out-of-range offset and the others carry k0 in
     // their vector offset.  Loads inside the K-loop carry no mask, which
     // keeps the loop's registers those of the untailed kernel.
+    // REG: chunk q of the next step to be written to LDS, in registers.  A
+    // load puts row 8 (wave + NWAVES i) + lane / 8, global chunk
+    // (lane % 8) ^ swizzle into rst[q] (the chunk the direct-to-LDS load
+    // would bring), and the write stores it at that load's LDS byte.
+    u32x4 rst[C::REG ? C::LPS : 1];
+    auto reg_load = [&](int step, auto qc, auto firstc) G18_INLINE {
+        constexpr int q = decltype(qc)::value;
+        constexpr bool isa = q < C::A_LOADS;
+        constexpr int i = isa ? q : q - C::A_LOADS;
+        const int k0 = kb + step * C::BK;
+        const __amdgpu_buffer_rsrc_t rs = step < n ? (isa ? ra : rb) : rz;
+        const uint32_t off = isa ? a_off[i] : b_off[i];
+        const uint32_t soff = (uint32_t)k0 * 2u;
+        if constexpr (KTAIL && decltype(firstc)::value) {
+            if (k0 < 0) {
+                // The item's first step starts before k = 0: a chunk whose
+                // first k is negative reads element by element, k < 0 as
+                // zero (such a chunk may start in the row before, or before
+                // the buffer).  Offsets wrap modulo 2^32, as soff does.
+                const int kk = k0 + (isa ? a_k[i] : b_k[i]);
+                if (kk >= 0) {
+                    rst[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + soff, 0, 0);
+                } else {
+                    u32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t o = off + soff + 4u * j;
+                        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                            rs, kk + 2 * j >= 0 ? o : kOob, 0, 0);
+                        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                            rs, kk + 2 * j + 1 >= 0 ? o + 2u : kOob, 0, 0);
+                        v[j] = lo | (hi << 16);
+                    }
+                    rst[q] = v;
+                }
+                return;
+            }
+        }
+        rst[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, 0);
+    };
+    auto reg_write = [&](auto sc, auto qc) G18_INLINE {
+        constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
+        constexpr bool isa = q < C::A_LOADS;
+        constexpr int i = isa ? q : q - C::A_LOADS;
+        constexpr int base = S * C::STAGE_BYTES + (isa ? 0 : C::BM * C::ROW_BYTES) +
+                             (i * C::NWAVES) * C::INST_BYTES;
+        *(u32x4 *)(smem + base + wave * C::INST_BYTES + lane * 16) = rst[q];
+    };
+
     auto issue_one = [&](int step, auto sc, auto qc, auto firstc) G18_INLINE {
         constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
+        if constexpr (C::REG) {
+            // stage S takes step `step` (already in registers); the registers
+            // then load step + 1
+            reg_write(sc, qc);
+            reg_load(step + 1, qc, std::false_type{});
+            return;
+        }
         const int k0 = kb + step * C::BK;
         const bool live = step < n;
         char *stage = smem + S * C::STAGE_BYTES;
@@ -987,10 +898,20 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                                 (wn * C::WTN + frow) * C::ROW_BYTES + ch;
             }
     };
-    X8 fr[2][C::TM + C::TN];
-    auto read_one = [&](X8 (&f)[C::TM + C::TN], auto sc, auto tc, auto qc) G18_INLINE {
+    // Two fragment sets (alternating slices): A blocks fa[set][i], B blocks
+    // fb[set][j].
+    X8 fa[2][C::TM], fb[2][C::TN];
+    auto frag = [&](auto setc, auto qc) G18_INLINE -> X8 & {
+        constexpr int f = decltype(setc)::value, q = decltype(qc)::value;
+        if constexpr (q < C::TM)
+            return fa[f][q];
+        else
+            return fb[f][q - C::TM];
+    };
+    auto read_one = [&](auto setc, auto sc, auto tc, auto qc) G18_INLINE {
         constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
         constexpr int off = C::MF * (q < C::TM ? q : q - C::TM) * C::ROW_BYTES;
+        X8 &f = frag(setc, qc);
         if constexpr (F8) {
             // 32 bytes: the chunks of both 16-bit slices (t is always 0)
             static_assert(t == 0, "an FP8 fragment spans the whole K-step");
@@ -998,9 +919,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             const uint32_t p1 = q < C::TM ? a_addr[S][1] : b_addr[S][1];
             const u32x4 lo = *(const u32x4 *)(smem + p0 + off);
             const u32x4 hi = *(const u32x4 *)(smem + p1 + off);
-            f[q] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            f = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-            f[q] = *(const X8 *)(smem + (q < C::TM ? a_addr[S][t] : b_addr[S][t]) + off);
+            f = *(const X8 *)(smem + (q < C::TM ? a_addr[S][t] : b_addr[S][t]) + off);
         }
     };
 
@@ -1008,8 +929,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // MFMAs per slice: all blocks, or (FP8) half of the block rows.
     constexpr int NMS = F8 ? NM / 2 : NM;
     constexpr int LHALF = C::LPS / 2;
-    // Loads issued in one slice: half a step's or a whole step's.
-    constexpr int LSL = C::SPLIT ? LHALF : C::LPS;
+    // Loads issued in one slice: half a step's or a whole step's (register
+    // staging: a step's writes and reloads over all its slices).
+    constexpr int LSL = C::REG ? C::LPS / C::SLICES : (C::SPLIT ? LHALF : C::LPS);
     // Spacing of the loads over the NMS MFMAs of a slice: one load every
     // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
     // than MFMAs (small tiles); the same for fragment reads (RPG).
@@ -1036,19 +958,22 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // slice only; the A fragments are not double buffered (see the FP8 read
     // schedule above), which keeps the 256 x 256 tile within the registers.
     // h: (FP8) which half of the block rows this slice multiplies.
-    auto slice = [&](const X8 (&cur)[C::TM + C::TN], X8 (&nxt)[C::TM + C::TN],
+    // cur, nxt: fragment sets (integral constants) multiplied and read.
+    auto slice = [&](auto cur, auto nxt,
                      auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
                      auto l0, auto hc) G18_INLINE {
         static_for<0, NMS>([&](auto pc) G18_INLINE {
             constexpr int p = decltype(pc)::value;
             constexpr int q = p + (F8 ? decltype(hc)::value * NMS : 0);
             constexpr int i = q / C::TN, j = q % C::TN;
+            using QA = std::integral_constant<int, i>;
+            using QB = std::integral_constant<int, C::TM + j>;
             if constexpr (F8 != 0)
-                acc[i][j] = mfma_f8<F8>(cur[C::TM + j], cur[i], acc[i][j]);
+                acc[i][j] = mfma_f8<F8>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             else if constexpr (C::MF == 32)
-                acc[i][j] = mfma32<BF>(cur[C::TM + j], cur[i], acc[i][j]);
+                acc[i][j] = mfma32<BF>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             else
-                acc[i][j] = mfma16<BF>(cur[C::TM + j], cur[i], acc[i][j]);
+                acc[i][j] = mfma16<BF>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             if constexpr (decltype(do_read)::value && F8 != 0 && decltype(hc)::value == 0) {
                 static_for<0, C::TN>([&](auto jc) G18_INLINE {
                     constexpr int jb = decltype(jc)::value;
@@ -1113,27 +1038,35 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, Z_{});
-            slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, F_{}, 0, S_{}, Z_{}, H1_{});
+            slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, Z_{});
+            slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, F_{}, 0, S_{}, Z_{}, H1_{});
         } else {
         static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
             constexpr int t = decltype(tc)::value;
             constexpr int c = t & 1;    // 16-bit slices alternate fragment sets
             using TN_ = std::integral_constant<int, t + 1>;
-            if constexpr (t == 0 && C::SPLIT) {
+            if constexpr (C::REG && t + 1 < C::SLICES) {
+                // group t + 1 of step u - 1 + NSTAGE (its stage was freed at
+                // the previous step's barrier)
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{},
+                      std::integral_constant<int, (t + 1) * LSL>{}, tc);
+            } else if constexpr (t == 0 && C::SPLIT) {
                 // second half of step u - 1 + NSTAGE
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{}, tc);
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{}, H_{}, tc);
             } else if constexpr (t + 1 < C::SLICES) {
-                slice(fr[c], fr[c ^ 1], T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{}, tc);
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, S_{}, TN_{}, F_{}, 0, S_{}, Z_{}, tc);
             } else {
                 // Step u+1 has landed once only steps u+2 .. u+NSTAGE-1 may
                 // be outstanding.  The fence keeps the previous slice's MFMAs
                 // ahead of the barrier, where they run while the wave waits.
+                // (Register staging waits for each chunk's load only before
+                // writing it; the compiler places those waits.)
                 __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
+                if constexpr (!C::REG)
+                    wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
                 lds_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                slice(fr[c], fr[c ^ 1], T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, tc);
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, tc);
             }
         });
         }
@@ -1313,7 +1246,26 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // Prologue: steps 0 .. NSTAGE-2 and, with split loads, the first half of
     // step NSTAGE-1 (its second half is issued by step 0's first slice, like
     // every later step); otherwise all of step NSTAGE-1 too.
-    constexpr int PRO_LAST = C::SPLIT ? LHALF : C::LPS;
+    constexpr int PRO_LAST = C::REG ? LSL : (C::SPLIT ? LHALF : C::LPS);
+    if constexpr (C::REG) {
+        // Steps 0 .. NSTAGE-2 and the first group of step NSTAGE-1 through
+        // the registers into their stages; those registers then load step
+        // NSTAGE, the others keep step NSTAGE-1's chunks for the slices of
+        // step 0 before its barrier.
+        static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
+            constexpr int st = decltype(sc)::value;
+            static_for<0, C::LPS>([&](auto qc) G18_INLINE {
+                reg_load(st, qc, std::integral_constant<bool, st == 0>{});
+            });
+            wait_vmcnt<0>();
+            static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
+                [&](auto qc) G18_INLINE { reg_write(sc, qc); });
+        });
+        static_for<0, PRO_LAST>([&](auto qc) G18_INLINE {
+            reg_load(C::NSTAGE, qc, std::false_type{});
+        });
+        lds_barrier();
+    } else {
     static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
         constexpr int st = decltype(sc)::value;
         static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
@@ -1323,7 +1275,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     });
     wait_vmcnt<C::LPS * (C::NSTAGE - 2) + PRO_LAST>();
     lds_barrier();
-    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(fr[0], Z_{}, Z_{}, qc); });
+    }
+    static_for<0, NR>([&](auto qc) G18_INLINE { read_one(Z_{}, Z_{}, Z_{}, qc); });
 
     // With two stages the step count is rounded up to even instead of
     // guarding each step (a guard costs registers at the loop back-edge):
@@ -1429,9 +1382,6 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 
 // ---------------------------------------------------------------------------
 // Host side.
-using Big = Cfg<256, 256, 2, 2>;     // 4 waves, 128 x 128 per wave
-using Mid = Cfg<128, 128, 2, 2>;     // 4 waves, 64 x 64 per wave
-using Thin = Cfg<64, 64, 2, 2>;      // 4 waves, 32 x 32 per wave
 // 256 x 256: 4 waves of 128 x 128 on 16x16x32 MFMAs, two 64 KB stages, each
 // step's loads issued right after the barrier.  16x16x32 keeps half as many
 // accumulator registers busy per FLOP as 32x32x16, so the part draws less
@@ -1446,7 +1396,14 @@ using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
 // instructions per step, so fewer stages keep the waits encodable.
 using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 16, 4, true>;
 using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4, false>;
-using BigDma4 = DmaCfg<256, 256, 2, 2, 64, 2, 32, 4, true>;
+// Register-staged 16-byte chunks (any K, operands 2-byte aligned): two
+// stages, each chunk loaded a step ahead into 64 (32, 16) registers.  The
+// 256 x 256 tile uses 32x32x16 MFMAs: their fragments take half the
+// registers of 16x16x32 ones, which leaves room for the 64 staging
+// registers (with 16x16x32 blocks the kernel spills).
+using BigReg = DmaCfg<256, 256, 2, 2, 64, 2, 32, 16, false, true>;
+using MidReg = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false, true>;
+using ThinReg = DmaCfg<64, 64, 2, 2, 64, 2, 16, 16, false, true>;
 
 enum class Tile { kBig, kMid, kThin };
 
@@ -1487,9 +1444,9 @@ inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
 inline void tile_dims(Tile t, int &bm, int &bn)
 {
     switch (t) {
-    case Tile::kBig: bm = Big::BM; bn = Big::BN; break;
-    case Tile::kMid: bm = Mid::BM; bn = Mid::BN; break;
-    default: bm = Thin::BM; bn = Thin::BN; break;
+    case Tile::kBig: bm = BigDma::BM; bn = BigDma::BN; break;
+    case Tile::kMid: bm = MidDma::BM; bn = MidDma::BN; break;
+    default: bm = ThinDma::BM; bn = ThinDma::BN; break;
     }
 }
 
@@ -1521,17 +1478,6 @@ EpiArg<EPI> epi_arg(const Epi &e)
         return e;
     else
         return NoEpi{};
-}
-
-template <class C, int LOADB, bool EPI, bool BF>
-void launch_cfg(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
-                const Epi &epi)
-{
-    using T = typename Elem<BF>::T;
-    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    hipLaunchKernelGGL((gemm_nt_reg_kernel<C, LOADB, EPI, BF>), dim3((unsigned)(tm * tn)),
-                       dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm, tn,
-                       vec, epi_arg<EPI>(epi));
 }
 
 template <class C, bool SK, bool EPI, bool BF>
@@ -1580,18 +1526,19 @@ inline int load_bytes(const void *A, const void *B, int64_t K)
 }
 
 // One workgroup per tile.  EPI: with the fused epilogue `epi`, whose C and
-// bias must then also be 8-byte aligned for vector accesses.
-template <class C, class CDma, class CDma4, bool EPI = false, bool BF = false>
+// bias must then also be 8-byte aligned for vector accesses.  CDma: the
+// direct-to-LDS pipeline (K % 8 == 0, A and B 16-byte aligned); CReg: the
+// same pipeline with register-staged 16-byte chunks (everything else).
+template <class CDma, class CReg, bool EPI = false, bool BF = false>
 void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
                  const Epi &epi = Epi{})
 {
     const int vec = store_mode(D, N, (uintptr_t)epi.C | (uintptr_t)epi.bias);
     const SkPlan none{};
-    switch (load_bytes(A, B, K)) {
-    case 16: launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    case 4: launch_dma<CDma4, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi); return;
-    default: launch_cfg<C, 2, EPI, BF>(A, B, D, M, N, K, vec, s, epi);
-    }
+    if (load_bytes(A, B, K) == 16)
+        launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
+    else
+        launch_dma<CReg, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
 }
 
 // ---------------------------------------------------------------------------

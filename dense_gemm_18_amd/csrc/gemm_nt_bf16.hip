@@ -19,13 +19,13 @@ int gemm_nt_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, in
     } else {
         switch (choose_tile(M, N, K)) {
         case Tile::kBig:
-            launch_tile<Big, BigDma, BigDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
+            launch_tile<BigDma, BigReg, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
             break;
         case Tile::kMid:
-            launch_tile<Mid, MidDma, MidDma4, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
+            launch_tile<MidDma, MidReg, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
             break;
         default:
-            launch_tile<Thin, ThinDma, ThinDma4, false, true>(A, B, D, (int)M, (int)N, (int)K,
+            launch_tile<ThinDma, ThinReg, false, true>(A, B, D, (int)M, (int)N, (int)K,
                                                               stream);
             break;
         }

@@ -19,9 +19,9 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                            (uint16_t *)D, count);
     } else {
         switch (choose_tile(M, N, K)) {
-        case Tile::kBig: launch_tile<Big, BigDma, BigDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        case Tile::kMid: launch_tile<Mid, MidDma, MidDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        default: launch_tile<Thin, ThinDma, ThinDma4>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kBig: launch_tile<BigDma, BigReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        case Tile::kMid: launch_tile<MidDma, MidReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
+        default: launch_tile<ThinDma, ThinReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
         }
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
@@ -54,8 +54,7 @@ int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, i
     if (M < 0 || N < 0 || K < 0 || !bm || !bn || !lbytes || !store)
         return GEMM_EINVAL;
     tile_dims(choose_tile(M, N, K), *bm, *bn);
-    const int lb = load_bytes(A, B, K);
-    *lbytes = lb ? lb : 2;
+    *lbytes = load_bytes(A, B, K) == 16 ? 16 : 1;
     *store = store_mode(D, N);
     return GEMM_OK;
 }

@@ -36,13 +36,13 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
     } else {
         switch (choose_tile(M, N, K)) {
         case Tile::kBig:
-            launch_tile<Big, BigDma, BigDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
+            launch_tile<BigDma, BigReg, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
             break;
         case Tile::kMid:
-            launch_tile<Mid, MidDma, MidDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
+            launch_tile<MidDma, MidReg, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
             break;
         default:
-            launch_tile<Thin, ThinDma, ThinDma4, true>(A, B, D, (int)M, (int)N, (int)K, stream,
+            launch_tile<ThinDma, ThinReg, true>(A, B, D, (int)M, (int)N, (int)K, stream,
                                                        epi);
             break;
         }

@@ -252,15 +252,16 @@ def test_tensor_convenience_rejects_before_any_gpu_use():
 
 @pytest.mark.parametrize("M,N,K,offs,want", [
     (8192, 8192, 8192, (0, 0, 0), (256, 256, 16, 2)),
-    (3000, 5000, 2050, (0, 0, 0), (256, 256, 4, 2)),
-    (2900, 4100, 97, (0, 0, 0), (256, 256, 2, 1)),       # N % 8 == 4: 8-byte stores
-    (2900, 4100, 64, (2, 0, 0), (256, 256, 2, 1)),       # A only 2-byte aligned
-    (2900, 4100, 64, (4, 0, 0), (256, 256, 4, 1)),       # A only 4-byte aligned
+    (3000, 5000, 2050, (0, 0, 0), (256, 256, 1, 2)),     # K % 8 != 0: register staging
+    (2900, 4100, 97, (0, 0, 0), (256, 256, 1, 1)),       # N % 8 == 4: 8-byte stores
+    (2900, 4100, 64, (2, 0, 0), (256, 256, 1, 1)),       # A only 2-byte aligned
+    (2900, 4100, 64, (4, 0, 0), (256, 256, 1, 1)),       # A only 4-byte aligned
+    (2900, 4100, 64, (16, 0, 0), (256, 256, 16, 1)),     # A 16-byte aligned
     (2900, 4096, 64, (0, 0, 8), (256, 256, 16, 1)),      # D 8-byte aligned: direct stores
     (2900, 4096, 64, (0, 0, 2), (256, 256, 16, 0)),      # D 2-byte aligned: element stores
-    (1100, 1100, 99, (0, 0, 0), (128, 128, 2, 1)),
-    (64, 300, 37, (0, 0, 0), (64, 64, 2, 1)),
-    (64, 302, 37, (0, 0, 0), (64, 64, 2, 0)),            # N % 4 != 0: element stores
+    (1100, 1100, 99, (0, 0, 0), (128, 128, 1, 1)),
+    (64, 300, 37, (0, 0, 0), (64, 64, 1, 1)),
+    (64, 302, 37, (0, 0, 0), (64, 64, 1, 0)),            # N % 4 != 0: element stores
 ])
 def test_kernel_introspection(M, N, K, offs, want):
     # the tile, operand load width and store form a call would take; the

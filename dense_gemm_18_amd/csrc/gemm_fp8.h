@@ -31,46 +31,6 @@ using Mid8 = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, false>;
 // per step, so two stages keep the waits encodable.
 using Mid84 = DmaCfg<128, 128, 2, 2, 64, 2, 16, 4, false>;
 
-// Exact FP8 -> fp32 decode from the format definitions (every FP8 value is
-// an fp32 value).  E4M3: bias 7, 3 fraction bits, S.1111.111 is NaN, no
-// infinities.  E5M2: bias 15, 2 fraction bits, IEEE-style specials: it is
-// the upper byte of an fp16.
-template <int FMT>
-__device__ __forceinline__ float fp8_value(uint32_t v)
-{
-    if constexpr (FMT == 1) {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(v << 8));
-    } else {
-        const uint32_t e = (v >> 3) & 15u, f = v & 7u;
-        float x = e ? __builtin_ldexpf((float)(8u + f), (int)e - 10) : __builtin_ldexpf((float)f, -9);
-        if (e == 15u && f == 7u)
-            x = __builtin_nanf("");
-        return (v & 0x80u) ? -x : x;
-    }
-}
-
-// Operands the direct-to-LDS pipeline cannot take (K % 4 != 0 or operands
-// not 4-byte aligned): one output per thread, fp32 sum in ascending k, times
-// scale (or scale * col_scale[n], formed in fp32, with column scales).
-template <int F8>
-__global__ void __launch_bounds__(256)
-gemm_nt_fp8_plain_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
-                         _Float16 *__restrict__ D, int64_t M, int64_t N, int64_t K, float scale,
-                         const float *__restrict__ col_scale)
-{
-    constexpr int fa = (F8 - 1) & 1, fb = (F8 - 1) >> 1;
-    const int64_t count = M * N;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < count; idx += stride) {
-        const int64_t m = idx / N, n = idx - m * N;
-        const uint8_t *a = A + m * K, *b = B + n * K;
-        float acc = 0.0f;
-        for (int64_t k = 0; k < K; ++k)
-            acc = __builtin_fmaf(fp8_value<fa>(a[k]), fp8_value<fb>(b[k]), acc);
-        D[idx] = (_Float16)(acc * (col_scale ? scale * col_scale[n] : scale));
-    }
-}
-
 template <class C, int F8>
 void launch_fp8_dma(const void *A, const void *B, void *D, int M, int N, int Kp, int vec,
                     hipStream_t s, const Epi &epi)
@@ -88,8 +48,29 @@ void launch_fp8_dma(const void *A, const void *B, void *D, int M, int N, int Kp,
                            (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
 }
 
+// Everything else (K % 4 != 0, or operands not 4-byte aligned): 16-byte
+// chunks loaded into registers at any alignment and written to LDS, with K
+// counted in bytes (the 128 x 128 or 64 x 64 tile: the 256 x 256 tile's FP8
+// fragments leave no registers for the staging).
+template <class C, int F8>
+void launch_fp8_reg(const void *A, const void *B, void *D, int M, int N, int K, int vec,
+                    hipStream_t s, const Epi &epi)
+{
+    using T = _Float16;
+    const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
+    const SkPlan none{};
+    if (K % C::ROW_BYTES == 0)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, false, true, false, F8, 1>),
+                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, K, tm, tn, vec, none, epi);
+    else
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, false, true, false, F8, 1>),
+                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, K, tm, tn, vec, none, epi);
+}
+
 // Bytes each lane moves per direct-to-LDS load for FP8 operands with K
-// bytes per row: 16, 4, or 0 (the plain kernel).
+// bytes per row: 16, 4, or 0 (register staging).
 int fp8_load_bytes(const void *A, const void *B, int64_t K)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
@@ -102,8 +83,9 @@ int fp8_load_bytes(const void *A, const void *B, int64_t K)
 
 // Tile of the FP8 product: the 16-bit choice on K / 2 byte pairs for 16-byte
 // loads (an FP8 step moves the same bytes and does twice the MFMA work);
-// with 4-byte loads the 128 x 128 tile (the 256 x 256 one would need more
-// loads in flight than the wait counter encodes) or the thin one.
+// with 4-byte loads or register staging the 128 x 128 tile (the 256 x 256
+// one would need more loads in flight than the wait counter encodes, or
+// more registers) or the thin one.
 Tile fp8_tile(int64_t M, int64_t N, int64_t K, int lb)
 {
     if (lb == 16)
@@ -117,16 +99,16 @@ void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int
 {
     const Epi epi{nullptr, nullptr, scale, 0.0f, col_scale};
     const int lb = fp8_load_bytes(A, B, K);
-    if (lb == 0) {
-        const int64_t blocks = cdiv(M * N, 256) < 8192 ? cdiv(M * N, 256) : 8192;
-        hipLaunchKernelGGL((gemm_nt_fp8_plain_kernel<F8>), dim3((unsigned)blocks), dim3(256), 0,
-                           s, (const uint8_t *)A, (const uint8_t *)B, (_Float16 *)D, M, N, K,
-                           scale, col_scale);
-        return;
-    }
     const int vec = store_mode(D, N);
     const int m = (int)M, n = (int)N, kp = (int)(K / 2);
     const Tile t = fp8_tile(M, N, K, lb);
+    if (lb == 0) {
+        if (t == Tile::kMid)
+            launch_fp8_reg<MidReg, F8>(A, B, D, m, n, (int)K, vec, s, epi);
+        else
+            launch_fp8_reg<ThinReg, F8>(A, B, D, m, n, (int)K, vec, s, epi);
+        return;
+    }
     if (lb == 16) {
         switch (t) {
         case Tile::kBig: launch_fp8_dma<BigDma, F8>(A, B, D, m, n, kp, vec, s, epi); break;

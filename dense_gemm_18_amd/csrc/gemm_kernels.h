@@ -712,7 +712,10 @@ constexpr int kSpinLimit = 1 << 24;
 // layout, swizzle and K masks are those of the 16-bit path.  A K-step (a
 // 128-byte row) is one f8f6f4 MFMA per block; its two slices split the
 // blocks by rows instead of the K-step by halves.
-template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0>
+// UB: bytes of one K unit: 2 (16-bit elements, or FP8 byte pairs), or 1 (FP8
+// bytes, register staging only: any K and any alignment).  K counts units;
+// a K-step is one 128-byte LDS row, BKU units.
+template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0, int UB = 2>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                    const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
@@ -723,6 +726,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     static_assert(F8 == 0 || (!BF && !SK && !C::SPLIT && C::MF == 16 && C::BK == 64 &&
                               C::SLICES == 2 && C::NSTAGE % 2 == 0 && C::TM % 2 == 0),
                   "FP8: 16x16 blocks, 128-byte rows, an even stage ring, loads after the barrier");
+    static_assert(UB == 2 || (UB == 1 && F8 != 0 && C::REG), "byte units: FP8, register staging");
+    constexpr int BKU = C::ROW_BYTES / UB;      // K units per step
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -738,21 +743,21 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // end of the item use it, chosen per step in scalar registers.
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void *)A, (short)0, 0, kRsrcFlags);
-    const int nk = (K + C::BK - 1) / C::BK;
+    const int nk = (K + BKU - 1) / BKU;
     auto set_item = [&](int tile, int s0, int s1) G18_INLINE {
         int64_t tm64, tn64;
         tile_coord(tile, tiles_m, tiles_n, tm64, tn64);
         m0 = (int)tm64 * C::BM;
         n0 = (int)tn64 * C::BN;
         const int rows_a = min(C::BM, M - m0), rows_b = min(C::BN, N - n0);
-        ra = __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0,
-                                               rows_a * K * 2, kRsrcFlags);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0,
-                                               rows_b * K * 2, kRsrcFlags);
+        ra = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)A + (int64_t)m0 * K * UB),
+                                               (short)0, rows_a * K * UB, kRsrcFlags);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)B + (int64_t)n0 * K * UB),
+                                               (short)0, rows_b * K * UB, kRsrcFlags);
         // With a K tail the steps are aligned to K's end instead of its
         // start: step 0 covers k in [-shift, BK - shift) and every later
         // step is full, so only the first step's loads need a K mask.
-        kb = s0 * C::BK - (KTAIL ? nk * C::BK - K : 0);
+        kb = s0 * BKU - (KTAIL ? nk * BKU - K : 0);
         n = s1 - s0;
     };
 
@@ -779,15 +784,15 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         for (int i = 0; i < C::A_LOADS; ++i) {
             const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
             const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-            a_k[i] = gch * 8 + sub / 2;
-            a_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
+            a_k[i] = (gch * 16 + sub) / UB;
+            a_off[i] = (uint32_t)row * (uint32_t)K * UB + (uint32_t)(gch * 16 + sub);
         }
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
             const int row = C::ROWS_PER_INST * (wave + C::NWAVES * i) + slot_row;
             const int gch = (slot_byte / 16) ^ swz_row<C::BK, C::MF>(row);
-            b_k[i] = gch * 8 + sub / 2;
-            b_off[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(gch * 16 + sub);
+            b_k[i] = (gch * 16 + sub) / UB;
+            b_off[i] = (uint32_t)row * (uint32_t)K * UB + (uint32_t)(gch * 16 + sub);
         }
     };
 
@@ -809,10 +814,10 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         constexpr int q = decltype(qc)::value;
         constexpr bool isa = q < C::A_LOADS;
         constexpr int i = isa ? q : q - C::A_LOADS;
-        const int k0 = kb + step * C::BK;
+        const int k0 = kb + step * BKU;
         const __amdgpu_buffer_rsrc_t rs = step < n ? (isa ? ra : rb) : rz;
         const uint32_t off = isa ? a_off[i] : b_off[i];
-        const uint32_t soff = (uint32_t)k0 * 2u;
+        const uint32_t soff = (uint32_t)k0 * (uint32_t)UB;
         if constexpr (KTAIL && decltype(firstc)::value) {
             if (k0 < 0) {
                 // The item's first step starts before k = 0: a chunk whose
@@ -827,11 +832,21 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t o = off + soff + 4u * j;
-                        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
-                            rs, kk + 2 * j >= 0 ? o : kOob, 0, 0);
-                        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
-                            rs, kk + 2 * j + 1 >= 0 ? o + 2u : kOob, 0, 0);
-                        v[j] = lo | (hi << 16);
+                        if constexpr (UB == 2) {
+                            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                                rs, kk + 2 * j >= 0 ? o : kOob, 0, 0);
+                            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                                rs, kk + 2 * j + 1 >= 0 ? o + 2u : kOob, 0, 0);
+                            v[j] = lo | (hi << 16);
+                        } else {
+                            uint32_t w = 0;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                                         rs, kk + 4 * j + e >= 0 ? o + e : kOob, 0, 0)
+                                     << (8 * e);
+                            v[j] = w;
+                        }
                     }
                     rst[q] = v;
                 }
@@ -858,7 +873,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             reg_load(step + 1, qc, std::false_type{});
             return;
         }
-        const int k0 = kb + step * C::BK;
+        const int k0 = kb + step * BKU;
         const bool live = step < n;
         char *stage = smem + S * C::STAGE_BYTES;
         constexpr bool isa = q < C::A_LOADS;
@@ -931,7 +946,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     constexpr int LHALF = C::LPS / 2;
     // Loads issued in one slice: half a step's or a whole step's (register
     // staging: a step's writes and reloads over all its slices).
-    constexpr int LSL = C::REG ? C::LPS / C::SLICES : (C::SPLIT ? LHALF : C::LPS);
+    constexpr int LSL = (C::REG && !F8) ? C::LPS / C::SLICES : (C::SPLIT ? LHALF : C::LPS);
     // Spacing of the loads over the NMS MFMAs of a slice: one load every
     // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
     // than MFMAs (small tiles); the same for fragment reads (RPG).
@@ -1035,7 +1050,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             constexpr int c = S & 1;
             using H1_ = std::integral_constant<int, 1>;
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
+            if constexpr (!C::REG)
+                wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, Z_{});

@@ -69,10 +69,6 @@ int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, in
     if (M < 0 || N < 0 || K < 0 || !bm || !bn)
         return GEMM_EINVAL;
     const int lb = K % 16 == 0 && aligned16 ? 16 : (K % 4 == 0 ? 4 : 0);
-    if (lb == 0) {
-        *bm = *bn = 0;
-        return GEMM_OK;
-    }
     tile_dims(fp8_tile(M, N, K, lb), *bm, *bn);
     return GEMM_OK;
 }

@@ -103,8 +103,10 @@ int gemm_nt_bf16(const void *A, const void *B, void *D,
  *   Products are exact and summed in fp32; the sum is multiplied by scale in
  *   fp32 and rounded once to fp16 (round to nearest even).  K == 0 gives
  *   scale * (+0).
- * Fast path: K % 16 == 0 with A and B 16-byte aligned (then K % 4 == 0
- *   with 4-byte alignment); anything else runs a plain per-output kernel.
+ * Load paths: K % 16 == 0 with A and B 16-byte aligned loads straight into
+ *   LDS (then K % 4 == 0 with 4-byte alignment, 4 bytes per lane); anything
+ *   else loads 16-byte chunks into registers at any alignment and writes
+ *   them to LDS (128 x 128 or 64 x 64 tiles), all on the FP8 MFMA.
  *
  * Returns as gemm_nt_f16 (sizes M, N, K in [0, 2^31 - 1], K <= GEMM_MAX_K),
  * and GEMM_EINVAL also for an unknown format or D overlapping A or B.
@@ -138,7 +140,7 @@ int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, 
 /*
  * Host-only: the output tile gemm_nt_fp8 uses for these sizes (aligned16:
  * whether A and B are 16-byte aligned; 4-byte alignment is assumed
- * otherwise).  *bm = *bn = 0 when the plain per-output kernel runs.
+ * otherwise; with K % 4 != 0 the tile of the register-staged loads).
  * GEMM_EINVAL for negative sizes or NULL outputs.
  */
 int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn);

@@ -226,7 +226,8 @@ def test_fp8_cs_empty_output_needs_no_scales():
     (8192, 8192, 8196, True, (128, 128)),    # K % 16 != 0: 4-byte loads, no 256 x 256 tile
     (8192, 8192, 8192, False, (128, 128)),   # operands only 4-byte aligned
     (40, 8192, 8196, True, (64, 64)),
-    (300, 200, 130, True, (0, 0)),           # K % 4 != 0: the plain kernel
+    (300, 200, 130, True, (128, 128)),       # K % 4 != 0: register staging
+    (50, 300, 131, True, (64, 64)),
 ])
 def test_fp8_tile_choice(M, N, K, aligned, tile):
     assert binding.gemm_nt_fp8_tile(M, N, K, aligned) == tile

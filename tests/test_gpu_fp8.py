@@ -11,7 +11,7 @@ only the fp32 accumulation and the one rounding differ.
 
 Shapes cover the 256 x 256, 128 x 128 and 64 x 64 tiles, ragged M and N
 edges, K tails inside a step (16-byte loads), 4-byte loads (K % 16 != 0 or
-4-byte-aligned operands), the plain kernel (K % 4 != 0, odd addresses),
+4-byte-aligned operands), register-staged loads (K % 4 != 0, odd addresses),
 every format pair, K = 0, special values and the full 8192^3 size on sampled
 rows.
 """
@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 E4, E5 = binding.GEMM_FP8_E4M3, binding.GEMM_FP8_E5M2
 
 # 256x256 (K tail inside a step), 128x128, 64x64, 128x128 with 4-byte loads,
-# 64x64 with 4-byte loads, the plain kernel (K % 4 == 2, K odd), one step
+# 64x64 with 4-byte loads, register staging (K % 4 == 2, K odd), one step
 SHAPES = [(2900, 4100, 400), (1100, 1100, 1024), (64, 300, 512), (700, 900, 4100),
           (50, 300, 260), (300, 200, 130), (150, 97, 37), (256, 256, 128)]
 
@@ -189,7 +189,7 @@ def _pow2_scales(seed, N):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_fp8_cs_integer_bitexact(M, N, K):
     # power-of-two column scales that differ per column: exact on every tile,
-    # load width and the plain kernel
+    # load width and register staging
     A, B = wl.fp8_integers(13000 + K, M, N, K)
     sb = _pow2_scales(13001 + N, N)
     note(f"fp8 column scales integer {M}x{N}x{K}")

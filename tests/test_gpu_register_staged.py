@@ -11,8 +11,8 @@ bit for bit, random inputs within |D - D_ref| <= 2^-10 |D_ref| + 1e-3 sqrt(K)
 (the definition of page "构建 Tiled GEMM", section "GEMM"; the tolerance is
 the fp16 rounding step plus fp32 accumulation drift).  The same shapes go
 through the bfloat16 and fused-epilogue entry points, which share the
-kernel, and the FP8 per-output kernel (K % 4 != 0) runs at a size with
-many workgroups per CU.
+kernel; FP8 operands with K % 4 != 0 or odd addresses take the same loads
+with K counted in bytes.
 """
 from __future__ import annotations
 
@@ -136,16 +136,35 @@ def test_register_staged_epilogue_random():
                      "epilogue random odd K", scale=0.7)
 
 
-@pytest.mark.parametrize("variant", ["integer", "normal"])
-def test_fp8_plain_kernel_at_size(variant):
-    M, N, K = 1100, 1100, 1030           # K % 4 == 2: the per-output kernel
-    assert binding.gemm_nt_fp8_tile(M, N, K, True) == (0, 0)
-    note(f"fp8 per-output kernel {variant} {M}x{N}x{K}")
-    if variant == "integer":
-        A, B = wl.fp8_integers(16200, M, N, K)
-        assert_bitexact(run_gemm_fp8(A, B, 0.25), oracle.gemm_nt_fp8(A, B, 0.25),
-                        "fp8 plain integer")
-    else:
-        A, B, s = wl.fp8_normal(16300, M, N, K)
-        assert_tolerance(run_gemm_fp8(A, B, s), oracle.gemm_nt_fp8(A, B, s), K,
-                         "fp8 plain normal")
+# FP8 with K % 4 != 0 (K counted in bytes, chunks at any byte alignment):
+# 128 x 128 and 64 x 64 tiles, K tails inside a step, odd K, odd addresses
+FP8_CASES = [(1100, 1100, 1030, 0, 128), (1100, 1100, 1031, 0, 128), (700, 900, 4101, 0, 128),
+             (64, 300, 131, 0, 64), (300, 200, 130, 1, 128), (1024, 1024, 4099, 3, 128),
+             (2, 3, 5, 0, 64)]
+
+
+@pytest.mark.parametrize("M,N,K,off,bm", FP8_CASES)
+def test_fp8_register_staged_integer(M, N, K, off, bm):
+    assert binding.gemm_nt_fp8_tile(M, N, K, True)[0] == bm
+    A, B = wl.fp8_integers(16200 + K, M, N, K)
+    note(f"fp8 register-staged integer {M}x{N}x{K} a+{off} tile {bm}")
+    for scale in (1.0, 0.25):
+        assert_bitexact(run_gemm_fp8(A, B, scale, a_off=off, b_off=off),
+                        oracle.gemm_nt_fp8(A, B, scale), f"fp8 reg {M}x{N}x{K} scale {scale}")
+
+
+@pytest.mark.parametrize("M,N,K,off,bm", FP8_CASES[:3])
+def test_fp8_register_staged_normal(M, N, K, off, bm):
+    A, B, s = wl.fp8_normal(16300 + K, M, N, K)
+    note(f"fp8 register-staged normal {M}x{N}x{K}")
+    assert_tolerance(run_gemm_fp8(A, B, s), oracle.gemm_nt_fp8(A, B, s), K,
+                     f"fp8 reg normal {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fa,fb", [(1, 0), (0, 1), (1, 1)])
+def test_fp8_register_staged_formats(fa, fb):
+    M, N, K = 700, 900, 1027
+    A, B = wl.fp8_integers(16400 + 3 * fa + fb, M, N, K, fa, fb)
+    note(f"fp8 register-staged formats {fa},{fb} {M}x{N}x{K}")
+    assert_bitexact(run_gemm_fp8(A, B, 0.5, fa, fb, a_off=1),
+                    oracle.gemm_nt_fp8(A, B, 0.5, bool(fa), bool(fb)), f"fp8 reg formats {fa},{fb}")

@@ -494,14 +494,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Direct-to-LDS buffer load of LB bytes per lane.  The size is spelled as a
 // literal in each branch: the builtin's host-side check of a dependent size
 // argument rejects 16 (a gfx950-only width) and silently drops the kernel.
-template <int LB>
+// AUX: the cache-policy bits (kNt: non-temporal).
+constexpr int kNt = 2;
+template <int LB, int AUX = 0>
 __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, char *dst, uint32_t voff,
                                          uint32_t soff)
 {
     if constexpr (LB == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, AUX);
     else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, voff, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, voff, soff, 0, AUX);
 }
 
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
@@ -556,8 +558,14 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int NSTAGE_, int MF_, int LB_, bool SPLIT_,
-          bool REG_ = false>
+          bool REG_ = false, bool B3_ = false>
 struct DmaCfg {
+    // B3: B gets a ring of three stages while A keeps two (two 32 KB A
+    // stages and three 32 KB B stages fill the 160 KB of LDS at 256 x 256).
+    // B's refills then go out in the first slice of a step, with a step and a
+    // half to land, and A's in the second as before: each slice issues half
+    // a step's loads instead of one slice issuing all of them.
+    static constexpr bool B3 = B3_;
     // LB: bytes one lane moves per load: 16 (buffer_load_dwordx4 ... lds,
     // needs K % 8 == 0 and 16-byte aligned operands) or 4 (buffer_load_dword
     // ... lds, needs K even and 4-byte aligned operands).
@@ -597,8 +605,18 @@ struct DmaCfg {
     static constexpr int A_LOADS = BM / ROWS_PER_INST / NWAVES;   // per wave per stage
     static constexpr int B_LOADS = BN / ROWS_PER_INST / NWAVES;
     static constexpr int LPS = A_LOADS + B_LOADS;            // vmcnt units per stage
+    // Stages: A and B interleaved per stage, or (B3) all A stages then all
+    // B stages.  Steps cycle through PERIOD ring positions; a step at
+    // position p uses A stage p % NSTAGE and B stage p % NSB.
+    static constexpr int NSB = B3 ? NSTAGE + 1 : NSTAGE;
+    static constexpr int PERIOD = B3 ? NSTAGE * NSB : NSTAGE;
     static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-    static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+    static constexpr int LDS_BYTES = NSTAGE * BM * ROW_BYTES + NSB * BN * ROW_BYTES;
+    static constexpr int a_base(int s) { return B3 ? s * BM * ROW_BYTES : s * STAGE_BYTES; }
+    static constexpr int b_base(int s)
+    {
+        return B3 ? NSTAGE * BM * ROW_BYTES + s * BN * ROW_BYTES : s * STAGE_BYTES + BM * ROW_BYTES;
+    }
     static_assert(MF == 32 || MF == 16, "MFMA block of 32x32 or 16x16");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA blocks");
     static_assert(BM % (ROWS_PER_INST * NWAVES) == 0 && BN % (ROWS_PER_INST * NWAVES) == 0,
@@ -613,6 +631,8 @@ struct DmaCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
     static_assert(!REG || (LB == 16 && NSTAGE == 2 && BK == 64 && !SPLIT && LPS % SLICES == 0),
                   "register staging: 16-byte chunks, two stages, writes in every slice");
+    static_assert(!B3 || (NSTAGE == 2 && !SPLIT && !REG && SLICES == 2 && A_LOADS == B_LOADS),
+                  "three B stages: two A stages, two slices, square load split");
 };
 
 // Stream-K work split of a persistent grid of P workgroups (one per CU, all
@@ -714,8 +734,11 @@ constexpr int kSpinLimit = 1 << 24;
 // blocks by rows instead of the K-step by halves.
 // UB: bytes of one K unit: 2 (16-bit elements, or FP8 byte pairs), or 1 (FP8
 // bytes, register staging only: any K and any alignment).  K counts units;
-// a K-step is one 128-byte LDS row, BKU units.
-template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0, int UB = 2>
+// a K-step is one 128-byte LDS row, BKU units.  NT (direct-to-LDS loads):
+// bit 0 loads A, bit 1 loads B with the non-temporal cache policy, set when
+// that operand is read exactly once per call (a single column or row of
+// tiles), so that streaming it does not allocate in the caches.
+template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0, int UB = 2, int NT = 0>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                    const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
@@ -726,6 +749,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     static_assert(F8 == 0 || (!BF && !SK && !C::SPLIT && C::MF == 16 && C::BK == 64 &&
                               C::SLICES == 2 && C::NSTAGE % 2 == 0 && C::TM % 2 == 0),
                   "FP8: 16x16 blocks, 128-byte rows, an even stage ring, loads after the barrier");
+    static_assert(F8 == 0 || !C::B3, "FP8: one ring for A and B");
     static_assert(UB == 2 || (UB == 1 && F8 != 0 && C::REG), "byte units: FP8, register staging");
     constexpr int BKU = C::ROW_BYTES / UB;      // K units per step
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -859,8 +883,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         constexpr int S = decltype(sc)::value, q = decltype(qc)::value;
         constexpr bool isa = q < C::A_LOADS;
         constexpr int i = isa ? q : q - C::A_LOADS;
-        constexpr int base = S * C::STAGE_BYTES + (isa ? 0 : C::BM * C::ROW_BYTES) +
-                             (i * C::NWAVES) * C::INST_BYTES;
+        constexpr int base = (isa ? C::a_base(S) : C::b_base(S)) + (i * C::NWAVES) * C::INST_BYTES;
         *(u32x4 *)(smem + base + wave * C::INST_BYTES + lane * 16) = rst[q];
     };
 
@@ -875,8 +898,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         }
         const int k0 = kb + step * BKU;
         const bool live = step < n;
-        char *stage = smem + S * C::STAGE_BYTES;
         constexpr bool isa = q < C::A_LOADS;
+        // S: the ring position of `step`
+        char *stage = smem + (isa ? C::a_base(S % C::NSTAGE) : C::b_base(S % C::NSB));
         constexpr int i = isa ? q : q - C::A_LOADS;
         uint32_t off = isa ? a_off[i] : b_off[i];
         uint32_t soff = (uint32_t)k0 * 2u;
@@ -887,8 +911,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 soff = 0;
             }
         }
-        char *dst = stage + (isa ? 0 : C::BM * C::ROW_BYTES) + (wave + C::NWAVES * i) * C::INST_BYTES;
-        load_lds<C::LB>(live ? (isa ? ra : rb) : rz, dst, off, soff);
+        char *dst = stage + (wave + C::NWAVES * i) * C::INST_BYTES;
+        load_lds<C::LB, (NT >> (isa ? 0 : 1)) & 1 ? kNt : 0>(live ? (isa ? ra : rb) : rz, dst, off,
+                                                              soff);
     };
 
     typename C::acc_t acc[C::TM][C::TN];
@@ -899,18 +924,18 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // both K-contiguous).  Fragment q < TM is A block q, the rest B blocks.
     // The LDS address of every (stage, slice) is precomputed, so a fragment
     // read is one ds_read_b128 with an immediate offset.
-    uint32_t a_addr[C::NSTAGE][C::SLICES], b_addr[C::NSTAGE][C::SLICES];
+    uint32_t a_addr[C::NSTAGE][C::SLICES], b_addr[C::NSB][C::SLICES];
     auto setup_reads = [&](int ln) G18_INLINE {
         const int frow = ln % C::MF, fhi = ln / C::MF;
         const int fsw = swz_row<C::BK, C::MF>(frow);   // fragment rows differ from frow by multiples of MF
 #pragma unroll
-        for (int st = 0; st < C::NSTAGE; ++st)
+        for (int st = 0; st < C::NSB; ++st)
 #pragma unroll
             for (int t = 0; t < C::SLICES; ++t) {
                 const uint32_t ch = (uint32_t)(((C::CHS * t + fhi) ^ fsw) * 16);
-                a_addr[st][t] = st * C::STAGE_BYTES + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
-                b_addr[st][t] = st * C::STAGE_BYTES + C::BM * C::ROW_BYTES +
-                                (wn * C::WTN + frow) * C::ROW_BYTES + ch;
+                if (st < C::NSTAGE)
+                    a_addr[st][t] = C::a_base(st) + (wm * C::WTM + frow) * C::ROW_BYTES + ch;
+                b_addr[st][t] = C::b_base(st) + (wn * C::WTN + frow) * C::ROW_BYTES + ch;
             }
     };
     // Two fragment sets (alternating slices): A blocks fa[set][i], B blocks
@@ -936,7 +961,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             const u32x4 hi = *(const u32x4 *)(smem + p1 + off);
             f = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-            f = *(const X8 *)(smem + (q < C::TM ? a_addr[S][t] : b_addr[S][t]) + off);
+            f = *(const X8 *)(smem + (q < C::TM ? a_addr[S % C::NSTAGE][t] : b_addr[S % C::NSB][t]) +
+                              off);
         }
     };
 
@@ -946,7 +972,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     constexpr int LHALF = C::LPS / 2;
     // Loads issued in one slice: half a step's or a whole step's (register
     // staging: a step's writes and reloads over all its slices).
-    constexpr int LSL = (C::REG && !F8) ? C::LPS / C::SLICES : (C::SPLIT ? LHALF : C::LPS);
+    constexpr int LSL = (C::REG && !F8) ? C::LPS / C::SLICES
+                        : C::B3           ? C::A_LOADS
+                                          : (C::SPLIT ? LHALF : C::LPS);
     // Spacing of the loads over the NMS MFMAs of a slice: one load every
     // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
     // than MFMAs (small tiles); the same for fragment reads (RPG).
@@ -1036,10 +1064,13 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // every iteration.  S is step u's stage, a compile-time constant: the
     // step loop is unrolled NSTAGE times.
     auto step_body = [&](int u, auto sc) G18_INLINE {
+        // S: the ring position of step u (the stage itself unless B3)
         constexpr int S = decltype(sc)::value;
         using S_ = std::integral_constant<int, S>;
-        using SP_ = std::integral_constant<int, (S + C::NSTAGE - 1) % C::NSTAGE>;   // step u-1+NSTAGE
-        using SN_ = std::integral_constant<int, (S + 1) % C::NSTAGE>;               // step u+1
+        using SP_ = std::integral_constant<int, (S + C::NSTAGE - 1) % C::PERIOD>;   // step u-1+NSTAGE
+        using SN_ = std::integral_constant<int, (S + 1) % C::PERIOD>;               // step u+1
+        using SR_ = std::integral_constant<int, (S + C::NSTAGE) % C::PERIOD>;       // step u+NSTAGE
+        using SB_ = std::integral_constant<int, (S + C::NSB - 1) % C::PERIOD>;      // step u+NSB-1
         if constexpr (F8 != 0) {
             // FP8: the barrier comes first (step u + 1 landed, step u's stage
             // free); the first slice refills the stage with step u + NSTAGE
@@ -1054,14 +1085,20 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, Z_{});
+            slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, SR_{}, Z_{}, Z_{});
             slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, F_{}, 0, S_{}, Z_{}, H1_{});
         } else {
         static_for<0, C::SLICES>([&](auto tc) G18_INLINE {
             constexpr int t = decltype(tc)::value;
             constexpr int c = t & 1;    // 16-bit slices alternate fragment sets
             using TN_ = std::integral_constant<int, t + 1>;
-            if constexpr (C::REG && t + 1 < C::SLICES) {
+            if constexpr (C::B3 && t == 0) {
+                // B's refill: step u + NSB - 1 into the B stage step u - 1
+                // left (free since the previous step's barrier)
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{},
+                      S_{}, TN_{}, T_{}, u + C::NSB - 1, SB_{},
+                      std::integral_constant<int, C::A_LOADS>{}, tc);
+            } else if constexpr (C::REG && t + 1 < C::SLICES) {
                 // group t + 1 of step u - 1 + NSTAGE (its stage was freed at
                 // the previous step's barrier)
                 slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, S_{}, TN_{}, T_{}, u - 1 + C::NSTAGE, SP_{},
@@ -1077,12 +1114,16 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 // ahead of the barrier, where they run while the wave waits.
                 // (Register staging waits for each chunk's load only before
                 // writing it; the compiler places those waits.)
+                // (B3: only B's refill for step u + 2, issued in this
+                // step's first slice, may be outstanding.)
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (!C::REG)
+                if constexpr (C::B3)
+                    wait_vmcnt<C::B_LOADS>();
+                else if constexpr (!C::REG)
                     wait_vmcnt<C::LPS * (C::NSTAGE - 2)>();
                 lds_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, S_{}, Z_{}, tc);
+                slice(std::integral_constant<int, c>{}, std::integral_constant<int, c ^ 1>{}, T_{}, SN_{}, Z_{}, T_{}, u + C::NSTAGE, SR_{}, Z_{}, tc);
             }
         });
         }
@@ -1299,9 +1340,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // an extra step multiplies the all-zero stage that the zero-length
     // resource filled, and adding +0 leaves every accumulator unchanged (an
     // fp32 sum that starts at +0 is never -0).
-    for (int u = 0; u < n; u += C::NSTAGE)
-        static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
-            if (C::NSTAGE <= 2 || u + decltype(sc)::value < n)
+    for (int u = 0; u < n; u += C::PERIOD)
+        static_for<0, C::PERIOD>([&](auto sc) G18_INLINE {
+            if (C::PERIOD <= 2 || u + decltype(sc)::value < n)
                 step_body(u + decltype(sc)::value, sc);
         });
     wait_vmcnt<0>();      // drain the zero-filling prefetches
@@ -1504,14 +1545,33 @@ void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int 
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
     if (!SK)
         grid = tm * tn;
+    auto go = [&](auto ktail, auto ntc) {
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, decltype(ktail)::value, SK, EPI, BF, 0, 2,
+                                               decltype(ntc)::value>),
+                           dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
+    };
+    auto go_nt = [&](auto ktail) {
+        // An operand read once per call (one tile row: B; one tile column:
+        // A) streams with the non-temporal policy: 64 x 16384 x 8192 with
+        // operands streamed from HBM reads 5.26 TB/s instead of 4.66 (but
+        // 5.36 instead of 6.0 when B stays resident in the last-level cache
+        // between calls).  The 128 x 128 and 64 x 64 direct-load tiles only.
+        const int nt = (C::BM <= 128 && !C::REG && !SK) ? (tn == 1 ? 1 : 0) | (tm == 1 ? 2 : 0) : 0;
+        if constexpr (C::BM <= 128 && !C::REG && !SK) {
+            switch (nt) {
+            case 1: go(ktail, std::integral_constant<int, 1>{}); return;
+            case 2: go(ktail, std::integral_constant<int, 2>{}); return;
+            case 3: go(ktail, std::integral_constant<int, 3>{}); return;
+            default: break;
+            }
+        }
+        go(ktail, std::integral_constant<int, 0>{});
+    };
     if (K % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, SK, EPI, BF>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
-                           tn, vec, sk, epi_arg<EPI>(epi));
+        go_nt(std::false_type{});
     else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, SK, EPI, BF>), dim3((unsigned)grid),
-                           dim3(C::THREADS), 0, s, (const T *)A, (const T *)B, (T *)D, M, N, K, tm,
-                           tn, vec, sk, epi_arg<EPI>(epi));
+        go_nt(std::true_type{});
 }
 
 // The kernels' vec_store flag: 0 element stores; 1 D (and the epilogue's C

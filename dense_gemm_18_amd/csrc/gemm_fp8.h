@@ -38,14 +38,29 @@ void launch_fp8_dma(const void *A, const void *B, void *D, int M, int N, int Kp,
     using T = _Float16;
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
     const SkPlan none{};
+    auto go = [&](auto ktail, auto ntc) {
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, decltype(ktail)::value, false, true, false, F8, 2,
+                                               decltype(ntc)::value>),
+                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
+    };
+    // As for 16-bit operands: an operand read once per call (one tile row:
+    // B; one tile column: A) streams with the non-temporal policy.
+    auto go_nt = [&](auto ktail) {
+        if constexpr (C::BM <= 128 && C::LB == 16) {
+            switch ((tn == 1 ? 1 : 0) | (tm == 1 ? 2 : 0)) {
+            case 1: go(ktail, std::integral_constant<int, 1>{}); return;
+            case 2: go(ktail, std::integral_constant<int, 2>{}); return;
+            case 3: go(ktail, std::integral_constant<int, 3>{}); return;
+            default: break;
+            }
+        }
+        go(ktail, std::integral_constant<int, 0>{});
+    };
     if (Kp % C::BK == 0)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, false, true, false, F8>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
-                           (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
+        go_nt(std::false_type{});
     else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, false, true, false, F8>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
-                           (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
+        go_nt(std::true_type{});
 }
 
 // Everything else (K % 4 != 0, or operands not 4-byte aligned): 16-byte

@@ -975,14 +975,10 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     constexpr int LSL = (C::REG && !F8) ? C::LPS / C::SLICES
                         : C::B3           ? C::A_LOADS
                                           : (C::SPLIT ? LHALF : C::LPS);
-    // Spacing of the loads over the NMS MFMAs of a slice: one load every
-    // LSPACE MFMAs, or LPG loads after each MFMA when there are more loads
-    // than MFMAs (small tiles); the same for fragment reads (RPG).
-    constexpr int LSPACE = NMS >= LSL ? NMS / LSL : 1;
-    constexpr int LPG = NMS >= LSL ? 1 : LSL / NMS;
+    // The LSL loads of a slice are spread evenly over its NMS MFMAs (load l
+    // after MFMA floor(l NMS / LSL)); RPG fragment reads follow each MFMA.
     constexpr int RPG = (NR + NM - 1) / NM;
-    static_assert(C::LPS % 2 == 0 && (NMS % LSL == 0 || LSL % NMS == 0),
-                  "loads split evenly over the slices that issue them");
+    static_assert(C::LPS % 2 == 0, "loads split evenly over the slices that issue them");
     // FP8 read schedule, by the slice's MFMA index p: the next step's B
     // blocks (double-buffered) during the first slice, B block j after
     // p = j * BSTEP; its A blocks (single-buffered) during the second: those
@@ -1033,13 +1029,15 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 static_for<q * RPG, (q * RPG + RPG < NR ? q * RPG + RPG : NR)>(
                     [&](auto rc) G18_INLINE { read_one(nxt, rs, rt, rc); });
             }
-            if constexpr (decltype(do_load)::value && p % LSPACE == 0)
-                static_for<0, LPG>([&](auto gc) G18_INLINE {
-                    issue_one(lstep, ls,
-                              std::integral_constant<int, decltype(l0)::value + (p / LSPACE) * LPG +
-                                                              decltype(gc)::value>{},
-                              std::false_type{});
-                });
+            // loads ceil(p LSL / NMS) .. ceil((p + 1) LSL / NMS) - 1 after MFMA p
+            if constexpr (decltype(do_load)::value)
+                static_for<(p * LSL + NMS - 1) / NMS, ((p + 1) * LSL + NMS - 1) / NMS>(
+                    [&](auto gc) G18_INLINE {
+                        issue_one(lstep, ls,
+                                  std::integral_constant<int, decltype(l0)::value +
+                                                                  decltype(gc)::value>{},
+                                  std::false_type{});
+                    });
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -1449,6 +1447,10 @@ using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
 // 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
 // eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
 using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
+// 64 x 32 and 32 x 64 (skinny shapes whose 64 x 64 tiles would leave CUs
+// idle, e.g. 64 x 8192 x K): 2 waves of 32 x 32, ten 12 KB stages.
+using ThinNDma = DmaCfg<64, 32, 2, 1, 64, 10, 16, 16, false>;
+using ThinMDma = DmaCfg<32, 64, 1, 2, 64, 10, 16, 16, false>;
 // 4-byte loads (K even, operands 4-byte aligned): four times as many load
 // instructions per step, so fewer stages keep the waits encodable.
 using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 16, 4, true>;
@@ -1462,7 +1464,7 @@ using BigReg = DmaCfg<256, 256, 2, 2, 64, 2, 32, 16, false, true>;
 using MidReg = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false, true>;
 using ThinReg = DmaCfg<64, 64, 2, 2, 64, 2, 16, 16, false, true>;
 
-enum class Tile { kBig, kMid, kThin };
+enum class Tile { kBig, kMid, kThin, kThinN, kThinM };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1483,8 +1485,18 @@ constexpr int kCUs = 256;
 // tile only when M or N is at most 64.
 inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
 {
-    if (M <= 64 || N <= 64)
+    if (M <= 64 || N <= 64) {
+        // Skinny: every CU streams its share of the long operand, so fewer
+        // than one 64 x 64 tile per CU leaves bandwidth unused; halving the
+        // tile along the long side then fills twice as many CUs.
+        if (thin_ok && cdiv(M, 64) * cdiv(N, 64) < kCUs) {
+            if (M <= 64 && N > 64)
+                return Tile::kThinN;
+            if (N <= 64 && M > 64)
+                return Tile::kThinM;
+        }
         return Tile::kThin;
+    }
     const bool wide = K % 8 == 0;
     const double big_tile = wide ? 4.0 : 6.6, mid_tile = wide ? 1.4 : 2.25;
     const double thin_tile = wide ? 0.85 : 1.3;
@@ -1498,11 +1510,20 @@ inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
     return mid <= thin ? Tile::kMid : Tile::kThin;
 }
 
+// The tile a call runs: register staging (direct == false) serves the
+// 64 x 32 and 32 x 64 tiles with the 64 x 64 kernel.
+inline Tile run_tile(Tile t, bool direct)
+{
+    return !direct && (t == Tile::kThinN || t == Tile::kThinM) ? Tile::kThin : t;
+}
+
 inline void tile_dims(Tile t, int &bm, int &bn)
 {
     switch (t) {
     case Tile::kBig: bm = BigDma::BM; bn = BigDma::BN; break;
     case Tile::kMid: bm = MidDma::BM; bn = MidDma::BN; break;
+    case Tile::kThinN: bm = ThinNDma::BM; bn = ThinNDma::BN; break;
+    case Tile::kThinM: bm = ThinMDma::BM; bn = ThinMDma::BN; break;
     default: bm = ThinDma::BM; bn = ThinDma::BN; break;
     }
 }
@@ -1615,6 +1636,21 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
         launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
     else
         launch_dma<CReg, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
+}
+
+// The tile `t` with direct-to-LDS loads when they apply, else register
+// staging (the 64 x 64 kernel serves the 64 x 32 and 32 x 64 tiles then).
+template <bool EPI = false, bool BF = false>
+void launch_plain(Tile t, const void *A, const void *B, void *D, int M, int N, int K,
+                  hipStream_t s, const Epi &epi = Epi{})
+{
+    switch (t) {
+    case Tile::kBig: launch_tile<BigDma, BigReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    case Tile::kMid: launch_tile<MidDma, MidReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    case Tile::kThinN: launch_tile<ThinNDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    case Tile::kThinM: launch_tile<ThinMDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    default: launch_tile<ThinDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    }
 }
 
 // ---------------------------------------------------------------------------

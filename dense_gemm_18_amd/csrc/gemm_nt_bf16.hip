@@ -17,18 +17,7 @@ int gemm_nt_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, in
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (uint16_t *)D, count);
     } else {
-        switch (choose_tile(M, N, K)) {
-        case Tile::kBig:
-            launch_tile<BigDma, BigReg, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
-            break;
-        case Tile::kMid:
-            launch_tile<MidDma, MidReg, false, true>(A, B, D, (int)M, (int)N, (int)K, stream);
-            break;
-        default:
-            launch_tile<ThinDma, ThinReg, false, true>(A, B, D, (int)M, (int)N, (int)K,
-                                                              stream);
-            break;
-        }
+        launch_plain<false, true>(choose_tile(M, N, K), A, B, D, (int)M, (int)N, (int)K, stream);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }

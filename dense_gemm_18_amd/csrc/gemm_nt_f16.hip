@@ -18,11 +18,7 @@ int gemm_nt_f16(const void *A, const void *B, void *D, int64_t M, int64_t N, int
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (uint16_t *)D, count);
     } else {
-        switch (choose_tile(M, N, K)) {
-        case Tile::kBig: launch_tile<BigDma, BigReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        case Tile::kMid: launch_tile<MidDma, MidReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        default: launch_tile<ThinDma, ThinReg>(A, B, D, (int)M, (int)N, (int)K, stream); break;
-        }
+        launch_plain(choose_tile(M, N, K), A, B, D, (int)M, (int)N, (int)K, stream);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }
@@ -42,7 +38,7 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk,
 {
     if (M < 0 || N < 0 || K < 0 || !bm || !bn || !bk || !workgroups)
         return GEMM_EINVAL;
-    tile_dims(choose_tile(M, N, K), *bm, *bn);
+    tile_dims(run_tile(choose_tile(M, N, K), K % 8 == 0), *bm, *bn);
     *bk = kBK;
     *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : cdiv(M, *bm) * cdiv(N, *bn);
     return GEMM_OK;
@@ -53,8 +49,8 @@ int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, i
 {
     if (M < 0 || N < 0 || K < 0 || !bm || !bn || !lbytes || !store)
         return GEMM_EINVAL;
-    tile_dims(choose_tile(M, N, K), *bm, *bn);
     *lbytes = load_bytes(A, B, K) == 16 ? 16 : 1;
+    tile_dims(run_tile(choose_tile(M, N, K), *lbytes == 16), *bm, *bn);
     *store = store_mode(D, N);
     return GEMM_OK;
 }

@@ -34,18 +34,8 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
         hipLaunchKernelGGL(epilogue_only_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (_Float16 *)D, epi, M, N);
     } else {
-        switch (choose_tile(M, N, K)) {
-        case Tile::kBig:
-            launch_tile<BigDma, BigReg, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
-            break;
-        case Tile::kMid:
-            launch_tile<MidDma, MidReg, true>(A, B, D, (int)M, (int)N, (int)K, stream, epi);
-            break;
-        default:
-            launch_tile<ThinDma, ThinReg, true>(A, B, D, (int)M, (int)N, (int)K, stream,
-                                                       epi);
-            break;
-        }
+        launch_plain<true>(choose_tile(M, N, K), A, B, D, (int)M, (int)N, (int)K, stream,
+                          epi);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }

@@ -101,7 +101,9 @@ def test_tile_introspection():
     (1100, 1100, 1024, 128),    # 81 mid tiles vs 324 thin tiles (2 waves)
     (1024, 1024, 1026, 64),     # 4-byte loads
     (2048, 1024, 1026, 128),
-    (64, 16384, 8192, 64),      # M <= 64: the thin tile
+    (64, 16384, 8192, 64),      # M <= 64: the thin tile (256 tiles fill the CUs)
+    (64, 8192, 8192, 64),       # 128 thin tiles would leave CUs idle: 64 x 32 (bm 64)
+    (8192, 64, 8192, 32),       # and 32 x 64
     (16384, 33, 128, 64),
 ])
 def test_tile_choice(M, N, K, bm):
@@ -276,3 +278,14 @@ def test_kernel_introspection(M, N, K, offs, want):
 def test_kernel_introspection_rejects_negative_sizes():
     with pytest.raises(binding.GemmError):
         binding.gemm_nt_f16_kernel(FAKE, FAKE, FAKE, -1, 4, 4)
+
+
+@pytest.mark.parametrize("M,N,K,tile", [
+    (64, 8192, 8192, (64, 32)), (50, 3000, 136, (64, 32)), (8192, 64, 512, (32, 64)),
+    (3000, 50, 72, (32, 64)), (64, 16384, 8192, (64, 64)), (64, 64, 64, (64, 64)),
+    (64, 8192, 8191, (64, 64)),       # K % 8 != 0: register staging on 64 x 64 tiles
+])
+def test_skinny_tiles(M, N, K, tile):
+    bm, bn, _, wg = binding.gemm_nt_f16_tile(M, N, K)
+    assert (bm, bn) == tile
+    assert wg == -(-M // bm) * -(-N // bn)

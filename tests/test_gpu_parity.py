@@ -126,7 +126,7 @@ def test_mn_sweep(M, N):
                                     (800, 2300, 72, 128), (2000, 700, 130, 128)])
 def test_tile_tails(M, N, K, bm):
     # ragged M, N and K on the 256 x 256 and the 128 x 128 tiles (K = 98 and
-    # 130 take the 4-byte loads)
+    # 130 take the register-staged loads)
     A, B = wl.integer_free(3000 + K, M, N, K)
     tbm, tbn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
     assert tbm == bm
@@ -163,7 +163,7 @@ def test_staged_and_direct_epilogue(M, N, K):
 
 
 def test_random_small_general_path():
-    A, B = wl.uniform_inputs(77, 333, 222, 1001)     # K odd: element loads
+    A, B = wl.uniform_inputs(77, 333, 222, 1001)     # K odd: register-staged loads
     note("random 333x222x1001")
     assert_tolerance(run_gemm(A, B), oracle.gemm_nt_f16(A, B), 1001, "odd K random")
 
@@ -208,3 +208,21 @@ def test_rejects_bad_arguments_without_launch():
     assert binding.gemm_nt_f16(p, p, p + 1, 1, 1, 1, 0) == binding.GEMM_EINVAL    # misaligned D
     assert binding.gemm_nt_f16(p, p, p, -1, 1, 1, 0) == binding.GEMM_EINVAL
     assert binding.gemm_nt_f16(p, p, p, 0, 3, 3, 0) == binding.GEMM_OK             # M = 0: no-op
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(64, 8192, 512, (64, 32)), (50, 3000, 136, (64, 32)),
+                                        (8192, 64, 512, (32, 64)), (3000, 50, 72, (32, 64)),
+                                        (33, 1000, 1000, (64, 32))])
+def test_skinny_half_tiles(M, N, K, tile):
+    # skinny shapes whose 64 x 64 tiles would leave CUs idle run 64 x 32 or
+    # 32 x 64 tiles (2 waves); integer inputs bit-exact, staged (D 16-byte
+    # aligned, N % 8 == 0) and direct stores, and random inputs in tolerance
+    bm, bn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
+    assert (bm, bn) == tile
+    A, B = wl.integer_free(7700 + M + N + K, M, N, K)
+    ref = oracle.gemm_nt_f16(A, B)
+    note(f"skinny half tiles {M}x{N}x{K} tile {bm}x{bn}")
+    assert_bitexact(run_gemm(A, B), ref, f"{M}x{N}x{K}")
+    assert_bitexact(run_gemm(A, B, d_off=4), ref, f"{M}x{N}x{K} direct stores")
+    Ar, Br = wl.uniform_inputs(7800 + K, M, N, K)
+    assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")

@@ -245,6 +245,15 @@ class ClockSampler:
             return out
         samples, limits = self.parse()
         out["power_limits_w"] = limits
+        if not limits:
+            # the static query's text, when its layout did not parse
+            static = []
+            for _, ln in self.lines:
+                if ln.strip() == "__METRIC__":
+                    break
+                if ln.strip():
+                    static.append(ln.strip())
+            out["power_limit_text"] = static[:16]
         inside = [x for x in samples if t0 <= x["t"] <= t1 and x["gfx"]]
         out["samples_total"] = len(samples)
         out["samples_under_load"] = len(inside)
@@ -307,13 +316,16 @@ def setup_path(path, w, torch, dev, binding, wl) -> dict:
         keep += [dA, dB]
     if path == "f16":
         import oracle
-        # HBM-bound shapes (below the ridge point) rotate over independent
-        # copies of A and B totalling more than 512 MB, so that the 256 MB
-        # MALL cannot serve the next launch's operands: every launch streams
-        # them from HBM.  Compute-bound shapes are timed warm.
+        # HBM-bound shapes (below the ridge point) whose operands are large
+        # (32 MB or more) rotate over independent copies of A and B totalling
+        # more than 512 MB, so that the 256 MB MALL cannot serve the next
+        # launch's operands: every launch streams them from HBM.  Compute-
+        # bound shapes, and problems small enough to be latency-bound, are
+        # timed warm.
         sets = [(pa, pb)]
-        if 2.0 * M * N * K / P["bytes"] < PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-            per_set = 2 * (M * K + N * K)
+        per_set = 2 * (M * K + N * K)
+        if (2.0 * M * N * K / P["bytes"] < PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+                and per_set >= (32 << 20)):
             for _ in range(max(2, -(-(512 << 20) // per_set) + 1) - 1):
                 cA, cB = dA.clone(), dB.clone()
                 keep += [cA, cB]

@@ -59,6 +59,11 @@ def _load():
     lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_acc16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_acc16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_acc16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p,
+                                                     ctypes.c_int]
+    lib.oracle_gemm_nt_f16_acc16_entries.restype = ctypes.c_int
     lib.oracle_bf16_decode.argtypes = [p, p, i64]
     lib.oracle_bf16_decode.restype = None
     lib.oracle_bf16_encode.argtypes = [p, p, i64]
@@ -138,6 +143,41 @@ def gemm_nt_f16_entries(A: np.ndarray, B: np.ndarray, rows, cols,
     out = np.empty(r.shape, dtype=np.uint16)
     _load().oracle_gemm_nt_f16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c),
                                        r.size, _ptr(out), int(threads))
+    return out
+
+
+def gemm_nt_f16_acc16(A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
+    """D = A * B^T with an fp16 running sum (page "如何用 Croqtile 一步步优化矩阵
+    乘法内核", the f16 accumulator of its kernels): chunks of 64 consecutive k,
+    aligned to K's end, each added to the fp16 sum with one rounding.  fp16
+    bit patterns (uint16, M x N)."""
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    M, K = a.shape
+    N = b.shape[0]
+    d = np.empty((M, N), dtype=np.uint16)
+    _load().oracle_gemm_nt_f16_acc16(_ptr(a), _ptr(b), _ptr(d), M, N, K, int(threads))
+    return d
+
+
+def gemm_nt_f16_acc16_entries(A: np.ndarray, B: np.ndarray, rows, cols,
+                              threads: int = 0) -> np.ndarray:
+    """Entries D[rows[i], cols[i]] of the fp16-accumulated product."""
+    a, b = _bits(A), _bits(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")
+    r = np.ascontiguousarray(rows, dtype=np.int64).ravel()
+    c = np.ascontiguousarray(cols, dtype=np.int64).ravel()
+    if r.shape != c.shape:
+        raise ValueError("rows and cols differ in length")
+    M, K = a.shape
+    N = b.shape[0]
+    if r.size and (r.min() < 0 or r.max() >= M or c.min() < 0 or c.max() >= N):
+        raise IndexError("entry index outside D")
+    out = np.empty(r.shape, dtype=np.uint16)
+    _load().oracle_gemm_nt_f16_acc16_entries(_ptr(a), _ptr(b), M, N, K, _ptr(r), _ptr(c),
+                                             r.size, _ptr(out), int(threads))
     return out
 
 

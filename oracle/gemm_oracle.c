@@ -66,6 +66,23 @@
  * rounding, as both scales are fp32 values), then multiplies the exact sum
  * before the one rounding to fp16.
  *
+ * fp16 accumulation (oracle_gemm_nt_f16_acc16): page "如何用 Croqtile 一步步
+ * 优化矩阵乘法内核" keeps the running sum itself in fp16: its naive kernel
+ * declares an f16 accumulator (section "内核 0：朴素版"), and its Hopper
+ * kernels fill the matrix-unit accumulator as f16, which it notes takes
+ * fewer registers (section "内核 2：Hopper TMA + WGMMA"; the tuned kernel of
+ * section "内核 4：生产级调优" keeps it).  A matrix-unit update with an fp16
+ * accumulator reads the fp16 partial sum, adds a group of products and
+ * writes the result back in fp16.  Readings taken where the page is silent:
+ *  - one update adds the products of 64 consecutive k (a chunk); the chunks
+ *    tile [0, K) from its end, so when K is not a multiple of 64 the first
+ *    chunk holds the K mod 64 leading terms;
+ *  - an update is s <- fp16(s + sum over the chunk of A[m,k] * B[n,k]): the
+ *    chunk's products and s are summed in fp64 and rounded once, to nearest
+ *    with ties to even;
+ *  - s starts at +0 and D[m,n] is the last s; K = 0 gives +0; an infinite
+ *    or NaN s stays so (NaN as 0x7E00).
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
  */
@@ -312,6 +329,58 @@ int oracle_gemm_nt_f16_ex(const uint16_t *A, const uint16_t *B, const uint16_t *
                 r = r + g_lut[bias[n]];
             D[m * N + n] = f16_encode_rne(r);
         }
+    return nt;
+}
+
+/* ---- fp16 accumulation -------------------------------------------------- */
+
+/* One output entry with an fp16 running sum: chunks of 64 consecutive k,
+ * aligned to K's end, each added to the sum with one rounding to fp16. */
+static uint16_t entry_acc16(const uint16_t *arow, const uint16_t *brow, int64_t K)
+{
+    double s = 0.0;                       /* always an fp16 value */
+    int64_t k0 = 0;
+    int64_t len = K % 64 ? K % 64 : 64;   /* the first chunk */
+    while (k0 < K) {
+        double c = 0.0;
+        for (int64_t k = k0; k < k0 + len; ++k)
+            c += g_lut[arow[k]] * g_lut[brow[k]];
+        s = g_lut[f16_encode_rne(s + c)];
+        k0 += len;
+        len = 64;
+    }
+    return f16_encode_rne(s);
+}
+
+/* Full D with an fp16 running sum (see the header comment). */
+int oracle_gemm_nt_f16_acc16(const uint16_t *A, const uint16_t *B, uint16_t *D,
+                             int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    lut_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            D[m * N + n] = entry_acc16(A + m * K, B + n * K, K);
+    return nt;
+}
+
+/* Selected entries of the fp16-accumulated product (index outside: NaN). */
+int oracle_gemm_nt_f16_acc16_entries(const uint16_t *A, const uint16_t *B,
+                                     int64_t M, int64_t N, int64_t K,
+                                     const int64_t *rows, const int64_t *cols,
+                                     int64_t count, uint16_t *out, int nthreads)
+{
+    lut_init();
+    int nt = pick_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = rows[i], n = cols[i];
+        if (m < 0 || m >= M || n < 0 || n >= N)
+            out[i] = 0x7e00;
+        else
+            out[i] = entry_acc16(A + m * K, B + n * K, K);
+    }
     return nt;
 }
 

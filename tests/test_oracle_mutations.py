@@ -8,7 +8,9 @@ beta or alpha on the wrong term, a transposed C, a rounding before the
 epilogue; in FP8 a wrong exponent bias, flushed subnormals, the other NaN
 convention, saturation in place of infinity, swapped formats, a rounding
 before the scale; with per-channel scales a scale per row, a dropped
-activation scale, a rounding before the scale), compiles the copy with gcc, points the oracle wrapper at it
+activation scale, a rounding before the scale; with an fp16 running sum a
+chunk of 32, chunks counted from k = 0, the chunk rounded before it is added,
+a wide running sum, a dropped chunk, a wrong sign, a wrong row of B), compiles the copy with gcc, points the oracle wrapper at it
 and runs the pin battery.  At least one pin must fail for every planted mistake.  All
 of this runs on the CPU; the real oracle is not modified.
 """
@@ -22,6 +24,7 @@ from pathlib import Path
 import pytest
 
 import oracle
+from tests import test_oracle_acc16_pins as hpins
 from tests import test_oracle_bf16_pins as bpins
 from tests import test_oracle_epilogue_pins as epins
 from tests import test_oracle_fp8_pins as fpins
@@ -85,6 +88,21 @@ MUTATIONS = {
                                         "const float sn = b_scale[n];"),
     "fp8_cs_round_before_scale": ("D[m * N + n] = f16_encode_rne((double)sn * acc);",
                                   "D[m * N + n] = f16_encode_rne((double)sn * g_lut[f16_encode_rne(acc)]);"),
+    # fp16 accumulation
+    "acc16_chunk_32": ("        len = 64;\n    }\n    return f16_encode_rne(s);",
+                       "        len = 32;\n    }\n    return f16_encode_rne(s);"),
+    "acc16_chunks_from_k_start": (
+        "int64_t len = K % 64 ? K % 64 : 64;   /* the first chunk */\n    while (k0 < K) {\n        double c = 0.0;\n        for (int64_t k = k0; k < k0 + len; ++k)",
+        "int64_t len = 64;   /* the first chunk */\n    while (k0 < K) {\n        double c = 0.0;\n        for (int64_t k = k0; k < k0 + len && k < K; ++k)"),
+    "acc16_chunk_rounded_first": ("s = g_lut[f16_encode_rne(s + c)];",
+                                  "s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];"),
+    "acc16_wide_running_sum": ("s = g_lut[f16_encode_rne(s + c)];", "s = s + c;"),
+    "acc16_dropped_first_chunk": ("        s = g_lut[f16_encode_rne(s + c)];\n        k0 += len;",
+                                  "        s = k0 ? g_lut[f16_encode_rne(s + c)] : 0.0;\n        k0 += len;"),
+    "acc16_wrong_sign": ("            c += g_lut[arow[k]] * g_lut[brow[k]];\n        s = g_lut",
+                         "            c -= g_lut[arow[k]] * g_lut[brow[k]];\n        s = g_lut"),
+    "acc16_b_row_index": ("out[i] = entry_acc16(A + m * K, B + n * K, K);",
+                          "out[i] = entry_acc16(A + m * K, B + ((n + 1) % N) * K, K);"),
 }
 
 
@@ -132,6 +150,17 @@ def _battery():
         lambda: fpins.test_f8_column_scales_integer_exact(True),
         lambda: fpins.test_f9_column_scales_brute_force(7, 131),
         lambda: fpins.test_f9_column_scales_brute_force(24, 132),
+        lambda: hpins.test_h1_stall_at_2048(1100, 2048),
+        lambda: hpins.test_h1_stall_at_2048(500, 1523),
+        hpins.test_h2_chunks_aligned_to_k_end,
+        hpins.test_h3_one_rounding_per_update,
+        lambda: hpins.test_h4_one_chunk_is_the_plain_product(33, 41),
+        lambda: hpins.test_h4_small_integers_are_exact(200),
+        lambda: hpins.test_h5_brute_force_exact(130, 51),
+        hpins.test_h5_brute_force_large_sums,
+        hpins.test_h6_symmetries,
+        hpins.test_h7_empty_overflow_and_sign,
+        hpins.test_entries_agree_with_full,
     ]
 
 
@@ -158,6 +187,11 @@ def _wrap(path: Path):
     lib.oracle_gemm_nt_f16_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_int]
     lib.oracle_gemm_nt_f16_ex.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_acc16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_nt_f16_acc16.restype = ctypes.c_int
+    lib.oracle_gemm_nt_f16_acc16_entries.argtypes = [p, p, i64, i64, i64, p, p, i64, p,
+                                                     ctypes.c_int]
+    lib.oracle_gemm_nt_f16_acc16_entries.restype = ctypes.c_int
     lib.oracle_bf16_decode.argtypes = [p, p, i64]
     lib.oracle_bf16_encode.argtypes = [p, p, i64]
     lib.oracle_gemm_nt_bf16.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int]

@@ -149,8 +149,8 @@ def gemm_nt_f16_entries(A: np.ndarray, B: np.ndarray, rows, cols,
 def gemm_nt_f16_acc16(A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
     """D = A * B^T with an fp16 running sum (page "如何用 Croqtile 一步步优化矩阵
     乘法内核", the f16 accumulator of its kernels): chunks of 64 consecutive k,
-    aligned to K's end, each added to the fp16 sum with one rounding.  fp16
-    bit patterns (uint16, M x N)."""
+    aligned to K's end; each chunk's sum is rounded to fp16 and added to the
+    fp16 sum with an fp16 addition.  fp16 bit patterns (uint16, M x N)."""
     a, b = _bits(A), _bits(B)
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
         raise ValueError(f"shapes {a.shape} and {b.shape} are not M x K and N x K")

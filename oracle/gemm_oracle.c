@@ -71,17 +71,18 @@
  * declares an f16 accumulator (section "内核 0：朴素版"), and its Hopper
  * kernels fill the matrix-unit accumulator as f16, which it notes takes
  * fewer registers (section "内核 2：Hopper TMA + WGMMA"; the tuned kernel of
- * section "内核 4：生产级调优" keeps it).  A matrix-unit update with an fp16
- * accumulator reads the fp16 partial sum, adds a group of products and
- * writes the result back in fp16.  Readings taken where the page is silent:
+ * section "内核 4：生产级调优" keeps it): the running sum is an fp16 value and
+ * every update of it is an fp16 addition.  Readings taken where the page is
+ * silent:
  *  - one update adds the products of 64 consecutive k (a chunk); the chunks
  *    tile [0, K) from its end, so when K is not a multiple of 64 the first
  *    chunk holds the K mod 64 leading terms;
- *  - an update is s <- fp16(s + sum over the chunk of A[m,k] * B[n,k]): the
- *    chunk's products and s are summed in fp64 and rounded once, to nearest
- *    with ties to even;
+ *  - the chunk's products are summed (in fp64) and the sum rounded to fp16,
+ *    then added to s with an fp16 addition: s <- fp16(s + fp16(chunk sum)),
+ *    each rounding to nearest with ties to even;
  *  - s starts at +0 and D[m,n] is the last s; K = 0 gives +0; an infinite
- *    or NaN s stays so (NaN as 0x7E00).
+ *    or NaN s stays so (NaN as 0x7E00).  A chunk sum that rounds to -0
+ *    adds as +0 + -0 = +0, so D is never -0.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no -ffast-math:
  * the sum must be evaluated exactly in the written order).
@@ -335,7 +336,8 @@ int oracle_gemm_nt_f16_ex(const uint16_t *A, const uint16_t *B, const uint16_t *
 /* ---- fp16 accumulation -------------------------------------------------- */
 
 /* One output entry with an fp16 running sum: chunks of 64 consecutive k,
- * aligned to K's end, each added to the sum with one rounding to fp16. */
+ * aligned to K's end; each chunk's sum, rounded to fp16, is added to the sum
+ * with an fp16 addition (the exact sum of two fp16 values, rounded once). */
 static uint16_t entry_acc16(const uint16_t *arow, const uint16_t *brow, int64_t K)
 {
     double s = 0.0;                       /* always an fp16 value */
@@ -345,7 +347,7 @@ static uint16_t entry_acc16(const uint16_t *arow, const uint16_t *brow, int64_t 
         double c = 0.0;
         for (int64_t k = k0; k < k0 + len; ++k)
             c += g_lut[arow[k]] * g_lut[brow[k]];
-        s = g_lut[f16_encode_rne(s + c)];
+        s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];
         k0 += len;
         len = 64;
     }

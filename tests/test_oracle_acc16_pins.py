@@ -5,22 +5,27 @@ Page "如何用 Croqtile 一步步优化矩阵乘法内核" keeps the running su
 (the f16 accumulator of its kernels, sections "内核 0：朴素版" and "内核 2：
 Hopper TMA + WGMMA").  The oracle's reading: s starts at +0; for each chunk of
 64 consecutive k, the chunks aligned to K's end (the first one holds the
-K mod 64 leading terms), s <- fp16(s + the chunk's sum of products), summed
-exactly and rounded once, to nearest with ties to even; D = s.
+K mod 64 leading terms), the chunk's exact sum of products is rounded to fp16
+and added to s with an fp16 addition, s <- fp16(s + fp16(chunk sum)), each
+rounding to nearest with ties to even; D = s.
 
   h1  closed form: one 1024 followed by chunks that each sum to 1 climbs by
       1 per chunk and stalls at 2048 (where 2049 is a tie that rounds to
       even), not at the exact sum
   h2  chunk alignment: with K = 65 the first chunk is k = 0 alone
-  h3  one rounding per update: a chunk summing to 0.5 + 2^-12 lifts 1024 to
-      1025 (rounding the chunk first would give a tie and stay at 1024)
+  h3  the chunk is rounded before it is added: a chunk summing to
+      0.5 + 2^-12 becomes 0.5 (a tie, to even) and leaves 1024 at 1024 (one
+      rounding of 1024.500244 would give 1025); a chunk summing to 2049
+      becomes 2048
   h4  one chunk (K <= 64) is the plain product, rounded once (the pinned
-      oracle_gemm_nt_f16); small integers whose partial sums stay within
+      oracle_gemm_nt_f16), except that a sum rounding to -0 gives +0 (the
+      fp16 addition +0 + -0); small integers whose partial sums stay within
       2048 give the exact integer result at any K
   h5  brute force: exact rational arithmetic with an independent fp16
       rounding, on tiny shapes with K around the chunk width
   h6  symmetries: D(-A, B) = -D(A, B), D(B, A) = D(A, B)^T
-  h7  K = 0 gives +0; overflow to infinity and its sign
+  h7  K = 0 gives +0, and so does a negative sum too small for fp16;
+      overflow to infinity and its sign
 
 None of these tests needs a GPU.
 """
@@ -57,7 +62,7 @@ def _exact_acc16(A: np.ndarray, B: np.ndarray) -> np.ndarray:
             k0, length = 0, (K % W) or W
             while k0 < K:
                 c = sum((ra[k] * rb[k] for k in range(k0, k0 + length)), Fraction(0))
-                s = nearest_f16(_value(s) + c)
+                s = nearest_f16(_value(s) + _value(nearest_f16(c)))
                 k0, length = k0 + length, W
             out[m, n] = s
     return out
@@ -101,14 +106,26 @@ def test_h2_chunks_aligned_to_k_end():
 
 
 # ------------------------------------------------------------------- h3 ---
-def test_h3_one_rounding_per_update():
+def test_h3_chunk_rounded_before_the_add():
     K = 2 * W
     A = np.zeros((1, K), dtype=np.float16)
     A[0, 0] = 1024.0
     A[0, W], A[0, W + 1] = 0.5, 2.0 ** -12
-    # 1024 + 0.500244140625 is above the midpoint 1024.5: 1025.  Rounding the
-    # chunk to fp16 first gives 0.5 (a tie, to even) and then 1024.5 -> 1024.
-    assert float(oracle.gemm_nt_f16_acc16(A, _ones_b(K)).view(np.float16)[0, 0]) == 1025.0
+    # the chunk 0.500244140625 rounds to 0.5 (a tie between 0.5 and
+    # 0.5 + 2^-11, to even), and 1024 + 0.5 is a tie that stays at 1024; one
+    # rounding of 1024 + 0.500244140625 would give 1025
+    assert float(oracle.gemm_nt_f16_acc16(A, _ones_b(K)).view(np.float16)[0, 0]) == 1024.0
+    # a single chunk summing to 2049 (1024 + 1025) rounds to 2048 (even)
+    A = np.zeros((1, W), dtype=np.float16)
+    A[0, 0], A[0, 1] = 1024.0, 1025.0
+    assert float(oracle.gemm_nt_f16_acc16(A, _ones_b(W)).view(np.float16)[0, 0]) == 2048.0
+    # s = 2050, then a chunk of 2049: rounded first it is 2048 and
+    # 2050 + 2048 = 4098 is a tie (step 4) that goes to 4096; one rounding of
+    # 2050 + 2049 = 4099 would give 4100
+    A = np.zeros((1, K), dtype=np.float16)
+    A[0, 0], A[0, 1] = 1024.0, 1026.0        # first chunk 2050
+    A[0, W], A[0, W + 1] = 1024.0, 1025.0    # second chunk 2049 -> 2048
+    assert float(oracle.gemm_nt_f16_acc16(A, _ones_b(K)).view(np.float16)[0, 0]) == 4096.0
     # each product is rounded with the rest of its chunk, not on its own:
     # 64 products of 2^-6 on top of 1024 give 1025, one at a time they vanish
     A = np.zeros((1, K), dtype=np.float16)
@@ -125,7 +142,9 @@ def test_h4_one_chunk_is_the_plain_product(K, seed):
     M, N = int(rng.integers(1, 9)), int(rng.integers(1, 9))
     A = wl.random_bits(seed * 100 + K, (M, K), finite_max=64.0)
     B = wl.random_bits(seed * 100 + K + 50, (N, K), finite_max=64.0)
-    assert np.array_equal(oracle.gemm_nt_f16_acc16(A, B), oracle.gemm_nt_f16(A, B))
+    plain = oracle.gemm_nt_f16(A, B)
+    plain[plain == 0x8000] = 0
+    assert np.array_equal(oracle.gemm_nt_f16_acc16(A, B), plain)
 
 
 @pytest.mark.parametrize("K", [65, 129, 200, 1000])
@@ -155,13 +174,13 @@ def test_h5_brute_force_exact(K, seed):
 
 
 def test_h5_brute_force_large_sums():
-    # integers 1..5 over 1000 terms (16 chunks): partial sums up to ~9000,
-    # far above 2048, where the fp16 running sum has a step of 2 to 8 and
-    # every update rounds
+    # integers 3..9 over 1000 terms (16 chunks): chunk sums around 2300,
+    # above 2048 where odd integers round, and partial sums up to ~36000,
+    # where the fp16 running sum has a step of 2 to 32 and every update rounds
     rng = np.random.default_rng(55)
     K = 1000
-    A = rng.integers(1, 6, size=(4, K)).astype(np.float16)
-    B = rng.integers(1, 6, size=(4, K)).astype(np.float16)
+    A = rng.integers(3, 10, size=(4, K)).astype(np.float16)
+    B = rng.integers(3, 10, size=(4, K)).astype(np.float16)
     got = oracle.gemm_nt_f16_acc16(A, B)
     assert np.array_equal(got, _exact_acc16(A, B))
     # and it is not the once-rounded exact sum everywhere
@@ -183,6 +202,11 @@ def test_h6_symmetries():
 def test_h7_empty_overflow_and_sign():
     z = oracle.gemm_nt_f16_acc16(np.zeros((3, 0), np.float16), np.zeros((2, 0), np.float16))
     assert z.shape == (3, 2) and np.all(z == 0)
+    # -2^-26 rounds to -0 as a chunk; +0 + -0 is +0 (the plain product is -0)
+    A = np.full((1, 1), -(2.0 ** -12), dtype=np.float16)
+    B = np.full((1, 1), 2.0 ** -14, dtype=np.float16)
+    assert oracle.gemm_nt_f16(A, B)[0, 0] == 0x8000
+    assert oracle.gemm_nt_f16_acc16(A, B)[0, 0] == 0
     A = np.full((2, 256), 16.0, dtype=np.float16)
     # chunks of 16384: 16384, 32768, 49152, then 65536 -> infinity
     assert np.all(oracle.gemm_nt_f16_acc16(A, A) == 0x7C00)

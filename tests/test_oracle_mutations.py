@@ -9,8 +9,8 @@ epilogue; in FP8 a wrong exponent bias, flushed subnormals, the other NaN
 convention, saturation in place of infinity, swapped formats, a rounding
 before the scale; with per-channel scales a scale per row, a dropped
 activation scale, a rounding before the scale; with an fp16 running sum a
-chunk of 32, chunks counted from k = 0, the chunk rounded before it is added,
-a wide running sum, a dropped chunk, a wrong sign, a wrong row of B), compiles the copy with gcc, points the oracle wrapper at it
+chunk of 32, chunks counted from k = 0, one rounding per update instead of
+the chunk's and the addition's, a wide running sum, a dropped chunk, a wrong sign, a wrong row of B), compiles the copy with gcc, points the oracle wrapper at it
 and runs the pin battery.  At least one pin must fail for every planted mistake.  All
 of this runs on the CPU; the real oracle is not modified.
 """
@@ -94,11 +94,12 @@ MUTATIONS = {
     "acc16_chunks_from_k_start": (
         "int64_t len = K % 64 ? K % 64 : 64;   /* the first chunk */\n    while (k0 < K) {\n        double c = 0.0;\n        for (int64_t k = k0; k < k0 + len; ++k)",
         "int64_t len = 64;   /* the first chunk */\n    while (k0 < K) {\n        double c = 0.0;\n        for (int64_t k = k0; k < k0 + len && k < K; ++k)"),
-    "acc16_chunk_rounded_first": ("s = g_lut[f16_encode_rne(s + c)];",
-                                  "s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];"),
-    "acc16_wide_running_sum": ("s = g_lut[f16_encode_rne(s + c)];", "s = s + c;"),
-    "acc16_dropped_first_chunk": ("        s = g_lut[f16_encode_rne(s + c)];\n        k0 += len;",
-                                  "        s = k0 ? g_lut[f16_encode_rne(s + c)] : 0.0;\n        k0 += len;"),
+    "acc16_one_rounding_per_update": ("s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];",
+                                      "s = g_lut[f16_encode_rne(s + c)];"),
+    "acc16_wide_running_sum": ("s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];",
+                               "s = s + c;"),
+    "acc16_dropped_first_chunk": ("        s = g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])];\n        k0 += len;",
+                                  "        s = k0 ? g_lut[f16_encode_rne(s + g_lut[f16_encode_rne(c)])] : 0.0;\n        k0 += len;"),
     "acc16_wrong_sign": ("            c += g_lut[arow[k]] * g_lut[brow[k]];\n        s = g_lut",
                          "            c -= g_lut[arow[k]] * g_lut[brow[k]];\n        s = g_lut"),
     "acc16_b_row_index": ("out[i] = entry_acc16(A + m * K, B + n * K, K);",
@@ -153,7 +154,7 @@ def _battery():
         lambda: hpins.test_h1_stall_at_2048(1100, 2048),
         lambda: hpins.test_h1_stall_at_2048(500, 1523),
         hpins.test_h2_chunks_aligned_to_k_end,
-        hpins.test_h3_one_rounding_per_update,
+        hpins.test_h3_chunk_rounded_before_the_add,
         lambda: hpins.test_h4_one_chunk_is_the_plain_product(33, 41),
         lambda: hpins.test_h4_small_integers_are_exact(200),
         lambda: hpins.test_h5_brute_force_exact(130, 51),

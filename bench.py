@@ -1,7 +1,7 @@
 """Throughput of the NT GEMM library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--path f16|f16_ex|f16_ws|bf16|fp8|fp8_cs]
+                    [--path f16|f16_ex|f16_ws|f16_acc16|bf16|fp8|fp8_cs]
 
 A step is one call of the chosen entry point (the whole hot path): by
 default gemm_nt_f16 on the 8192 x 8192 x 8192 workload, A [M,K] and B [N,K]
@@ -47,6 +47,7 @@ PATH_SOURCES = {
     "f16": ["gemm_kernels.h", "gemm_nt_f16.hip"],
     "f16_ws": ["gemm_kernels.h", "gemm_nt_f16.hip"],
     "f16_ex": ["gemm_kernels.h", "gemm_nt_f16_ex.hip"],
+    "f16_acc16": ["gemm_kernels.h", "gemm_nt_f16_acc16.hip"],
     "bf16": ["gemm_kernels.h", "gemm_nt_bf16.hip"],
     "fp8": ["gemm_kernels.h", "gemm_fp8.h", "gemm_nt_fp8.hip"],
     "fp8_cs": ["gemm_kernels.h", "gemm_fp8.h", "gemm_nt_fp8.hip"],
@@ -308,7 +309,7 @@ def setup_path(path, w, torch, dev, binding, wl) -> dict:
     keep = [dD]              # device buffers the steps use stay alive with P
     P = {"keep": keep, "peak": PEAK_FP16_TFLOPS, "bytes": algorithmic_bytes(M, N, K),
          "dtype": "fp16", "inputs": fp16_inputs, "tile": list(binding.gemm_nt_f16_tile(M, N, K)[:3])}
-    if path in ("f16", "f16_ws", "f16_ex"):
+    if path in ("f16", "f16_ws", "f16_ex", "f16_acc16"):
         A, B = wl.random_inputs(w)
         dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
         pa, pb = dA.data_ptr(), dB.data_ptr()
@@ -358,6 +359,14 @@ def setup_path(path, w, torch, dev, binding, wl) -> dict:
                  cpu_rows=lambda r0, r1, t: oracle.gemm_nt_f16(A[r0:r1], B, threads=t))
         P["inputs"] = dict(fp16_inputs, workspace_bytes=need, stream_k_tiles=skt,
                            workgroups=wg)
+    elif path == "f16_acc16":
+        import oracle
+        bm, bn, lb = binding.gemm_nt_f16_acc16_kernel(pa, pb, M, N, K)
+        P.update(entry="gemm_nt_f16_acc16", tile=[bm, bn, 64], accumulate="fp16 (64-wide chunks)",
+                 metric=f"fp16 GEMM TFLOPS (2MNK/t) with an fp16 running sum, {M}x{N}x{K}",
+                 step=lambda: check(binding.gemm_nt_f16_acc16(pa, pb, pd, M, N, K, sptr),
+                                    "gemm_nt_f16_acc16"),
+                 cpu_rows=lambda r0, r1, t: oracle.gemm_nt_f16_acc16(A[r0:r1], B, threads=t))
     elif path == "f16_ex":
         import oracle
         rng = np.random.default_rng(w.seeds[0] + 77)
@@ -589,7 +598,8 @@ def run(args, sampler) -> int:
         "config": {
             "workload": name, "M": M, "N": N, "K": K, "entry_point": P["entry"],
             **P["inputs"],
-            "accumulate": "fp32", "layout": "A MxK, B NxK (D = A B^T), row-major",
+            "accumulate": P.get("accumulate", "fp32"),
+            "layout": "A MxK, B NxK (D = A B^T), row-major",
             "tile": P["tile"],
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

@@ -24,7 +24,8 @@ GEMM_FP8_E5M2 = 1
 EXPORTS = ("gemm_nt_f16", "gemm_nt_f16_strerror", "gemm_nt_f16_tile", "gemm_nt_f16_tile_coord",
            "gemm_nt_bf16", "gemm_nt_f16_ex", "gemm_nt_f16_ws", "gemm_nt_f16_ws_size", "gemm_nt_f16_ws_tile",
            "gemm_nt_f16_ws_items", "gemm_nt_fp8", "gemm_nt_fp8_cs", "gemm_nt_fp8_tile",
-           "gemm_nt_f16_kernel", "gemm_nt_f16_ws_noalloc")
+           "gemm_nt_f16_kernel", "gemm_nt_f16_ws_noalloc", "gemm_nt_f16_acc16",
+           "gemm_nt_f16_acc16_kernel")
 
 
 class GemmError(RuntimeError):
@@ -66,6 +67,10 @@ def lib():
     L.gemm_nt_f16_kernel.restype = ctypes.c_int
     L.gemm_nt_f16_tile_coord.argtypes = [i64, i64, i64, lp, lp]
     L.gemm_nt_f16_tile_coord.restype = ctypes.c_int
+    L.gemm_nt_f16_acc16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_nt_f16_acc16.restype = ctypes.c_int
+    L.gemm_nt_f16_acc16_kernel.argtypes = [vp, vp, i64, i64, i64, ip, ip, ip]
+    L.gemm_nt_f16_acc16_kernel.restype = ctypes.c_int
     L.gemm_nt_bf16.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     L.gemm_nt_bf16.restype = ctypes.c_int
     L.gemm_nt_f16_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float,
@@ -124,6 +129,22 @@ def gemm_nt_f16_kernel(A: int, B: int, D: int, M: int, N: int, K: int):
     if rc != GEMM_OK:
         raise GemmError(rc, "gemm_nt_f16_kernel")
     return bm.value, bn.value, lb.value, st.value
+
+
+def gemm_nt_f16_acc16(A: int, B: int, D: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    """Raw call of the fp16-accumulating product; returns the C return code."""
+    return lib().gemm_nt_f16_acc16(A or None, B or None, D or None, M, N, K, stream or None)
+
+
+def gemm_nt_f16_acc16_kernel(A: int, B: int, M: int, N: int, K: int):
+    """(BM, BN, load_bytes) of the kernel a gemm_nt_f16_acc16 call with these
+    device addresses and sizes takes (host-only, nothing is read)."""
+    bm, bn, lb = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().gemm_nt_f16_acc16_kernel(A or None, B or None, M, N, K, ctypes.byref(bm),
+                                        ctypes.byref(bn), ctypes.byref(lb))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_nt_f16_acc16_kernel")
+    return bm.value, bn.value, lb.value
 
 
 def gemm_nt_f16_tile_coord(wg: int, tiles_m: int, tiles_n: int):

@@ -12,7 +12,8 @@ CSRC = PKG / "csrc"
 # One translation unit per entry-point family; they share gemm_kernels.h and
 # compile in parallel.
 SOURCES = [CSRC / "gemm_nt_f16.hip", CSRC / "gemm_nt_f16_ex.hip", CSRC / "gemm_nt_bf16.hip",
-           CSRC / "gemm_nt_fp8.hip", CSRC / "gemm_nt_fp8_b5.hip", CSRC / "gemm_nt_f16_noalloc.hip"]
+           CSRC / "gemm_nt_fp8.hip", CSRC / "gemm_nt_fp8_b5.hip", CSRC / "gemm_nt_f16_noalloc.hip",
+           CSRC / "gemm_nt_f16_acc16.hip"]
 HEADERS = [CSRC / "gemm_kernels.h", CSRC / "gemm_fp8.h", ROOT / "include" / "gemm_nt_f16.h"]
 LIB = PKG / "libgemm18.so"
 

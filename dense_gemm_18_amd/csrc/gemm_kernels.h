@@ -124,6 +124,29 @@ __device__ __forceinline__ f32x4 mfma_f8(i32x8 b, i32x8 a, f32x4 c)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, fb, fa, 0, 0, 0, 0);
 }
 
+// fp16 accumulation (page "如何用 Croqtile 一步步优化矩阵乘法内核": an f16
+// accumulator, sections "内核 0：朴素版" and "内核 2：Hopper TMA + WGMMA"):
+// one 64-wide K-step of a 16x16 block.  CDNA4's MFMAs accumulate in fp32
+// only: the step's two 16x16x32 MFMAs sum its 64 products in fp32 from +0,
+// the sum is rounded to fp16 (to nearest even) and added to the fp16
+// running sum s with a packed fp16 addition, s <- fp16(s + fp16(step sum)).
+// Four VALU instructions per block and step (two conversions of pairs, two
+// packed adds); widening s into the MFMA's fp32 addend instead would take
+// six, and with one wave per SIMD already issuing the MFMAs the VALU issue
+// slots are what bounds this kernel.  b and a hold the lane's two 8-element
+// K groups of the step (the first for the step's first 32 K).
+__device__ __forceinline__ f16x4 mma_acc16(i32x8 b, i32x8 a, f16x4 s)
+{
+    const f16x8 b0 = __builtin_bit_cast(f16x8, __builtin_shufflevector(b, b, 0, 1, 2, 3));
+    const f16x8 b1 = __builtin_bit_cast(f16x8, __builtin_shufflevector(b, b, 4, 5, 6, 7));
+    const f16x8 a0 = __builtin_bit_cast(f16x8, __builtin_shufflevector(a, a, 0, 1, 2, 3));
+    const f16x8 a1 = __builtin_bit_cast(f16x8, __builtin_shufflevector(a, a, 4, 5, 6, 7));
+    f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, a0, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                     0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, a1, c, 0, 0, 0);
+    return s + __builtin_convertvector(c, f16x4);
+}
+
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
 constexpr int kGroupM = 4;         // tile rows per rasterisation group
 constexpr int kXcds = 8;           // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -737,19 +760,29 @@ constexpr int kSpinLimit = 1 << 24;
 // a K-step is one 128-byte LDS row, BKU units.  NT (direct-to-LDS loads):
 // bit 0 loads A, bit 1 loads B with the non-temporal cache policy, set when
 // that operand is read exactly once per call (a single column or row of
-// tiles), so that streaming it does not allocate in the caches.
-template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0, int UB = 2, int NT = 0>
+// tiles), so that streaming it does not allocate in the caches.  H16: the
+// running sum is fp16 (mma_acc16), one update per K-step and block.
+template <class C, bool KTAIL, bool SK, bool EPI, bool BF, int F8 = 0, int UB = 2, int NT = 0,
+          bool H16 = false>
 __global__ void __launch_bounds__(C::THREADS, 1)
 gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                    const typename Elem<BF>::T *__restrict__ B, typename Elem<BF>::T *__restrict__ D,
                    int M, int N, int K, int tiles_m, int tiles_n, int vec_store, SkPlan sk,
                    EpiArg<EPI> epi)
 {
-    using X8 = typename std::conditional<F8 != 0, i32x8, typename Elem<BF>::x8>::type;
-    static_assert(F8 == 0 || (!BF && !SK && !C::SPLIT && C::MF == 16 && C::BK == 64 &&
-                              C::SLICES == 2 && C::NSTAGE % 2 == 0 && C::TM % 2 == 0),
-                  "FP8: 16x16 blocks, 128-byte rows, an even stage ring, loads after the barrier");
-    static_assert(F8 == 0 || !C::B3, "FP8: one ring for A and B");
+    // WIDE: a fragment holds the lane's part of a whole K-step (32 bytes),
+    // and each block takes all of a step's products at once: FP8 (one f8f6f4
+    // MFMA per step) and fp16 accumulation (both 16x16x32 MFMAs of the step
+    // back to back, before the fp16 rounding).  The two slices of a step
+    // then split the blocks by rows instead of the K-step by halves.
+    constexpr bool WIDE = F8 != 0 || H16;
+    using X8 = typename std::conditional<WIDE, i32x8, typename Elem<BF>::x8>::type;
+    static_assert(!WIDE || (!BF && !SK && !C::SPLIT && C::MF == 16 && C::BK == 64 &&
+                            C::SLICES == 2 && C::NSTAGE % 2 == 0 && C::TM % 2 == 0),
+                  "whole-step fragments: 16x16 blocks, 128-byte rows, an even stage ring, "
+                  "loads after the barrier");
+    static_assert(!WIDE || !C::B3, "whole-step fragments: one ring for A and B");
+    static_assert(!H16 || (F8 == 0 && !EPI && UB == 2), "fp16 accumulation: fp16 operands");
     static_assert(UB == 2 || (UB == 1 && F8 != 0 && C::REG), "byte units: FP8, register staging");
     constexpr int BKU = C::ROW_BYTES / UB;      // K units per step
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -916,7 +949,17 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                                                               soff);
     };
 
-    typename C::acc_t acc[C::TM][C::TN];
+    // Accumulators: fp32 blocks, or (H16) the fp16 running sums, four per
+    // lane and 16x16 block in the fp32 layout.
+    using AccT = typename std::conditional<H16, f16x4, typename C::acc_t>::type;
+    AccT acc[C::TM][C::TN];
+    // Block (i, j) in fp32 for the epilogue (exact for fp16 sums).
+    auto accf = [&](int i, int j) G18_INLINE {
+        if constexpr (H16)
+            return __builtin_convertvector(acc[i][j], f32x4);
+        else
+            return acc[i][j];
+    };
 
     // Fragments of one K slice (16 wide for 32x32x16, 32 wide for 16x16x32):
     // lane l holds row l % MF of each MF-row block and K chunk
@@ -952,9 +995,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         constexpr int S = decltype(sc)::value, t = decltype(tc)::value, q = decltype(qc)::value;
         constexpr int off = C::MF * (q < C::TM ? q : q - C::TM) * C::ROW_BYTES;
         X8 &f = frag(setc, qc);
-        if constexpr (F8) {
+        if constexpr (WIDE) {
             // 32 bytes: the chunks of both 16-bit slices (t is always 0)
-            static_assert(t == 0, "an FP8 fragment spans the whole K-step");
+            static_assert(t == 0, "a whole-step fragment spans the K-step");
             const uint32_t p0 = q < C::TM ? a_addr[S][0] : b_addr[S][0];
             const uint32_t p1 = q < C::TM ? a_addr[S][1] : b_addr[S][1];
             const u32x4 lo = *(const u32x4 *)(smem + p0 + off);
@@ -968,18 +1011,19 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 
     constexpr int NM = C::TM * C::TN, NR = C::TM + C::TN;
     // MFMAs per slice: all blocks, or (FP8) half of the block rows.
-    constexpr int NMS = F8 ? NM / 2 : NM;
+    constexpr int NMS = WIDE ? NM / 2 : NM;
     constexpr int LHALF = C::LPS / 2;
     // Loads issued in one slice: half a step's or a whole step's (register
     // staging: a step's writes and reloads over all its slices).
-    constexpr int LSL = (C::REG && !F8) ? C::LPS / C::SLICES
+    constexpr int LSL = (C::REG && !WIDE) ? C::LPS / C::SLICES
                         : C::B3           ? C::A_LOADS
                                           : (C::SPLIT ? LHALF : C::LPS);
     // The LSL loads of a slice are spread evenly over its NMS MFMAs (load l
     // after MFMA floor(l NMS / LSL)); RPG fragment reads follow each MFMA.
     constexpr int RPG = (NR + NM - 1) / NM;
     static_assert(C::LPS % 2 == 0, "loads split evenly over the slices that issue them");
-    // FP8 read schedule, by the slice's MFMA index p: the next step's B
+    // Whole-step read schedule (FP8, fp16 accumulation), by the slice's MFMA
+    // index p: the next step's B
     // blocks (double-buffered) during the first slice, B block j after
     // p = j * BSTEP; its A blocks (single-buffered) during the second: those
     // of the first half-rows (dead since the first slice) after p = 0, 1, ...,
@@ -993,34 +1037,38 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // this issue order: with one wavefront per SIMD nothing else fills an
     // issue gap, and the four waves share the CU's load pipe (about 25 cycles
     // per 1 KB load), so loads are spread evenly rather than issued in a burst.
-    // FP8 fragments are twice as large and a K-step's are read in its second
-    // slice only; the A fragments are not double buffered (see the FP8 read
-    // schedule above), which keeps the 256 x 256 tile within the registers.
-    // h: (FP8) which half of the block rows this slice multiplies.
+    // Whole-step fragments are twice as large and a K-step's are read in its
+    // second slice only; the A fragments are not double buffered (see the
+    // whole-step read schedule above), which keeps the 256 x 256 FP8 tile
+    // within the registers.
+    // h: (whole-step fragments) which half of the block rows this slice
+    // multiplies.
     // cur, nxt: fragment sets (integral constants) multiplied and read.
     auto slice = [&](auto cur, auto nxt,
                      auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
                      auto l0, auto hc) G18_INLINE {
         static_for<0, NMS>([&](auto pc) G18_INLINE {
             constexpr int p = decltype(pc)::value;
-            constexpr int q = p + (F8 ? decltype(hc)::value * NMS : 0);
+            constexpr int q = p + (WIDE ? decltype(hc)::value * NMS : 0);
             constexpr int i = q / C::TN, j = q % C::TN;
             using QA = std::integral_constant<int, i>;
             using QB = std::integral_constant<int, C::TM + j>;
             if constexpr (F8 != 0)
                 acc[i][j] = mfma_f8<F8>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
+            else if constexpr (H16)
+                acc[i][j] = mma_acc16(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             else if constexpr (C::MF == 32)
                 acc[i][j] = mfma32<BF>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             else
                 acc[i][j] = mfma16<BF>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
-            if constexpr (decltype(do_read)::value && F8 != 0 && decltype(hc)::value == 0) {
+            if constexpr (decltype(do_read)::value && WIDE && decltype(hc)::value == 0) {
                 static_for<0, C::TN>([&](auto jc) G18_INLINE {
                     constexpr int jb = decltype(jc)::value;
                     constexpr int pb = jb * BSTEP < NMS ? jb * BSTEP : NMS - 1;
                     if constexpr (p == pb)
                         read_one(nxt, rs, rt, std::integral_constant<int, C::TM + jb>{});
                 });
-            } else if constexpr (decltype(do_read)::value && F8 != 0) {
+            } else if constexpr (decltype(do_read)::value && WIDE) {
                 if constexpr (p < HR)
                     read_one(nxt, rs, rt, std::integral_constant<int, p>{});
                 if constexpr (j == C::TN - 1)
@@ -1069,10 +1117,11 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         using SN_ = std::integral_constant<int, (S + 1) % C::PERIOD>;               // step u+1
         using SR_ = std::integral_constant<int, (S + C::NSTAGE) % C::PERIOD>;       // step u+NSTAGE
         using SB_ = std::integral_constant<int, (S + C::NSB - 1) % C::PERIOD>;      // step u+NSB-1
-        if constexpr (F8 != 0) {
-            // FP8: the barrier comes first (step u + 1 landed, step u's stage
-            // free); the first slice refills the stage with step u + NSTAGE
-            // and reads step u + 1's B blocks, the second reads its A blocks.
+        if constexpr (WIDE) {
+            // Whole-step fragments (FP8, fp16 accumulation): the barrier
+            // comes first (step u + 1 landed, step u's stage free); the first
+            // slice refills the stage with step u + NSTAGE and reads step
+            // u + 1's B blocks, the second reads its A blocks.
             // LDS reads and DMA writes are then spread over the whole step,
             // and each refill still has the step's second slice to land.
             // Both slices multiply fragment set S & 1 (an even ring).
@@ -1149,7 +1198,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             if (staged) {
                 lds_barrier();
                 char *stage = smem + wave * St::BYTES;
-                auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
+                auto get = [&](int i, int j) G18_INLINE { return accf(i, j); };
                 if constexpr (EPI) {     // FP8: the scale alone, or per-column scales
                     if (epi.col_scale)
                         store_blocks16_epi<C::TM, C::TN, decltype(get), false, true, false, true>(
@@ -1166,7 +1215,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             }
         }
         if constexpr (EPI) {
-            auto get = [&](int i, int j) G18_INLINE { return acc[i][j]; };
+            auto get = [&](int i, int j) G18_INLINE { return accf(i, j); };
             if constexpr (C::MF == 32)
                 store_blocks<C::TM, C::TN>(get, D, M, N, mb, nb, lane, vec_store,
                                            EpiFin{epi, N, vec_store});
@@ -1182,6 +1231,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             }
         } else if constexpr (C::MF == 32) {
             store_acc<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
+        } else if constexpr (H16) {
+            store_blocks16<C::TM, C::TN>(accf, D, M, N, mb, nb, lane, vec_store);
         } else {
             store_acc16<C::TM, C::TN>(acc, D, M, N, mb, nb, lane, vec_store);
         }
@@ -1255,7 +1306,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // writes NaN instead.
     auto store_ok = [&](bool ok) G18_INLINE {
         auto get = [&](int bi, int bj) G18_INLINE {
-            return ok ? acc[bi][bj] : typename C::acc_t{} + __builtin_nanf("");
+            return ok ? accf(bi, bj) : typename C::acc_t{} + __builtin_nanf("");
         };
         if constexpr (C::MF == 32)
             store_blocks<C::TM, C::TN>(get, D, M, N, m0 + wm * C::WTM, n0 + wn * C::WTN, lane,
@@ -1296,7 +1347,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = typename C::acc_t{};
+            acc[i][j] = AccT{};
 
     // Prologue: steps 0 .. NSTAGE-2 and, with split loads, the first half of
     // step NSTAGE-1 (its second half is issued by step 0's first slice, like

@@ -111,6 +111,19 @@ def integer_free(seed: int, M: int, N: int, K: int, lo: int = -2, hi: int = 2):
     return A, B
 
 
+def coarse_uniform(seed: int, M: int, N: int, K: int, step: float = 2.0 ** -6,
+                   lim: float = 2.0):
+    """Free-shape inputs uniform over the multiples of ``step`` in
+    [-lim, lim] (both exact in fp16).  With the defaults every product is a
+    multiple of 2^-12 below 4 in magnitude, so any sum of 64 of them has at
+    most 20 significant bits and is exact in fp32, whatever the order."""
+    rng = np.random.default_rng(seed)
+    n = int(round(lim / step))
+    A = (rng.integers(-n, n + 1, size=(M, K)) * step).astype(np.float16)
+    B = (rng.integers(-n, n + 1, size=(N, K)) * step).astype(np.float16)
+    return A, B
+
+
 def random_bits(seed: int, shape, finite_max: float | None = None) -> np.ndarray:
     """Uniformly random fp16 bit patterns over all finite values (subnormals,
     zeros and +-65504 included); optionally restricted to |x| <= finite_max."""

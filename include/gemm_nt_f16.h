@@ -82,6 +82,37 @@ int gemm_nt_f16(const void *A, const void *B, void *D,
 int gemm_nt_bf16(const void *A, const void *B, void *D,
                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/*
+ * The fp16 product with an fp16 running sum instead of fp32 (the f16
+ * accumulator of page "如何用 Croqtile 一步步优化矩阵乘法内核", sections
+ * "内核 0：朴素版" and "内核 2：Hopper TMA + WGMMA", which notes that it takes
+ * fewer registers):
+ *
+ *     s = +0;  for each chunk c of 64 consecutive k (the chunks aligned to
+ *     K's end, so the first holds the K mod 64 leading terms when K is not a
+ *     multiple of 64):  s = fp16(s + fp16(sum_{k in c} A[m,k] * B[n,k]));
+ *     D[m,n] = s
+ *
+ * Each chunk's products are summed in fp32 by the matrix unit, the sum is
+ * rounded to fp16 and added to s with an fp16 addition (both roundings to
+ * nearest even), so partial sums above 2048 lose integer precision and
+ * errors grow with the number of chunks.  D is never -0.
+ * Arguments, layout, ownership, degenerate sizes and errors exactly as
+ * gemm_nt_f16.
+ */
+int gemm_nt_f16_acc16(const void *A, const void *B, void *D,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * Host-only introspection of gemm_nt_f16_acc16: the output tile (*bm x *bn)
+ * and load mode (*lbytes: 16 = 16-byte direct-to-LDS loads, 1 =
+ * register-staged chunks) a call with these pointers and sizes runs.
+ * A and B are only inspected for alignment, never dereferenced.  Returns
+ * GEMM_OK, or GEMM_EINVAL for a negative size or a NULL output pointer.
+ */
+int gemm_nt_f16_acc16_kernel(const void *A, const void *B, int64_t M, int64_t N, int64_t K,
+                             int *bm, int *bn, int *lbytes);
+
 /* FP8 operand formats (OCP 8-bit floating point). */
 #define GEMM_FP8_E4M3 0  /* 1 sign, 4 exponent (bias 7), 3 fraction bits; S.1111.111
                             is NaN; no infinities; largest finite 448            */

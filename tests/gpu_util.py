@@ -49,11 +49,12 @@ def to_dev(x: np.ndarray, misalign_elems: int = 0):
 
 
 def run_gemm(A: np.ndarray, B: np.ndarray, *, a_off: int = 0, b_off: int = 0, d_off: int = 0,
-             check_canary: bool = True, repeat: int = 1) -> np.ndarray:
+             check_canary: bool = True, repeat: int = 1, acc16: bool = False) -> np.ndarray:
     """D = A B^T on the GPU through the C ABI; returns fp16 bit patterns.
 
     D lives inside a buffer with GUARD canary elements on both sides; the
-    canaries must survive.  `*_off` shift operands by whole fp16 elements."""
+    canaries must survive.  `*_off` shift operands by whole fp16 elements.
+    acc16: through gemm_nt_f16_acc16 (fp16 running sum) instead."""
     import torch
     from dense_gemm_18_amd import binding
 
@@ -67,8 +68,9 @@ def run_gemm(A: np.ndarray, B: np.ndarray, *, a_off: int = 0, b_off: int = 0, d_
                       device=dev)
     dptr = dbuf.data_ptr() + 2 * (GUARD + d_off)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    fn = binding.gemm_nt_f16_acc16 if acc16 else binding.gemm_nt_f16
     for _ in range(repeat):
-        rc = binding.gemm_nt_f16(dA.data_ptr(), dB.data_ptr(), dptr, M, N, K, stream)
+        rc = fn(dA.data_ptr(), dB.data_ptr(), dptr, M, N, K, stream)
         assert rc == binding.GEMM_OK, binding.gemm_nt_f16_strerror(rc)
     torch.cuda.synchronize(dev)
     host = dbuf.cpu().numpy().view(np.uint16)

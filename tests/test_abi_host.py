@@ -289,3 +289,28 @@ def test_skinny_tiles(M, N, K, tile):
     bm, bn, _, wg = binding.gemm_nt_f16_tile(M, N, K)
     assert (bm, bn) == tile
     assert wg == -(-M // bm) * -(-N // bn)
+
+
+@pytest.mark.parametrize("M,N,K,offs,want", [
+    (8192, 8192, 8192, (0, 0), (256, 256, 16)),      # 8 waves of 128 x 64
+    (3000, 5000, 2048, (0, 0), (256, 256, 16)),      # one wave of 240 tiles
+    (2048, 2048, 2048, (0, 0), (128, 128, 16)),      # 256 tiles, two per CU
+    (1024, 1024, 1024, (0, 0), (128, 128, 16)),
+    (8192, 8192, 8191, (0, 0), (128, 128, 1)),       # register staging: 128 x 128
+    (8192, 8192, 8192, (2, 0), (128, 128, 1)),       # A 2-byte aligned
+    (64, 16384, 8192, (0, 0), (64, 64, 16)),         # skinny
+    (16384, 40, 8192, (0, 4), (64, 64, 1)),
+])
+def test_acc16_kernel_introspection(M, N, K, offs, want):
+    a, b = FAKE + offs[0], FAKE + 0x4000000 + offs[1]
+    assert binding.gemm_nt_f16_acc16_kernel(a, b, M, N, K) == want
+
+
+def test_acc16_rejects_bad_arguments_before_any_hip_call():
+    assert binding.gemm_nt_f16_acc16(FAKE, FAKE + 32, FAKE, 4, 4, 2, 0) == binding.GEMM_EINVAL
+    assert binding.gemm_nt_f16_acc16(FAKE, FAKE, FAKE + 1, 1, 1, 1, 0) == binding.GEMM_EINVAL
+    assert binding.gemm_nt_f16_acc16(FAKE, FAKE, FAKE, -1, 1, 1, 0) == binding.GEMM_EINVAL
+    assert binding.gemm_nt_f16_acc16(FAKE, FAKE, FAKE, 2, 2, binding.GEMM_MAX_K + 1, 0) == \
+        binding.GEMM_EINVAL
+    with pytest.raises(binding.GemmError):
+        binding.gemm_nt_f16_acc16_kernel(FAKE, FAKE, -1, 4, 4)

@@ -34,7 +34,8 @@ def test_tflops_and_bytes():
 def test_source_hash_ignores_comments_only():
     h = bench.kernel_source_hash("f16")
     assert len(h) == 16 and h == bench.kernel_source_hash("f16")
-    assert set(bench.PATH_SOURCES) == {"f16", "f16_ws", "f16_ex", "bf16", "fp8", "fp8_cs"}
+    assert set(bench.PATH_SOURCES) == {"f16", "f16_ws", "f16_ex", "f16_acc16", "bf16", "fp8",
+                                       "fp8_cs"}
     for files in bench.PATH_SOURCES.values():
         for f in files:
             assert (bench.CSRC / f).exists(), f

@@ -140,10 +140,11 @@ class ClockSampler:
     touches the GPU and stopped (its process group) once the GPU work is
     done.  A reader thread stamps each line with the time it arrived, so the
     samples that fall inside the loaded part of the run can be picked out.
-    The power limit comes from `amd-smi static --limit`, run first by the
-    same child."""
+    The power cap comes from `rocm-smi --showmaxpower` (amd-smi's static
+    limit query is not offered on a guest), run first by the same child."""
 
-    CMD = "amd-smi static -g 0 --limit; echo __METRIC__; amd-smi metric -g 0 -c -p -w 1"
+    CMD = ("rocm-smi -d 0 --showmaxpower --json; echo __METRIC__; "
+           "amd-smi metric -g 0 -c -p -w 1")
 
     def __init__(self):
         import subprocess
@@ -192,6 +193,9 @@ class ClockSampler:
                 in_metric = True
                 continue
             if not in_metric:
+                m = re.search(r'Max Graphics Package Power \(W\)"?\s*:\s*"?([0-9.]+)', s)
+                if m:
+                    limits["max_graphics_package_power"] = float(m.group(1))
                 m = re.match(r"^(PPT\d+):", s)
                 if m:
                     ppt = m.group(1)
@@ -239,8 +243,8 @@ class ClockSampler:
             rocm = Path("/opt/rocm/.info/version").read_text().strip()
         except OSError:
             pass
-        out = {"source": "amd-smi metric -g 0 -c -p -w 1, a child process started before the "
-                         "GPU was first used", "rocm": rocm}
+        out = {"source": "amd-smi metric -g 0 -c -p -w 1 (and rocm-smi --showmaxpower), a child "
+                         "process started before the GPU was first used", "rocm": rocm}
         if self.error:
             out["error"] = self.error
             return out

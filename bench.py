@@ -636,6 +636,14 @@ def run(args, sampler) -> int:
         torch.cuda.synchronize(dev)
         out["context_torch_linear_tflops"] = round(
             tflops(M, N, K, ts[0].elapsed_time(ts[1]) / args.steps / 1e3), 2)
+    if name == wl.HEADLINE and path in ("f16", "f16_acc16"):
+        # the pages' own figures for this workload, on other hardware:
+        # context, not a reference (page 1, "如何用 Croqtile 一步步优化矩阵乘法
+        # 内核", sections "性能一览" and "SOTA 对比"; its tuned kernel
+        # accumulates in fp16)
+        out["context_published"] = {
+            "hardware": "NVIDIA H800 PCIe", "cublas_torch_mm_tflops": 447.5,
+            "tuned_kernel_fp16_accumulate_tflops": 489.9}
     if sampler is not None:
         sampler.stop()
         # samples from 1 s into the load (the clock settles) to the end of the

@@ -9,8 +9,9 @@
 // NT layout follow page "构建 Tiled GEMM" ("Building a Tiled GEMM", mlc.ai
 // modern-gpu-programming-for-mlsys, chapter gemm_basics), section "GEMM".
 // The same kernels also serve bfloat16 storage, FP8 operands (2-byte units,
-// see mfma_f8) and the fused alpha/beta/bias epilogue.  The kernel design is
-// gfx950's own; what it keeps from the pages is listed next to each part.
+// see mfma_f8), an fp16 running sum (mma_acc16) and the fused
+// alpha/beta/bias epilogue.  The kernel design is gfx950's own; what it keeps
+// from the pages is listed next to each part.
 //
 // One workgroup computes one BM x BN output tile:
 //   * Tile -> workgroup map: an XCD-aware remap (consecutive workgroup ids
@@ -37,14 +38,16 @@
 //     the swizzle removes).  A ring of stages keeps the loads for later
 //     K-steps in flight while the MFMAs of the current one run (page 1,
 //     "内核 4", double buffering with STAGES = 2).
-//   * MFMA: v_mfma_f32_16x16x32_f16 (32x32x16 in two configurations), fp32
-//     accumulators in registers.  The B tile is fed as the instruction's
+//   * MFMA: v_mfma_f32_16x16x32_f16 (32x32x16 in the register-staged
+//     256 x 256 configuration), fp32 accumulators in registers (or fp16
+//     running sums updated once per K-step).  The B tile is fed as the instruction's
 //     first operand and the A tile as its second, so each lane's
 //     accumulators hold 4 consecutive columns n of D for one row m and the
 //     epilogue writes 8-byte vectors.
 //   * Epilogue: fp32 -> fp16 with v_cvt_f16_f32 (round to nearest even),
-//     masked at the M and N edges; the fused form loads C and bias first and
-//     forms alpha * acc + beta * C + bias in fp32.
+//     masked at the M and N edges, or staged through the freed LDS stages
+//     into whole-line stores for tiles wholly inside D; the fused form loads
+//     C and bias first and forms alpha * acc + beta * C + bias in fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1498,6 +1498,15 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 using BigDma = DmaCfg<256, 256, 2, 2, 64, 2, 16, 16, false>;
 // 128 x 128: 4 waves of 64 x 64 on 16x16x32 MFMAs, four 32 KB stages.
 using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
+// The same tile with two 32 KB stages: two workgroups share a CU, so one's
+// prologue, epilogue and waits run under the other's MFMAs.  Measured on
+// MI355X (TFLOP/s, two stages / four): 2048 x 4096 x 2048 (512 tiles)
+// 1077 / 1033, 2304^2 x 4096 (324) 947 / 869, 1280 x 4096^2 (320) 943 / 866,
+// 2560^2 x 2048 (400) 904 / 869, 2048 x 3072 x 1024 (384) 843 / 784; but with
+// at most 256 tiles the dispatcher puts two on one CU and leaves others idle:
+// 2048^3 (256) 734 / 1013, 1792^2 x 8192 (196) 769 / 1079.  So it serves
+// calls with more tiles than CUs.
+using Mid2Dma = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false>;
 // 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
 // eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.
 using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
@@ -1703,7 +1712,12 @@ void launch_plain(Tile t, const void *A, const void *B, void *D, int M, int N, i
 {
     switch (t) {
     case Tile::kBig: launch_tile<BigDma, BigReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
-    case Tile::kMid: launch_tile<MidDma, MidReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    case Tile::kMid:
+        if (cdiv(M, 128) * cdiv(N, 128) > kCUs)
+            launch_tile<Mid2Dma, MidReg, EPI, BF>(A, B, D, M, N, K, s, epi);
+        else
+            launch_tile<MidDma, MidReg, EPI, BF>(A, B, D, M, N, K, s, epi);
+        break;
     case Tile::kThinN: launch_tile<ThinNDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
     case Tile::kThinM: launch_tile<ThinMDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
     default: launch_tile<ThinDma, ThinReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;

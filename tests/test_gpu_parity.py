@@ -226,3 +226,20 @@ def test_skinny_half_tiles(M, N, K, tile):
     assert_bitexact(run_gemm(A, B, d_off=4), ref, f"{M}x{N}x{K} direct stores")
     Ar, Br = wl.uniform_inputs(7800 + K, M, N, K)
     assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")
+
+
+@pytest.mark.parametrize("M,N,K", [(2100, 2200, 200), (2100, 2200, 136), (2048, 4096, 256),
+                                   (1300, 4100, 72)])
+def test_mid_two_stage_tiles(M, N, K):
+    # more 128 x 128 tiles than CUs: the two-stage 128 x 128 kernel (two
+    # workgroups per CU); K tails, staged and direct stores, integer inputs
+    # bit-exact and random inputs in tolerance
+    bm, bn, _, wg = binding.gemm_nt_f16_tile(M, N, K)
+    assert (bm, bn) == (128, 128) and wg > 256
+    A, B = wl.integer_free(7900 + M + K, M, N, K)
+    ref = oracle.gemm_nt_f16(A, B)
+    note(f"two-stage 128x128 {M}x{N}x{K} ({wg} tiles)")
+    assert_bitexact(run_gemm(A, B), ref, f"{M}x{N}x{K}")
+    assert_bitexact(run_gemm(A, B, d_off=4), ref, f"{M}x{N}x{K} direct stores")
+    Ar, Br = wl.uniform_inputs(7950 + K, M, N, K)
+    assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")

@@ -27,6 +27,12 @@ namespace {
 // 128 x 128 tile for FP8: the 16-bit mid tile's pipeline with each step's
 // loads issued after the barrier (an FP8 step is a single MFMA slice).
 using Mid8 = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, false>;
+// With more 128 x 128 tiles than CUs: two 32 KB stages, two workgroups per
+// CU (as Mid2Dma for 16-bit operands).  Measured on MI355X (TFLOP/s, two
+// stages / four): 2048 x 4096 x 4096 2081 / 1803, 2560^2 x 4096 1789 / 1486,
+// 2304^2 x 8192 1861 / 1670, 3072 x 2048 x 8192 2052 / 1890; at 256 tiles
+// (2048^2 x 4096) 1427 / 1859, so the four-stage tile keeps those.
+using Mid82 = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false>;
 // 4-byte loads (K % 4 == 0, operands 4-byte aligned): 32 load instructions
 // per step, so two stages keep the waits encodable.
 using Mid84 = DmaCfg<128, 128, 2, 2, 64, 2, 16, 4, false>;
@@ -127,7 +133,12 @@ void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int
     if (lb == 16) {
         switch (t) {
         case Tile::kBig: launch_fp8_dma<BigDma, F8>(A, B, D, m, n, kp, vec, s, epi); break;
-        case Tile::kMid: launch_fp8_dma<Mid8, F8>(A, B, D, m, n, kp, vec, s, epi); break;
+        case Tile::kMid:
+            if (cdiv(M, 128) * cdiv(N, 128) > kCUs)
+                launch_fp8_dma<Mid82, F8>(A, B, D, m, n, kp, vec, s, epi);
+            else
+                launch_fp8_dma<Mid8, F8>(A, B, D, m, n, kp, vec, s, epi);
+            break;
         default: launch_fp8_dma<ThinDma, F8>(A, B, D, m, n, kp, vec, s, epi); break;
         }
     } else if (t == Tile::kMid) {

@@ -31,9 +31,11 @@ pytestmark = pytest.mark.gpu
 E4, E5 = binding.GEMM_FP8_E4M3, binding.GEMM_FP8_E5M2
 
 # 256x256 (K tail inside a step), 128x128, 64x64, 128x128 with 4-byte loads,
-# 64x64 with 4-byte loads, register staging (K % 4 == 2, K odd), one step
+# 64x64 with 4-byte loads, register staging (K % 4 == 2, K odd), one step,
+# two-stage 128x128 (more tiles than CUs, K tail inside a step)
 SHAPES = [(2900, 4100, 400), (1100, 1100, 1024), (64, 300, 512), (700, 900, 4100),
-          (50, 300, 260), (300, 200, 130), (150, 97, 37), (256, 256, 128)]
+          (50, 300, 260), (300, 200, 130), (150, 97, 37), (256, 256, 128),
+          (2100, 2200, 528)]
 
 
 def _ref(A, B, scale, fa, fb):
@@ -79,7 +81,7 @@ def test_fp8_misaligned_operands(a_off, b_off):
 
 
 @pytest.mark.parametrize("M,N,K,bm", [(4096, 4096, 128, 256), (1024, 1024, 512, 128),
-                                    (64, 2048, 1024, 64)])
+                                    (64, 2048, 1024, 64), (2100, 2200, 256, 128)])
 def test_fp8_staged_and_direct_epilogue(M, N, K, bm):
     # Whole tiles with D 16-byte aligned and N % 8 == 0 are written through
     # LDS; D only 8-byte aligned (d_off = 4) takes the direct stores.  Both

@@ -31,7 +31,8 @@ using Mid8 = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, false>;
 // CU (as Mid2Dma for 16-bit operands).  Measured on MI355X (TFLOP/s, two
 // stages / four): 2048 x 4096 x 4096 2081 / 1803, 2560^2 x 4096 1789 / 1486,
 // 2304^2 x 8192 1861 / 1670, 3072 x 2048 x 8192 2052 / 1890; at 256 tiles
-// (2048^2 x 4096) 1427 / 1859, so the four-stage tile keeps those.
+// (2048^2 x 4096, one workgroup per CU) 1427 / 1859, so the four-stage tile
+// keeps those.
 using Mid82 = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false>;
 // 4-byte loads (K % 4 == 0, operands 4-byte aligned): 32 load instructions
 // per step, so two stages keep the waits encodable.

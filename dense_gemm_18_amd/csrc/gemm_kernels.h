@@ -1502,10 +1502,11 @@ using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
 // prologue, epilogue and waits run under the other's MFMAs.  Measured on
 // MI355X (TFLOP/s, two stages / four): 2048 x 4096 x 2048 (512 tiles)
 // 1077 / 1033, 2304^2 x 4096 (324) 947 / 869, 1280 x 4096^2 (320) 943 / 866,
-// 2560^2 x 2048 (400) 904 / 869, 2048 x 3072 x 1024 (384) 843 / 784; but with
-// at most 256 tiles the dispatcher puts two on one CU and leaves others idle:
-// 2048^3 (256) 734 / 1013, 1792^2 x 8192 (196) 769 / 1079.  So it serves
-// calls with more tiles than CUs.
+// 2560^2 x 2048 (400) 904 / 869, 2048 x 3072 x 1024 (384) 843 / 784.  With at
+// most 256 tiles each CU runs one workgroup, and two stages then hide too
+// little load latency: 2048^3 (256) 705-734 / 905-1013, 1792^2 x 8192 (196)
+// 711-769 / 1001-1079 (also with one workgroup per CU forced by padding the
+// LDS request: 720 at 2048^3).  So it serves calls with more tiles than CUs.
 using Mid2Dma = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false>;
 // 64 x 64 (skinny, HBM-bound shapes): 4 waves of 32 x 32 on 16x16x32 MFMAs,
 // eight 16 KB stages so that each CU keeps ~112 KB of loads in flight.

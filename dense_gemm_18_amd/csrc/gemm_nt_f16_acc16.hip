@@ -13,35 +13,42 @@
 
 namespace {
 
-// Tiles.  The fp16 sums fit in the arch VGPRs (the AGPRs stay empty), so two
-// waves share each SIMD: the block update's VALU work of one wave then issues
-// while the other's MFMAs run.  256 x 256 with 8 waves of 128 x 64 (one
-// workgroup per CU, 218 VGPRs); 128 x 128 with 4 waves of 64 x 64 and two
-// 32 KB stages (two workgroups per CU); 64 x 64 for skinny shapes.  Measured
-// on MI355X, 8192^3: 1218 TFLOP/s on the 256 x 256 tile, 924 on 128 x 128
-// (the fp32-accumulating kernel: 1481); a 128 x 128 tile with one workgroup
-// per CU (four stages) runs 550.
+// Tiles.  The fp16 sums fit in the arch VGPRs (the AGPRs stay empty), so at
+// least two waves share each SIMD: the block update's VALU work of one wave
+// then issues while another's MFMAs run.  256 x 256 with 8 waves of 128 x 64
+// (one workgroup per CU); 128 x 128 with 8 waves of 64 x 32, two 32 KB stages
+// (two workgroups per CU) when there are more such tiles than CUs, four
+// stages (one per CU) otherwise; 64 x 64 for skinny shapes.  Measured on
+// MI355X (TFLOP/s): 8192^3 1218-1236 on 256 x 256 (the fp32-accumulating
+// kernel: 1481), 1034 on 128 x 128; 4096 x 2048 x 4096 1000 on 128 x 128 with
+// 8 waves against 927 with 4 waves of 64 x 64 and 927 on 256 x 256; with at
+// most 256 tiles 8 waves and four stages against 4 waves and two: 2048^3 796
+// / 581, 1792^2 x 8192 850 / 563, 2048 x 1024 x 4096 586 / 358.  With one wave
+// per SIMD (4 waves of 128 x 128 on 256 x 256) the kernel ran 550-600.
 using H16Big = DmaCfg<256, 256, 2, 4, 64, 2, 16, 16, false>;
-using H16Mid = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false>;
+using H16Mid = DmaCfg<128, 128, 2, 4, 64, 2, 16, 16, false>;
+using H16Mid4 = DmaCfg<128, 128, 2, 4, 64, 4, 16, 16, false>;
 using H16Thin = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
 // Register-staged 16-byte chunks (K % 8 != 0 or operands only 2-byte
 // aligned); 128 x 128 at 825 TFLOP/s on 8192^3 with aligned operands.
 using H16MidReg = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false, true>;
 using H16ThinReg = DmaCfg<64, 64, 2, 2, 64, 2, 16, 16, false, true>;
 
-// Tile choice: the smaller (waves of workgroups) x (time per wave), with the
-// 128 x 128 tile's two workgroups per CU: a wave of 256 x 256 tiles costs
-// 4 / 1218 and a wave of twice 256 128 x 128 tiles 2 / 924 (time per FLOP of
-// one 128 x 128 x K tile at the measured rates).  Skinny shapes (M or N at
-// most 64) take 64 x 64.
+// Tile choice: the smaller (waves of workgroups) x (time per wave), in units
+// of the time one CU takes for a 128 x 128 x K tile at the measured rates: a
+// wave of 256 x 256 tiles costs 4 / 1218, a wave of up to 256 128 x 128 tiles
+// (one per CU) 1 / 850 and a wave of twice 256 (two per CU) 2 / 1034.
+// Skinny shapes (M or N at most 64) take 64 x 64.
 Tile acc16_tile(int64_t M, int64_t N, bool direct)
 {
     if (M <= 64 || N <= 64)
         return Tile::kThin;
     if (!direct)
         return Tile::kMid;
+    const int64_t mid_tiles = cdiv(M, 128) * cdiv(N, 128);
     const double big = (double)cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs) * 4.0 / 1218.0;
-    const double mid = (double)cdiv(cdiv(M, 128) * cdiv(N, 128), 2 * kCUs) * 2.0 / 924.0;
+    const double mid = mid_tiles <= kCUs ? 1.0 / 850.0
+                                         : (double)cdiv(mid_tiles, 2 * kCUs) * 2.0 / 1034.0;
     return big <= mid ? Tile::kBig : Tile::kMid;
 }
 
@@ -109,7 +116,9 @@ int gemm_nt_f16_acc16(const void *A, const void *B, void *D, int64_t M, int64_t 
     switch (acc16_tile(M, N, direct)) {
     case Tile::kBig: launch_acc16<H16Big>(A, B, D, m, n, k, stream); break;
     case Tile::kMid:
-        if (direct)
+        if (direct && cdiv(M, 128) * cdiv(N, 128) <= kCUs)
+            launch_acc16<H16Mid4>(A, B, D, m, n, k, stream);
+        else if (direct)
             launch_acc16<H16Mid>(A, B, D, m, n, k, stream);
         else
             launch_acc16<H16MidReg>(A, B, D, m, n, k, stream);

@@ -60,10 +60,12 @@ def _run(A, B, **kw):
 
 
 # (M, N, K, a_off, b_off, tile, load bytes): the 256 x 256 (8 waves), 128 x 128
-# and 64 x 64 tiles with direct loads, and the register-staged 128 x 128 and
-# 64 x 64 kernels (odd K, K % 8 != 0, 2-byte aligned operands)
+# (four stages with at most 256 tiles, two beyond: 2300 x 2200) and 64 x 64
+# tiles with direct loads, and the register-staged 128 x 128 and 64 x 64
+# kernels (odd K, K % 8 != 0, 2-byte aligned operands)
 CASES = [(2900, 4100, 512, 0, 0, 256, 16), (2900, 4100, 520, 0, 0, 256, 16),
          (1000, 1100, 576, 0, 0, 128, 16), (700, 900, 200, 0, 0, 128, 16),
+         (2300, 2200, 264, 0, 0, 128, 16),
          (64, 3000, 448, 0, 0, 64, 16), (3000, 40, 200, 0, 0, 64, 16),
          (1000, 1100, 577, 0, 0, 128, 1), (700, 900, 202, 0, 0, 128, 1),
          (1000, 1100, 512, 1, 0, 128, 1), (700, 900, 200, 0, 3, 128, 1),

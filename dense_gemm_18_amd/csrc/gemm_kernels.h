@@ -1674,11 +1674,11 @@ inline int store_mode(const void *D, int64_t N, uintptr_t other = 0)
     return ((d & 15u) == 0 && N % 8 == 0) ? 2 : 1;
 }
 
-// CDma: the direct-to-LDS pipeline with 16-byte loads; CDma4: the same with
-// 4-byte loads; C: the register-staged kernel for whatever remains (odd K or
-// 2-byte aligned operands).
 // Bytes each lane moves per direct-to-LDS load for these operands: 16, 4,
-// or 0 when only the register-staged kernel can serve them.
+// or 0 when only the register-staged kernel can serve them.  The one-tile-
+// per-workgroup launches use the direct loads only at 16 bytes and stage
+// everything else through registers; the stream-K grid also runs 4-byte
+// direct loads.
 inline int load_bytes(const void *A, const void *B, int64_t K)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;

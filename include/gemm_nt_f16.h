@@ -28,8 +28,10 @@
  * Errors: every argument check happens before any HIP runtime call, so the
  * checks can be exercised on a machine without a GPU.
  *
- * Thread safety: every entry point is re-entrant; the library holds no
- * mutable state.
+ * Thread safety: every entry point is re-entrant.  The library's only
+ * mutable state is a per-device cache of the CU count (written once, with
+ * atomic accesses) and the static workspace of gemm_nt_f16_ws_noalloc, whose
+ * own comment states how calls share it.
  */
 #ifndef GEMM_NT_F16_H
 #define GEMM_NT_F16_H

@@ -1595,10 +1595,15 @@ inline void tile_dims(Tile t, int &bm, int &bn)
     }
 }
 
+// Sizes every entry point accepts: M, N in [0, 2^31 - 1], K in [0, GEMM_MAX_K].
+inline bool sizes_ok(int64_t M, int64_t N, int64_t K)
+{
+    return M >= 0 && N >= 0 && K >= 0 && M <= INT32_MAX && N <= INT32_MAX && K <= GEMM_MAX_K;
+}
+
 inline int validate(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t lim = INT32_MAX;
-    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > GEMM_MAX_K)
+    if (!sizes_ok(M, N, K))
         return GEMM_EINVAL;
     const uint64_t a_bytes = (uint64_t)M * (uint64_t)K * 2u;
     const uint64_t b_bytes = (uint64_t)N * (uint64_t)K * 2u;

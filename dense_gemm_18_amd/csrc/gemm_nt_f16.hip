@@ -36,7 +36,7 @@ const char *gemm_nt_f16_strerror(int code)
 
 int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk, int64_t *workgroups)
 {
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !bk || !workgroups)
+    if (!sizes_ok(M, N, K) || !bm || !bn || !bk || !workgroups)
         return GEMM_EINVAL;
     tile_dims(run_tile(choose_tile(M, N, K), K % 8 == 0), *bm, *bn);
     *bk = kBK;
@@ -47,7 +47,7 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk,
 int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, int64_t N,
                        int64_t K, int *bm, int *bn, int *lbytes, int *store)
 {
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !lbytes || !store)
+    if (!sizes_ok(M, N, K) || !bm || !bn || !lbytes || !store)
         return GEMM_EINVAL;
     *lbytes = load_bytes(A, B, K) == 16 ? 16 : 1;
     tile_dims(run_tile(choose_tile(M, N, K), *lbytes == 16), *bm, *bn);
@@ -58,7 +58,8 @@ int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, i
 int gemm_nt_f16_tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n, int64_t *tile_m,
                            int64_t *tile_n)
 {
-    if (tiles_m <= 0 || tiles_n <= 0 || wg < 0 || wg >= tiles_m * tiles_n || !tile_m || !tile_n)
+    if (tiles_m <= 0 || tiles_n <= 0 || tiles_m > INT32_MAX || tiles_n > INT32_MAX || wg < 0 ||
+        wg >= tiles_m * tiles_n || !tile_m || !tile_n)
         return GEMM_EINVAL;
     tile_coord(wg, tiles_m, tiles_n, *tile_m, *tile_n);
     return GEMM_OK;
@@ -105,7 +106,7 @@ int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, 
 int gemm_nt_f16_ws_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int64_t *workgroups,
                         int64_t *sk_tiles)
 {
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !workgroups || !sk_tiles)
+    if (!sizes_ok(M, N, K) || !bm || !bn || !workgroups || !sk_tiles)
         return GEMM_EINVAL;
     const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
     const Plan pl = make_plan(M, N, K, (M && N && K) ? lb : 0, kCUs);

@@ -136,7 +136,7 @@ int gemm_nt_f16_acc16(const void *A, const void *B, void *D, int64_t M, int64_t 
 int gemm_nt_f16_acc16_kernel(const void *A, const void *B, int64_t M, int64_t N, int64_t K,
                              int *bm, int *bn, int *lbytes)
 {
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn || !lbytes)
+    if (!sizes_ok(M, N, K) || !bm || !bn || !lbytes)
         return GEMM_EINVAL;
     const bool direct = load_bytes(A, B, K) == 16;
     *lbytes = direct ? 16 : 1;

@@ -9,8 +9,7 @@ int fp8_call(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_
              const float *col_scale, bool want_cols, int a_format, int b_format,
              hipStream_t stream)
 {
-    const int64_t lim = INT32_MAX;
-    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > GEMM_MAX_K)
+    if (!sizes_ok(M, N, K))
         return GEMM_EINVAL;
     if ((a_format != GEMM_FP8_E4M3 && a_format != GEMM_FP8_E5M2) ||
         (b_format != GEMM_FP8_E4M3 && b_format != GEMM_FP8_E5M2))
@@ -66,7 +65,7 @@ int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, 
 
 int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn)
 {
-    if (M < 0 || N < 0 || K < 0 || !bm || !bn)
+    if (!sizes_ok(M, N, K) || !bm || !bn)
         return GEMM_EINVAL;
     const int lb = K % 16 == 0 && aligned16 ? 16 : (K % 4 == 0 ? 4 : 0);
     tile_dims(fp8_tile(M, N, K, lb), *bm, *bn);

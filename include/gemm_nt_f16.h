@@ -110,7 +110,8 @@ int gemm_nt_f16_acc16(const void *A, const void *B, void *D,
  * and load mode (*lbytes: 16 = 16-byte direct-to-LDS loads, 1 =
  * register-staged chunks) a call with these pointers and sizes runs.
  * A and B are only inspected for alignment, never dereferenced.  Returns
- * GEMM_OK, or GEMM_EINVAL for a negative size or a NULL output pointer.
+ * GEMM_OK, or GEMM_EINVAL for a size out of the entry points' range or a
+ * NULL output pointer.
  */
 int gemm_nt_f16_acc16_kernel(const void *A, const void *B, int64_t M, int64_t N, int64_t K,
                              int *bm, int *bn, int *lbytes);
@@ -174,7 +175,7 @@ int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, 
  * Host-only: the output tile gemm_nt_fp8 uses for these sizes (aligned16:
  * whether A and B are 16-byte aligned; 4-byte alignment is assumed
  * otherwise; with K % 4 != 0 the tile of the register-staged loads).
- * GEMM_EINVAL for negative sizes or NULL outputs.
+ * GEMM_EINVAL for sizes out of the entry points' range or NULL outputs.
  */
 int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn);
 
@@ -284,7 +285,8 @@ int64_t gemm_nt_f16_ws_size(int64_t M, int64_t N, int64_t K);
  * Host-only introspection (no HIP call) of gemm_nt_f16_ws's plan for 16-byte
  * aligned operands on 256 CUs: the tile, the workgroups launched and how
  * many tiles are split by K-steps (0: the plain one-workgroup-per-tile
- * launch).  Returns GEMM_OK or GEMM_EINVAL (negative size or NULL output).
+ * launch).  Returns GEMM_OK or GEMM_EINVAL (a size out of the entry
+ * points' range, or a NULL output).
  */
 int gemm_nt_f16_ws_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn,
                         int64_t *workgroups, int64_t *sk_tiles);
@@ -311,7 +313,7 @@ const char *gemm_nt_f16_strerror(int code);
  * step BK that gemm_nt_f16 uses for an M x N x K problem with operands
  * aligned to 16 bytes, and the number of workgroups it launches.  Tests use
  * it to pick rows and columns at tile edges.  Returns GEMM_OK or GEMM_EINVAL
- * (negative size or NULL output).
+ * (a size out of the entry points' range, or a NULL output).
  */
 int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
                      int *bm, int *bn, int *bk, int64_t *workgroups);
@@ -327,7 +329,8 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
  * stores; 1: 8-byte stores, D 8-byte aligned and N % 4 == 0; 2: whole tiles
  * staged through LDS and written with 16-byte stores, D 16-byte aligned and
  * N % 8 == 0).  The pointers are only inspected, never dereferenced.
- * Returns GEMM_OK or GEMM_EINVAL (negative size or NULL output).
+ * Returns GEMM_OK or GEMM_EINVAL (a size out of the entry points' range, or
+ * a NULL output).
  */
 int gemm_nt_f16_kernel(const void *A, const void *B, const void *D,
                        int64_t M, int64_t N, int64_t K,
@@ -336,9 +339,10 @@ int gemm_nt_f16_kernel(const void *A, const void *B, const void *D,
 /*
  * Host-only introspection (no HIP call): the output tile (tile_m, tile_n)
  * that workgroup `wg` computes when the output is split into tiles_m x
- * tiles_n tiles.  The map is a bijection of [0, tiles_m*tiles_n) onto the
- * tiles; it keeps tiles that share A or B rows on the same L2 slice.
- * Returns GEMM_OK or GEMM_EINVAL (wg or a count out of range, NULL output).
+ * tiles_n tiles (each count in [1, 2^31 - 1]).  The map is a bijection of
+ * [0, tiles_m*tiles_n) onto the tiles; it keeps tiles that share A or B rows
+ * on the same L2 slice.  Returns GEMM_OK or GEMM_EINVAL (wg or a count out
+ * of range, NULL output).
  */
 int gemm_nt_f16_tile_coord(int64_t wg, int64_t tiles_m, int64_t tiles_n,
                            int64_t *tile_m, int64_t *tile_n);

@@ -126,6 +126,35 @@ def test_tile_map_is_a_bijection(tiles_m, tiles_n):
         binding.gemm_nt_f16_tile_coord(total, tiles_m, tiles_n)
 
 
+def test_introspection_rejects_sizes_out_of_range():
+    # the same size range as the entry points: M, N <= 2^31 - 1, K <= GEMM_MAX_K
+    for M, N, K in [(2 ** 31, 4, 4), (4, 2 ** 31, 4), (4, 4, binding.GEMM_MAX_K + 1),
+                    (2 ** 62, 2 ** 62, 64), (-1, 4, 4)]:
+        for call in (lambda: binding.gemm_nt_f16_tile(M, N, K),
+                     lambda: binding.gemm_nt_f16_kernel(1 << 20, 1 << 21, 1 << 22, M, N, K),
+                     lambda: binding.gemm_nt_f16_ws_tile(M, N, K),
+                     lambda: binding.gemm_nt_f16_acc16_kernel(1 << 20, 1 << 21, M, N, K),
+                     lambda: binding.gemm_nt_fp8_tile(M, N, K, True)):
+            with pytest.raises(binding.GemmError):
+                call()
+        assert binding.gemm_nt_f16_ws_size(M, N, K) == 0
+    # the largest accepted sizes still answer
+    top = 2 ** 31 - 1
+    assert binding.gemm_nt_f16_tile(top, top, binding.GEMM_MAX_K)[0] == 256
+
+
+def test_tile_map_rejects_counts_out_of_range():
+    big = 2 ** 31
+    for tm, tn, wg in [(big, 1, 0), (1, big, 0), (2 ** 62, 4, 0), (0, 5, 0), (5, -1, 0),
+                       (3, 3, -1)]:
+        with pytest.raises(binding.GemmError):
+            binding.gemm_nt_f16_tile_coord(wg, tm, tn)
+    # the largest counts still map, and the last workgroup lands on a tile
+    top = 2 ** 31 - 1
+    tm, tn = binding.gemm_nt_f16_tile_coord(top * top - 1, top, top)
+    assert 0 <= tm < top and 0 <= tn < top
+
+
 def test_tile_map_keeps_xcd_neighbours_close():
     # 32 x 32 tiles (8192^2 at 256^2): the workgroups that run together on one
     # XCD (ids x, x+8, x+16, ...) cover a compact block of tiles, so they

@@ -248,7 +248,8 @@ def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0, b_scale=None):
     contiguous float32 tensor of N per-row scales of B on the same device),
     gemm_nt_fp8_cs with a_scale = ``scale``.  ``out`` (optional) is a
     contiguous [M, N] tensor of D's dtype on the same device.  The call is
-    enqueued on ``stream`` (default: the current stream).
+    enqueued on ``stream`` (default: A's device's current stream; a stream
+    given must belong to A's device), with A's device made current for it.
     """
     import torch
 
@@ -281,19 +282,22 @@ def gemm_nt(A, B, out=None, stream=None, scale: float = 1.0, b_scale=None):
         if (b_scale.dtype != torch.float32 or b_scale.numel() != N or not b_scale.is_contiguous()
                 or b_scale.device != A.device):
             raise ValueError("b_scale must be a contiguous float32 tensor of N values on A's device")
-    if A.dtype in fp8 and b_scale is not None:
-        name = "gemm_nt_fp8_cs"
-        rc = gemm_nt_fp8_cs(pa, pb, pd, M, N, K, scale, b_scale.data_ptr(), fp8[A.dtype],
-                            fp8[B.dtype], s.cuda_stream)
-    elif A.dtype in fp8:
-        name = "gemm_nt_fp8"
-        rc = gemm_nt_fp8(pa, pb, pd, M, N, K, scale, fp8[A.dtype], fp8[B.dtype], s.cuda_stream)
-    elif A.dtype == torch.bfloat16:
-        name = "gemm_nt_bf16"
-        rc = gemm_nt_bf16(pa, pb, pd, M, N, K, s.cuda_stream)
-    else:
-        name = "gemm_nt_f16"
-        rc = gemm_nt_f16(pa, pb, pd, M, N, K, s.cuda_stream)
+    # the library launches on the current device: make it the operands' one
+    with torch.cuda.device(A.device):
+        if A.dtype in fp8 and b_scale is not None:
+            name = "gemm_nt_fp8_cs"
+            rc = gemm_nt_fp8_cs(pa, pb, pd, M, N, K, scale, b_scale.data_ptr(), fp8[A.dtype],
+                                fp8[B.dtype], s.cuda_stream)
+        elif A.dtype in fp8:
+            name = "gemm_nt_fp8"
+            rc = gemm_nt_fp8(pa, pb, pd, M, N, K, scale, fp8[A.dtype], fp8[B.dtype],
+                             s.cuda_stream)
+        elif A.dtype == torch.bfloat16:
+            name = "gemm_nt_bf16"
+            rc = gemm_nt_bf16(pa, pb, pd, M, N, K, s.cuda_stream)
+        else:
+            name = "gemm_nt_f16"
+            rc = gemm_nt_f16(pa, pb, pd, M, N, K, s.cuda_stream)
     if rc != GEMM_OK:
         raise GemmError(rc, name)
     return out

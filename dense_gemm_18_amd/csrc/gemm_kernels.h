@@ -1496,6 +1496,22 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
 // accumulator registers busy per FLOP as 32x32x16, so the part draws less
 // power and holds a higher clock under its power limit.
 using BigDma = DmaCfg<256, 256, 2, 2, 64, 2, 16, 16, false>;
+// The same tile with three B stages (two 32 KB A stages, three 32 KB B
+// stages: the whole 160 KB), for K % 512 != 0.  B's refills then go out in
+// a step's first slice and A's in its second, so each slice issues half a
+// step's loads.  When the rows' 128-byte K-segments cross cache lines, a
+// step's load burst backs up between L1 and L2: at 8192^2 x 8200 the L1
+// makes twice the L2 read requests it makes at 8192^3 and its
+// TCP_TCR_TCP_STALL_CYCLES rise 9x, while the vendor library's kernel, with
+// the same request counts, shows no such rise.  Halving the burst recovers
+// most of the loss, and also helps a pitch of 129 lines.  Measured on MI355X
+// (TFLOP/s, two stages / three B stages): 8192^2 x 8200 1215 / 1330,
+// 8192^2 x 8136 1167 / 1278, 8192^2 x 8256 1431 / 1496, 4096^2 x 4104
+// 1196 / 1307, 3000 x 5000 x 2056 1016 / 1127, 16384^2 x 1032 991 / 1079;
+// with K % 512 == 0 the two are alike (8192^3 1505 / 1502, 4096^3 1412 /
+// 1423, 3000 x 5000 x 2048 1195 / 1193, 16384^2 x 1024 1204 / 1189), and
+// those keep the two-stage ring.
+using BigDma3 = DmaCfg<256, 256, 2, 2, 64, 2, 16, 16, false, false, true>;
 // 128 x 128: 4 waves of 64 x 64 on 16x16x32 MFMAs, four 32 KB stages.
 using MidDma = DmaCfg<128, 128, 2, 2, 64, 4, 16, 16, true>;
 // The same tile with two 32 KB stages: two workgroups share a CU, so one's
@@ -1717,7 +1733,12 @@ void launch_plain(Tile t, const void *A, const void *B, void *D, int M, int N, i
                   hipStream_t s, const Epi &epi = Epi{})
 {
     switch (t) {
-    case Tile::kBig: launch_tile<BigDma, BigReg, EPI, BF>(A, B, D, M, N, K, s, epi); break;
+    case Tile::kBig:
+        if (K % 512 != 0)
+            launch_tile<BigDma3, BigReg, EPI, BF>(A, B, D, M, N, K, s, epi);
+        else
+            launch_tile<BigDma, BigReg, EPI, BF>(A, B, D, M, N, K, s, epi);
+        break;
     case Tile::kMid:
         if (cdiv(M, 128) * cdiv(N, 128) > kCUs)
             launch_tile<Mid2Dma, MidReg, EPI, BF>(A, B, D, M, N, K, s, epi);

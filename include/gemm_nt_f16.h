@@ -328,7 +328,9 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
  * epilogue's store form (0: element
  * stores; 1: 8-byte stores, D 8-byte aligned and N % 4 == 0; 2: whole tiles
  * staged through LDS and written with 16-byte stores, D 16-byte aligned and
- * N % 8 == 0).  The pointers are only inspected, never dereferenced.
+ * N % 8 == 0).  (The 256 x 256 tile with 16-byte loads keeps A in two LDS
+ * stages and B in three when K % 512 != 0, in two otherwise.)  The pointers
+ * are only inspected, never dereferenced.
  * Returns GEMM_OK or GEMM_EINVAL (a size out of the entry points' range, or
  * a NULL output).
  */

@@ -228,6 +228,25 @@ def test_skinny_half_tiles(M, N, K, tile):
     assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")
 
 
+@pytest.mark.parametrize("M,N,K", [(2900, 4100, 512), (2900, 4100, 1024), (2900, 4100, 520),
+                                   (2900, 4100, 576), (2900, 4100, 1032)])
+def test_big_tile_b_rings(M, N, K):
+    # the 256 x 256 direct-to-LDS kernel keeps two B stages when K % 512 == 0
+    # (512, 1024) and runs three B stages otherwise (520 and 1032 with a K
+    # tail, 576 without); integer inputs bit-exact with staged and
+    # direct stores, random inputs in tolerance
+    bm, bn, lb, _ = binding.gemm_nt_f16_kernel(1 << 20, 2 << 20, 3 << 20, M, N, K)
+    assert (bm, bn, lb) == (256, 256, 16)
+    A, B = wl.integer_free(8100 + K, M, N, K)
+    ref = oracle.gemm_nt_f16(A, B)
+    rings = "two" if K % 512 == 0 else "three"
+    note(f"256x256 {rings} B stages {M}x{N}x{K}")
+    assert_bitexact(run_gemm(A, B), ref, f"{M}x{N}x{K}")
+    assert_bitexact(run_gemm(A, B, d_off=4), ref, f"{M}x{N}x{K} direct stores")
+    Ar, Br = wl.uniform_inputs(8150 + K, M, N, K)
+    assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")
+
+
 @pytest.mark.parametrize("M,N,K", [(2100, 2200, 200), (2100, 2200, 136), (2048, 4096, 256),
                                    (1300, 4100, 72)])
 def test_mid_two_stage_tiles(M, N, K):

@@ -532,6 +532,25 @@ __device__ __forceinline__ void load_lds(__amdgpu_buffer_rsrc_t rs, char *dst, u
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, voff, soff, 0, AUX);
 }
 
+// The eight 16-bit elements of v moved up by s places (s in 1..7, uniform
+// across the wave): element j of the result is element j - s of v, and
+// elements 0 .. s-1 are zero.
+__device__ __forceinline__ u32x4 shift_up_halves(u32x4 v, int s)
+{
+    const uint64_t lo = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    const uint64_t hi = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
+    const int b = 16 * s;
+    uint64_t nlo, nhi;
+    if (b < 64) {
+        nlo = lo << b;
+        nhi = (hi << b) | (lo >> (64 - b));
+    } else {
+        nlo = 0;
+        nhi = lo << (b - 64);
+    }
+    return u32x4{(uint32_t)nlo, (uint32_t)(nlo >> 32), (uint32_t)nhi, (uint32_t)(nhi >> 32)};
+}
+
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 // 128-byte rows read by 16x16x32 fragments (16 rows x 16 bytes per quarter
@@ -1375,6 +1394,42 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         });
         lds_barrier();
     } else {
+    // With K % 8 != 0 the steps, aligned to K's end, start their 16-byte
+    // chunks at k = K mod 8 + 8j, so in the item's first step (k0 < 0) one
+    // chunk of each row holds k = -8 + e .. e - 1 with e = K mod 8: 8 - e
+    // elements of the row before (or of no row) and the row's first e.  Its
+    // direct load, like those of the chunks wholly before k = 0, gets the
+    // out-of-range offset and fills zeros; the row's first eight elements
+    // are loaded into registers ahead of the stage's direct loads (so the
+    // stage's wait covers them), moved up by 8 - e places and written over
+    // those zeros before the barrier that publishes the stage.  Rows past
+    // the tile's valid rows load zeros.  (Needs K >= 8: a row then spans the
+    // 16 bytes read from its start.)
+    constexpr bool FIX = KTAIL && UB == 2 && C::LB == 16;
+    const int fe = FIX && kb < 0 ? (kb & 7) : 0;       // uniform: K mod 8, or 0
+    u32x4 fixv[FIX ? C::LPS : 1];
+    auto fix_chunk = [&](auto qc) G18_INLINE -> bool {
+        constexpr int q = decltype(qc)::value;
+        constexpr bool isa = q < C::A_LOADS;
+        constexpr int i = isa ? q : q - C::A_LOADS;
+        const int kk = kb + (isa ? a_k[i] : b_k[i]);
+        return kk < 0 && kk > -8;
+    };
+    if constexpr (FIX) {
+        if (fe != 0) {
+            static_for<0, C::LPS>([&](auto qc) G18_INLINE {
+                constexpr int q = decltype(qc)::value;
+                constexpr bool isa = q < C::A_LOADS;
+                constexpr int i = isa ? q : q - C::A_LOADS;
+                if (fix_chunk(qc)) {
+                    const uint32_t row0 = (isa ? a_off[i] : b_off[i]) -
+                                          (uint32_t)((isa ? a_k[i] : b_k[i]) * 2);
+                    fixv[q] = __builtin_amdgcn_raw_buffer_load_b128(n > 0 ? (isa ? ra : rb) : rz,
+                                                                    row0, 0, 0);
+                }
+            });
+        }
+    }
     static_for<0, C::NSTAGE>([&](auto sc) G18_INLINE {
         constexpr int st = decltype(sc)::value;
         static_for<0, (st + 1 < C::NSTAGE ? C::LPS : PRO_LAST)>(
@@ -1383,6 +1438,20 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             });
     });
     wait_vmcnt<C::LPS * (C::NSTAGE - 2) + PRO_LAST>();
+    if constexpr (FIX) {
+        if (fe != 0) {
+            static_for<0, C::LPS>([&](auto qc) G18_INLINE {
+                constexpr int q = decltype(qc)::value;
+                constexpr bool isa = q < C::A_LOADS;
+                constexpr int i = isa ? q : q - C::A_LOADS;
+                if (fix_chunk(qc)) {
+                    char *dst = smem + (isa ? C::a_base(0) : C::b_base(0)) +
+                                (wave + C::NWAVES * i) * C::INST_BYTES + lane * 16;
+                    *(u32x4 *)dst = shift_up_halves(fixv[q], 8 - fe);
+                }
+            });
+        }
+    }
     lds_barrier();
     }
     static_for<0, NR>([&](auto qc) G18_INLINE { read_one(Z_{}, Z_{}, Z_{}, qc); });
@@ -1531,9 +1600,9 @@ using ThinDma = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
 // idle, e.g. 64 x 8192 x K): 2 waves of 32 x 32, ten 12 KB stages.
 using ThinNDma = DmaCfg<64, 32, 2, 1, 64, 10, 16, 16, false>;
 using ThinMDma = DmaCfg<32, 64, 1, 2, 64, 10, 16, 16, false>;
-// 4-byte loads (K even, operands 4-byte aligned): four times as many load
-// instructions per step, so fewer stages keep the waits encodable.
-using MidDma4 = DmaCfg<128, 128, 2, 2, 64, 3, 16, 4, true>;
+// 4-byte loads (FP8 with K % 4 == 0, operands 4-byte aligned): four times
+// as many load instructions per step, so fewer stages keep the waits
+// encodable.
 using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4, false>;
 // Register-staged 16-byte chunks (any K, operands 2-byte aligned): two
 // stages, each chunk loaded a step ahead into registers.  The 256 x 256 tile
@@ -1580,7 +1649,7 @@ inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
         }
         return Tile::kThin;
     }
-    const bool wide = K % 8 == 0;
+    const bool wide = K >= 8;      // 16-byte direct-to-LDS loads (load_bytes, M, N > 64)
     const double big_tile = wide ? 4.0 : 6.6, mid_tile = wide ? 1.4 : 2.25;
     const double thin_tile = wide ? 0.85 : 1.3;
     const double big = cdiv(cdiv(M, 256) * cdiv(N, 256), kCUs) * big_tile;
@@ -1695,19 +1764,25 @@ inline int store_mode(const void *D, int64_t N, uintptr_t other = 0)
     return ((d & 15u) == 0 && N % 8 == 0) ? 2 : 1;
 }
 
-// Bytes each lane moves per direct-to-LDS load for these operands: 16, 4,
-// or 0 when only the register-staged kernel can serve them.  The one-tile-
-// per-workgroup launches use the direct loads only at 16 bytes and stage
-// everything else through registers; the stream-K grid also runs 4-byte
-// direct loads.
-inline int load_bytes(const void *A, const void *B, int64_t K)
+// Bytes each lane moves per direct-to-LDS load for these operands: 16, or 0
+// for the register-staged kernel.  Rows that start 16-byte aligned (K % 8
+// == 0, A and B 16-byte aligned) always take the direct loads.  The 16-byte
+// direct-to-LDS loads also take any 2-byte aligned address on gfx950, so
+// rows that do not (K % 8 != 0, or operands offset by whole elements) take
+// them too, with two exceptions that stay with register staging: K < 8
+// (the first K-step's fix-up reads 16 bytes from each row's start, which a
+// row of fewer than 8 elements does not span) and skinny shapes (M or N <=
+// 64), whose tiles stream the long operand from HBM faster with register
+// staging at such rows (measured on MI355X, TFLOP/s, direct / register-
+// staged: 64 x 32768 x 4095 182 / 240, 64 x 16384 x 8191 224 / 249;
+// elsewhere direct wins: 3000 x 5000 x 2050 1023-1080 / 847, 8192^2 x 8191
+// 1174 / 1046, 2048^2 x 2047 648-668 / 591, 1024^2 x 4095 367 / 337).
+inline int load_bytes(const void *A, const void *B, int64_t M, int64_t N, int64_t K)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
     if (K % 8 == 0 && (ab & 15u) == 0)
         return 16;
-    if (K % 2 == 0 && (ab & 3u) == 0)
-        return 4;
-    return 0;
+    return K >= 8 && (ab & 1u) == 0 && M > 64 && N > 64 ? 16 : 0;
 }
 
 // One workgroup per tile.  EPI: with the fused epilogue `epi`, whose C and
@@ -1720,7 +1795,7 @@ void launch_tile(const void *A, const void *B, void *D, int M, int N, int K, hip
 {
     const int vec = store_mode(D, N, (uintptr_t)epi.C | (uintptr_t)epi.bias);
     const SkPlan none{};
-    if (load_bytes(A, B, K) == 16)
+    if (load_bytes(A, B, M, N, K) == 16)
         launch_dma<CDma, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
     else
         launch_dma<CReg, false, EPI, BF>(A, B, D, M, N, K, vec, s, none, 0, epi);
@@ -1787,7 +1862,7 @@ inline SkPlan sk_split(int64_t tiles, int64_t steps, int P)
 
 constexpr int64_t kSkMinSteps = 192;
 
-// lb: 16 or 4 (0: the register-staged path, no stream-K).
+// lb: 16 (0: the register-staged path, no stream-K).
 inline Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
 {
     Plan pl;
@@ -1818,10 +1893,7 @@ inline void launch_sk(const void *A, const void *B, void *D, int M, int N, int K
                       const SkPlan &sk, int grid)
 {
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    if (load_bytes(A, B, K) == 16)
-        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
-    else
-        launch_dma<MidDma4, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+    launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
 }
 
 // Header, flags and slots of a stream-K plan inside workspace `ws`.

@@ -38,7 +38,9 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int *bk,
 {
     if (!sizes_ok(M, N, K) || !bm || !bn || !bk || !workgroups)
         return GEMM_EINVAL;
-    tile_dims(run_tile(choose_tile(M, N, K), K % 8 == 0), *bm, *bn);
+    // the load mode of 16-byte aligned operands (load_bytes)
+    const bool direct = K % 8 == 0 || (K >= 8 && M > 64 && N > 64);
+    tile_dims(run_tile(choose_tile(M, N, K), direct), *bm, *bn);
     *bk = kBK;
     *workgroups = (M == 0 || N == 0 || K == 0) ? 0 : cdiv(M, *bm) * cdiv(N, *bn);
     return GEMM_OK;
@@ -49,7 +51,7 @@ int gemm_nt_f16_kernel(const void *A, const void *B, const void *D, int64_t M, i
 {
     if (!sizes_ok(M, N, K) || !bm || !bn || !lbytes || !store)
         return GEMM_EINVAL;
-    *lbytes = load_bytes(A, B, K) == 16 ? 16 : 1;
+    *lbytes = load_bytes(A, B, M, N, K) == 16 ? 16 : 1;
     tile_dims(run_tile(choose_tile(M, N, K), *lbytes == 16), *bm, *bn);
     *store = store_mode(D, N);
     return GEMM_OK;
@@ -69,7 +71,7 @@ int64_t gemm_nt_f16_ws_size(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0 || M > INT32_MAX || N > INT32_MAX || K > GEMM_MAX_K)
         return 0;
-    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    const int lb = K >= 8 ? 16 : 0;
     return workspace_bytes(make_plan(M, N, K, lb, kCUs));
 }
 
@@ -90,7 +92,7 @@ int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, 
         if (hits(A, M * K * 2) || hits(B, N * K * 2) || hits(D, M * N * 2))
             return GEMM_EINVAL;
     }
-    const int lb = load_bytes(A, B, K);
+    const int lb = load_bytes(A, B, M, N, K);
     if (M == 0 || N == 0 || K == 0 || lb == 0)
         return gemm_nt_f16(A, B, D, M, N, K, stream);
     const Plan pl = make_plan(M, N, K, lb, device_cus());
@@ -108,7 +110,7 @@ int gemm_nt_f16_ws_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn, int64
 {
     if (!sizes_ok(M, N, K) || !bm || !bn || !workgroups || !sk_tiles)
         return GEMM_EINVAL;
-    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    const int lb = K >= 8 ? 16 : 0;
     const Plan pl = make_plan(M, N, K, (M && N && K) ? lb : 0, kCUs);
     tile_dims(pl.tile, *bm, *bn);
     *sk_tiles = pl.sk ? pl.split.sk_tiles : 0;
@@ -122,7 +124,7 @@ int gemm_nt_f16_ws_items(int64_t M, int64_t N, int64_t K, int64_t wg, int64_t *i
     if (M <= 0 || N <= 0 || K <= 0 || M > INT32_MAX || N > INT32_MAX || K > GEMM_MAX_K ||
         max_items < 0 || (max_items && !items) || !count)
         return GEMM_EINVAL;
-    const int lb = K % 8 == 0 ? 16 : (K % 2 == 0 ? 4 : 0);
+    const int lb = K >= 8 ? 16 : 0;
     const Plan pl = make_plan(M, N, K, lb, kCUs);
     *count = 0;
     if (!pl.sk)

@@ -111,7 +111,7 @@ int gemm_nt_f16_acc16(const void *A, const void *B, void *D, int64_t M, int64_t 
                            (uint16_t *)D, count);
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
     }
-    const bool direct = load_bytes(A, B, K) == 16;
+    const bool direct = load_bytes(A, B, M, N, K) == 16;
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (acc16_tile(M, N, direct)) {
     case Tile::kBig: launch_acc16<H16Big>(A, B, D, m, n, k, stream); break;
@@ -138,7 +138,7 @@ int gemm_nt_f16_acc16_kernel(const void *A, const void *B, int64_t M, int64_t N,
 {
     if (!sizes_ok(M, N, K) || !bm || !bn || !lbytes)
         return GEMM_EINVAL;
-    const bool direct = load_bytes(A, B, K) == 16;
+    const bool direct = load_bytes(A, B, M, N, K) == 16;
     *lbytes = direct ? 16 : 1;
     acc16_dims(acc16_tile(M, N, direct), *bm, *bn);
     return GEMM_OK;

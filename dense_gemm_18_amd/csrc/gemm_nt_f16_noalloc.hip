@@ -62,7 +62,7 @@ int gemm_nt_f16_ws_noalloc(const void *A, const void *B, void *D, int64_t M, int
     const int rc = validate(A, B, D, M, N, K);
     if (rc != GEMM_OK)
         return rc;
-    const int lb = load_bytes(A, B, K);
+    const int lb = load_bytes(A, B, M, N, K);
     if (M == 0 || N == 0 || K == 0 || lb == 0)
         return gemm_nt_f16(A, B, D, M, N, K, stream);
     const Plan pl = make_plan(M, N, K, lb, device_cus());

@@ -322,9 +322,10 @@ int gemm_nt_f16_tile(int64_t M, int64_t N, int64_t K,
  * Host-only introspection (no HIP call) of the kernel a gemm_nt_f16 call
  * with these pointers and sizes takes (gemm_nt_bf16 and gemm_nt_f16_ex take
  * the same one): the output tile *bm x *bn; *load_bytes, how operand chunks
- * reach LDS (16: 16-byte loads straight into LDS, when K % 8 == 0 and A, B
- * are 16-byte aligned; 1: 16-byte loads into registers at any alignment,
- * then LDS writes, for every other K and alignment); *store, the
+ * reach LDS (16: 16-byte loads straight into LDS, at any 2-byte alignment,
+ * when K % 8 == 0 with A and B 16-byte aligned, and otherwise when K >= 8
+ * and M, N > 64; 1: 16-byte loads into registers, then LDS writes, for
+ * K < 8 and for M or N <= 64 with rows not 16-byte aligned); *store, the
  * epilogue's store form (0: element
  * stores; 1: 8-byte stores, D 8-byte aligned and N % 4 == 0; 2: whole tiles
  * staged through LDS and written with 16-byte stores, D 16-byte aligned and

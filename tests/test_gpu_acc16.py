@@ -61,14 +61,16 @@ def _run(A, B, **kw):
 
 # (M, N, K, a_off, b_off, tile, load bytes): the 256 x 256 (8 waves), 128 x 128
 # (four stages with at most 256 tiles, two beyond: 2300 x 2200) and 64 x 64
-# tiles with direct loads, and the register-staged 128 x 128 and 64 x 64
-# kernels (odd K, K % 8 != 0, 2-byte aligned operands)
+# tiles with direct loads, also at rows not 16-byte aligned (odd K, K % 8
+# != 0, 2-byte aligned operands; 2900 x 4100 x 521), and the register-staged
+# 128 x 128 and 64 x 64 kernels (K < 8; skinny shapes with such rows)
 CASES = [(2900, 4100, 512, 0, 0, 256, 16), (2900, 4100, 520, 0, 0, 256, 16),
          (1000, 1100, 576, 0, 0, 128, 16), (700, 900, 200, 0, 0, 128, 16),
          (2300, 2200, 264, 0, 0, 128, 16),
          (64, 3000, 448, 0, 0, 64, 16), (3000, 40, 200, 0, 0, 64, 16),
-         (1000, 1100, 577, 0, 0, 128, 1), (700, 900, 202, 0, 0, 128, 1),
-         (1000, 1100, 512, 1, 0, 128, 1), (700, 900, 200, 0, 3, 128, 1),
+         (1000, 1100, 577, 0, 0, 128, 16), (700, 900, 202, 0, 0, 128, 16),
+         (1000, 1100, 512, 1, 0, 128, 16), (700, 900, 200, 0, 3, 128, 16),
+         (2900, 4100, 521, 0, 0, 256, 16), (1000, 1100, 5, 0, 0, 128, 1),
          (64, 3000, 449, 0, 0, 64, 1), (3000, 40, 130, 2, 0, 64, 1)]
 
 
@@ -80,7 +82,8 @@ def test_acc16_integer(M, N, K, a_off, b_off, bm, lb):
     note(f"acc16 integer {M}x{N}x{K} a+{a_off} b+{b_off} tile {tbm}x{tbn} load {tlb}")
     d = _run(A, B, a_off=a_off, b_off=b_off)
     ref = oracle.gemm_nt_f16_acc16(A, B)
-    assert oracle.decode(ref).max() > 4096          # the fp16 running sum rounds
+    if K >= 128:
+        assert oracle.decode(ref).max() > 4096      # the fp16 running sum rounds
     assert_bitexact(d, ref, f"acc16 {M}x{N}x{K}")
 
 

@@ -6,7 +6,8 @@ alone, and that in turn equals the oracle (integer inputs, so the fp32 sums
 are exact and both sides round the same value once).
 
 The cases cover the 256 x 256, 128 x 128 and 64 x 64 direct-to-LDS tiles,
-the register-staged tiles, the fp16-accumulating and FP8 entry points, and
+rows that are not 16-byte aligned on the direct loads and on the register-
+staged ones, the fp16-accumulating and FP8 entry points, and
 the stream-K form.  The stream-K calls overlap the others but never each
 other: they share one workspace, and each grid expects to get every CU once
 the kernels around it finish, so all of them go on one stream, as the
@@ -49,8 +50,8 @@ class Case:
             A, B = wl.integer_free(seed, M, N, K, -2, 2)
             self.ref = oracle.gemm_nt_f16(A, B)
         if kind == "reg":
-            # K is odd for this kind: the register-staged kernel
-            assert K % 2 == 1
+            # odd K on a skinny shape: the register-staged kernel
+            assert K % 2 == 1 and min(M, N) <= 64
         self.dA = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8)).to(dev)
         self.dB = torch.from_numpy(np.ascontiguousarray(B).view(np.uint8)).to(dev)
         self.outs = [torch.empty((M, N), dtype=torch.int16, device=dev) for _ in range(ROUNDS)]
@@ -91,7 +92,8 @@ def cases():
     return [Case("256x256 tile", 2900, 4100, 512, 24001),
             Case("128x128 tile", 1000, 1100, 576, 24002),
             Case("64x64 tile", 64, 3000, 448, 24003),
-            Case("register-staged", 700, 900, 201, 24004, "reg"),
+            Case("unaligned rows", 700, 900, 201, 24004),
+            Case("register-staged", 64, 3000, 201, 24008, "reg"),
             Case("fp16 accumulation", 1000, 1100, 320, 24005, "acc16"),
             Case("fp8", 1000, 1100, 1024, 24006, "fp8"),
             Case("stream-K", 512, 640, 12352, 24007, "ws")]

@@ -126,7 +126,7 @@ def test_mn_sweep(M, N):
                                     (800, 2300, 72, 128), (2000, 700, 130, 128)])
 def test_tile_tails(M, N, K, bm):
     # ragged M, N and K on the 256 x 256 and the 128 x 128 tiles (K = 98 and
-    # 130 take the register-staged loads)
+    # 130: rows not 16-byte aligned, direct loads with the first-step fix-up)
     A, B = wl.integer_free(3000 + K, M, N, K)
     tbm, tbn, _, _ = binding.gemm_nt_f16_tile(M, N, K)
     assert tbm == bm
@@ -163,7 +163,7 @@ def test_staged_and_direct_epilogue(M, N, K):
 
 
 def test_random_small_general_path():
-    A, B = wl.uniform_inputs(77, 333, 222, 1001)     # K odd: register-staged loads
+    A, B = wl.uniform_inputs(77, 333, 222, 1001)     # K odd: rows 2-byte aligned
     note("random 333x222x1001")
     assert_tolerance(run_gemm(A, B), oracle.gemm_nt_f16(A, B), 1001, "odd K random")
 

@@ -1,17 +1,21 @@
-"""GPU parity of the kernels that serve odd K and 2-byte-aligned operands,
-at shapes that reach every tile they run on.
+"""GPU parity of the kernels that serve rows not 16-byte aligned (odd K,
+K % 8 != 0, or A or B offset by whole elements), at shapes that reach every
+tile they run on.
 
-Odd K, K % 8 != 0, or A or B not 16-byte aligned cannot use the
-direct-to-LDS loads; those calls load 16-byte chunks into registers at any
-alignment and write them to LDS, on whichever tile the shape picks.  Each
-case first asks the library which kernel it takes (``gemm_nt_f16_kernel``:
-tile and load mode, 1 = register-staged) and asserts the one it targets,
-then compares with the oracle: integer inputs
-bit for bit, random inputs within |D - D_ref| <= 2^-10 |D_ref| + 1e-3 sqrt(K)
-(the definition of page "构建 Tiled GEMM", section "GEMM"; the tolerance is
-the fp16 rounding step plus fp32 accumulation drift).  The same shapes go
-through the bfloat16 and fused-epilogue entry points, which share the
-kernel; FP8 operands with K % 4 != 0 or odd addresses take the same loads
+Such rows take the 16-byte direct-to-LDS loads too (gfx950 accepts 2-byte
+aligned addresses); in the first K-step each row's chunk that holds k = 0
+also holds elements of the row before, and is loaded into registers from
+the row's start, shifted and written over the zeros its direct load left.
+K < 8, and skinny shapes (M or N <= 64) with such rows, load 16-byte chunks
+into registers at any alignment and write them to LDS instead.  Each case
+first asks the library which kernel it takes (``gemm_nt_f16_kernel``: tile
+and load mode, 16 = direct, 1 = register-staged) and asserts the one it
+targets, then compares with the oracle: integer inputs bit for bit, random
+inputs within |D - D_ref| <= 2^-10 |D_ref| + 1e-3 sqrt(K) (the definition of
+page "构建 Tiled GEMM", section "GEMM"; the tolerance is the fp16 rounding
+step plus fp32 accumulation drift).  The same shapes go through the
+bfloat16 and fused-epilogue entry points, which share the kernels; FP8
+operands with K % 4 != 0 or odd addresses take the register-staged loads
 with K counted in bytes.
 """
 from __future__ import annotations
@@ -37,65 +41,74 @@ def _kernel(M, N, K, a_off=0, b_off=0, d_off=0):
                                       3 * ALIGNED + 2 * d_off, M, N, K)
 
 
-# (M, N, K, a_off, b_off, tile): odd K, K % 8 != 0 and 2- or 4-byte-aligned
-# operands on the 256 x 256 tile, plus the 128 x 128 and 64 x 64 tiles
-REG_CASES = [(2900, 4100, 97, 0, 0, 256), (3000, 5000, 2049, 0, 0, 256),
-             (2900, 4100, 64, 1, 0, 256), (2900, 4100, 64, 0, 1, 256),
-             (1100, 1100, 99, 0, 0, 128), (1100, 1100, 64, 1, 3, 128),
-             (64, 300, 37, 0, 0, 64), (300, 64, 64, 0, 1, 64),
-             (2900, 4100, 2050, 0, 0, 256), (2900, 4100, 2054, 2, 0, 256)]
+# (M, N, K, a_off, b_off, tile, load): rows not 16-byte aligned on the
+# direct loads (odd K, K % 8 != 0, 2- or 4-byte aligned operands; K = 8 and
+# 9, the shortest rows that take them) on the 256 x 256 (both B rings),
+# 128 x 128 (four and two stages) and 64 x 64 tiles, then the register-
+# staged kernels: K < 8 on every tile and skinny shapes
+CASES = [(2900, 4100, 97, 0, 0, 256, 16), (3000, 5000, 2049, 0, 0, 256, 16),
+         (2900, 4100, 64, 1, 0, 256, 16), (2900, 4100, 64, 0, 1, 256, 16),
+         (2900, 4100, 2050, 0, 0, 256, 16), (2900, 4100, 2054, 2, 0, 256, 16),
+         (2900, 4100, 9, 0, 0, 256, 16), (1100, 1100, 99, 0, 0, 128, 16),
+         (1100, 1100, 64, 1, 3, 128, 16), (1000, 1100, 9, 0, 0, 128, 16),
+         (1000, 1100, 8, 1, 0, 128, 16), (2100, 2200, 201, 0, 0, 128, 16),
+         (300, 200, 130, 0, 0, 64, 16), (700, 900, 202, 0, 0, 64, 16),
+         (2900, 4100, 7, 0, 0, 256, 1), (1100, 1100, 5, 0, 0, 128, 1),
+         (300, 200, 3, 0, 0, 64, 1), (64, 300, 37, 0, 0, 64, 1), (300, 64, 64, 0, 1, 64, 1),
+         (8192, 64, 1025, 2, 0, 64, 1)]
 
 
-@pytest.mark.parametrize("M,N,K,a_off,b_off,bm", REG_CASES)
-def test_register_staged_integer(M, N, K, a_off, b_off, bm):
-    tbm, tbn, lb, _ = _kernel(M, N, K, a_off, b_off)
-    assert (tbm, lb) == (bm, 1), (tbm, tbn, lb)
+@pytest.mark.parametrize("M,N,K,a_off,b_off,bm,lb", CASES)
+def test_unaligned_rows_integer(M, N, K, a_off, b_off, bm, lb):
+    tbm, tbn, tlb, _ = _kernel(M, N, K, a_off, b_off)
+    assert (tbm, tlb) == (bm, lb), (tbm, tbn, tlb)
     A, B = wl.integer_free(15000 + K + a_off + 7 * b_off, M, N, K)
-    note(f"register-staged integer {M}x{N}x{K} a+{a_off} b+{b_off} tile {tbm}x{tbn}")
+    note(f"unaligned rows integer {M}x{N}x{K} a+{a_off} b+{b_off} tile {tbm}x{tbn} load {tlb}")
     assert_bitexact(run_gemm(A, B, a_off=a_off, b_off=b_off), oracle.gemm_nt_f16(A, B),
                     f"{M}x{N}x{K} a+{a_off} b+{b_off}")
 
 
-@pytest.mark.parametrize("M,N,K,a_off,b_off,bm", [REG_CASES[0], REG_CASES[1], REG_CASES[2]])
-def test_register_staged_random(M, N, K, a_off, b_off, bm):
-    tbm, tbn, lb, _ = _kernel(M, N, K, a_off, b_off)
-    assert (tbm, lb) == (bm, 1), (tbm, tbn, lb)
+@pytest.mark.parametrize("M,N,K,a_off,b_off,bm,lb", [CASES[0], CASES[1], CASES[2], CASES[7],
+                                                     CASES[14], CASES[17]])
+def test_unaligned_rows_random(M, N, K, a_off, b_off, bm, lb):
+    tbm, tbn, tlb, _ = _kernel(M, N, K, a_off, b_off)
+    assert (tbm, tlb) == (bm, lb), (tbm, tbn, tlb)
     A, B = wl.uniform_inputs(15500 + K, M, N, K)
-    note(f"register-staged random {M}x{N}x{K} a+{a_off} b+{b_off} tile {tbm}x{tbn}")
+    note(f"unaligned rows random {M}x{N}x{K} a+{a_off} b+{b_off} tile {tbm}x{tbn} load {tlb}")
     assert_tolerance(run_gemm(A, B, a_off=a_off, b_off=b_off), oracle.gemm_nt_f16(A, B), K,
                      f"{M}x{N}x{K} random")
 
 
-def test_register_staged_ragged_workload_odd_k():
+def test_unaligned_rows_ragged_workload_odd_k():
     # the ragged workload's distribution (N(0,1)/sqrt(K) on both operands)
-    # with K one less, so that it takes the register-staged 256 x 256 kernel
+    # with K one less (odd: 2-byte aligned rows) on the 256 x 256 tile
     w = wl.WORKLOADS["ragged_3000x5000x2050"]
     K = w.K - 1
-    assert _kernel(w.M, w.N, K)[:3] == (256, 256, 1)
+    assert _kernel(w.M, w.N, K)[:3] == (256, 256, 16)
     rng = np.random.default_rng(w.seeds[0])
     A = (rng.standard_normal((w.M, K)) / math.sqrt(K)).astype(np.float16)
     B = (rng.standard_normal((w.N, K)) / math.sqrt(K)).astype(np.float16)
-    note(f"register-staged ragged {w.M}x{w.N}x{K}")
+    note(f"unaligned rows ragged {w.M}x{w.N}x{K}")
     assert_tolerance(run_gemm(A, B), oracle.gemm_nt_f16(A, B), K, "ragged odd K")
 
 
-@pytest.mark.parametrize("M,N,K,a_off,b_off,bm", [REG_CASES[0], REG_CASES[1], REG_CASES[4],
-                                                  REG_CASES[6]])
-def test_register_staged_bf16_integer(M, N, K, a_off, b_off, bm):
-    assert _kernel(M, N, K)[0::2] == (bm, 1)
+@pytest.mark.parametrize("M,N,K,a_off,b_off,bm,lb", [CASES[0], CASES[1], CASES[7], CASES[12],
+                                                     CASES[14], CASES[17]])
+def test_unaligned_rows_bf16_integer(M, N, K, a_off, b_off, bm, lb):
+    assert _kernel(M, N, K)[0::2] == (bm, lb)
     A, B = wl.bf16_integers(15700 + K, M, N, K)
-    note(f"register-staged bf16 integer {M}x{N}x{K}")
+    note(f"unaligned rows bf16 integer {M}x{N}x{K} load {lb}")
     d = run_gemm_bf16(A, B)
     ref = oracle.gemm_nt_bf16(A, B)
     diff = np.flatnonzero(d != ref)
     assert diff.size == 0, f"{diff.size} entries differ, first {diff[:5]}"
 
 
-def test_register_staged_bf16_random():
+def test_unaligned_rows_bf16_random():
     M, N, K = 2900, 4100, 97
-    assert _kernel(M, N, K)[0::2] == (256, 1)
+    assert _kernel(M, N, K)[0::2] == (256, 16)
     A, B = wl.bf16_uniform(15800, M, N, K)
-    note(f"register-staged bf16 random {M}x{N}x{K}")
+    note(f"unaligned rows bf16 random {M}x{N}x{K}")
     g = oracle.bf16_decode(run_gemm_bf16(A, B))
     r = oracle.bf16_decode(oracle.gemm_nt_bf16(A, B))
     bad = np.flatnonzero(~(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3 * math.sqrt(K)))
@@ -110,27 +123,28 @@ def _epi_operands(seed, M, N, K):
     return A, B, C, bias
 
 
-@pytest.mark.parametrize("M,N,K,bm", [(2900, 4100, 97, 256), (3000, 5000, 2049, 256),
-                                      (1100, 1100, 99, 128), (64, 300, 37, 64),
-                                      (300, 64, 45, 64)])
-def test_register_staged_epilogue_integer(M, N, K, bm):
-    assert _kernel(M, N, K)[0::2] == (bm, 1)
+@pytest.mark.parametrize("M,N,K,bm,lb", [(2900, 4100, 97, 256, 16), (3000, 5000, 2049, 256, 16),
+                                         (1100, 1100, 99, 128, 16), (300, 200, 130, 64, 16),
+                                         (2900, 4100, 7, 256, 1), (64, 300, 37, 64, 1),
+                                         (300, 64, 45, 64, 1)])
+def test_unaligned_rows_epilogue_integer(M, N, K, bm, lb):
+    assert _kernel(M, N, K)[0::2] == (bm, lb)
     A, B, C, bias = _epi_operands(16000 + K, M, N, K)
-    note(f"register-staged epilogue integer {M}x{N}x{K}")
+    note(f"unaligned rows epilogue integer {M}x{N}x{K} load {lb}")
     d = run_gemm_ex(A, B, C, bias, 2.0, -1.0)
     ref = oracle.gemm_nt_f16_ex(A, B, C, bias, 2.0, -1.0)
     assert np.abs(oracle.decode(ref)).max() < 2048
     assert_bitexact(d, ref, f"epilogue {M}x{N}x{K}")
 
 
-def test_register_staged_epilogue_random():
+def test_unaligned_rows_epilogue_random():
     M, N, K = 2900, 4100, 97
-    assert _kernel(M, N, K)[0::2] == (256, 1)
+    assert _kernel(M, N, K)[0::2] == (256, 16)
     A, B = wl.uniform_inputs(16100, M, N, K)
     rng = np.random.default_rng(16101)
     C = rng.normal(size=(M, N)).astype(np.float16)
     bias = rng.normal(size=N).astype(np.float16)
-    note(f"register-staged epilogue random {M}x{N}x{K}")
+    note(f"unaligned rows epilogue random {M}x{N}x{K}")
     d = run_gemm_ex(A, B, C, bias, 0.7, -1.3)
     assert_tolerance(d, oracle.gemm_nt_f16_ex(A, B, C, bias, 0.7, -1.3), K,
                      "epilogue random odd K", scale=0.7)

@@ -85,9 +85,9 @@ def test_schedule_covers_each_step_once(M, N, K):
     (1024, 1024, 12224, 64, 0),      # 191 K-steps
     (1024, 1024, 12288, 128, 64),
     (1024, 1024, 16384, 128, 64),
-    (900, 1000, 12290, 128, 64),     # 4-byte loads
+    (900, 1000, 12290, 128, 64),     # K % 8 != 0: the same 16-byte loads
     (64, 16384, 8192, 64, 0),        # thin tiles never split
-    (1024, 1024, 16383, 64, 0),      # odd K: register-staged path, no stream-K
+    (1024, 1024, 16383, 128, 64),    # odd K as well
 ])
 def test_plan_choice(M, N, K, bm, sk):
     got = binding.gemm_nt_f16_ws_tile(M, N, K)

@@ -25,13 +25,15 @@
 //     serves both.  Each lane moves 16-byte chunks (8 fp16 along K); 8 lanes
 //     cover one 128-byte row of a K-step, so the accesses are fully
 //     coalesced (page 1, "内核 1：共享内存分块", shows the cooperative
-//     coalesced tile copy).  With K % 8 == 0 and 16-byte aligned operands
-//     the chunks go straight to LDS (buffer loads that write LDS); otherwise
-//     they are loaded into registers at whatever alignment the rows have and
+//     coalesced tile copy).  The chunks go straight to LDS (buffer loads
+//     that write LDS), also where rows start only 2-byte aligned (odd K,
+//     K % 8 != 0, operands offset by whole elements); for K < 8, and for
+//     skinny shapes with such rows, they are loaded into registers and
 //     written to the same LDS bytes.  The buffer resource of each workgroup
 //     spans only its valid rows, so rows past M or N read as zero in
 //     hardware; with a K tail the K-steps are aligned to K's end, so only the
-//     first step's loads carry a K mask.
+//     first step's loads carry a K mask (and, when K % 8 != 0, each row's
+//     chunk that holds k = 0 is rewritten from registers).
 //   * LDS layout: rows of 64 fp16 (128 B = eight 16-byte chunks), chunk index
 //     XOR-swizzled by the row so that the MFMA fragment reader is free of
 //     bank conflicts (page 1, "为什么 swizzle 重要", explains the conflict
@@ -618,7 +620,9 @@ struct DmaCfg {
     // REG: the same 16-byte chunks, loaded into registers at any alignment
     // (gfx950's vector memory loads take unaligned addresses) and written to
     // LDS with ds_write_b128 at the byte the direct-to-LDS load would fill;
-    // serves any K and any 2-byte-aligned operands.  Each chunk is loaded
+    // serves any K and any 2-byte-aligned operands (used for K < 8, skinny
+    // shapes whose rows are not 16-byte aligned, and FP8 rows at any byte
+    // alignment).  Each chunk is loaded
     // one step ahead of its LDS write, and the register is reloaded right
     // after the write, so every load has a full step to land wherever the
     // write sits in the step.  The writes of a step are spread evenly over
@@ -1604,14 +1608,17 @@ using ThinMDma = DmaCfg<32, 64, 1, 2, 64, 10, 16, 16, false>;
 // as many load instructions per step, so fewer stages keep the waits
 // encodable.
 using ThinDma4 = DmaCfg<64, 64, 2, 2, 64, 4, 16, 4, false>;
-// Register-staged 16-byte chunks (any K, operands 2-byte aligned): two
-// stages, each chunk loaded a step ahead into registers.  The 256 x 256 tile
+// Register-staged 16-byte chunks (any K, operands 2-byte aligned; taken for
+// K < 8 and for skinny shapes whose rows are not 16-byte aligned, see
+// load_bytes): two stages, each chunk loaded a step ahead into registers.
+// The 256 x 256 tile
 // runs 8 waves of 128 x 64 on 32x32x16 MFMAs, two per SIMD, each with its
 // accumulators, fragments and 32 staging registers in 250 arch VGPRs: while
 // one wave waits for a chunk the other multiplies.  Measured on MI355X
 // (TFLOP/s, 8 waves / 4 waves of 128 x 128 with 64 staging registers):
 // 3000 x 5000 x 2050 896 / 858, x 2049 871 / 833, 8192^2 x 8194 1170 / 1162,
-// 4096^2 x 4097 1037 / 1025.  (4 waves with 16x16x32 blocks spill.)
+// 4096^2 x 4097 1037 / 1025, when those shapes still ran here.  (4 waves
+// with 16x16x32 blocks spill.)
 using BigReg = DmaCfg<256, 256, 2, 4, 64, 2, 32, 16, false, true>;
 using MidReg = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false, true>;
 using ThinReg = DmaCfg<64, 64, 2, 2, 64, 2, 16, 16, false, true>;

@@ -29,8 +29,8 @@ using H16Big = DmaCfg<256, 256, 2, 4, 64, 2, 16, 16, false>;
 using H16Mid = DmaCfg<128, 128, 2, 4, 64, 2, 16, 16, false>;
 using H16Mid4 = DmaCfg<128, 128, 2, 4, 64, 4, 16, 16, false>;
 using H16Thin = DmaCfg<64, 64, 2, 2, 64, 8, 16, 16, false>;
-// Register-staged 16-byte chunks (K % 8 != 0 or operands only 2-byte
-// aligned); 128 x 128 at 825 TFLOP/s on 8192^3 with aligned operands.
+// Register-staged 16-byte chunks (K < 8, or skinny shapes whose rows are not
+// 16-byte aligned); 128 x 128 at 825 TFLOP/s on 8192^3 with aligned operands.
 using H16MidReg = DmaCfg<128, 128, 2, 2, 64, 2, 16, 16, false, true>;
 using H16ThinReg = DmaCfg<64, 64, 2, 2, 64, 2, 16, 16, false, true>;
 

@@ -92,11 +92,18 @@ void launch_fp8_reg(const void *A, const void *B, void *D, int M, int N, int K, 
 }
 
 // Bytes each lane moves per direct-to-LDS load for FP8 operands with K
-// bytes per row: 16, 4, or 0 (register staging).
-int fp8_load_bytes(const void *A, const void *B, int64_t K)
+// bytes per row: 16, 4, or 0 (register staging).  The 16-byte loads take
+// rows that start 16-byte aligned and, as for 16-bit operands, rows that
+// start 2-byte aligned (K even, operands 2-byte aligned) on shapes with
+// M, N > 64 and at least eight byte pairs per row (the kernel then counts K
+// in byte pairs, and the first K-step's chunk that holds k = 0 is rewritten
+// from registers).
+int fp8_load_bytes(const void *A, const void *B, int64_t M, int64_t N, int64_t K)
 {
     const uintptr_t ab = (uintptr_t)A | (uintptr_t)B;
     if (K % 16 == 0 && (ab & 15u) == 0)
+        return 16;
+    if (K % 2 == 0 && (ab & 1u) == 0 && K >= 16 && M > 64 && N > 64)
         return 16;
     if (K % 4 == 0 && (ab & 3u) == 0)
         return 4;
@@ -120,7 +127,7 @@ void launch_fp8(const void *A, const void *B, void *D, int64_t M, int64_t N, int
                 float scale, const float *col_scale, hipStream_t s)
 {
     const Epi epi{nullptr, nullptr, scale, 0.0f, col_scale};
-    const int lb = fp8_load_bytes(A, B, K);
+    const int lb = fp8_load_bytes(A, B, M, N, K);
     const int vec = store_mode(D, N);
     const int m = (int)M, n = (int)N, kp = (int)(K / 2);
     const Tile t = fp8_tile(M, N, K, lb);

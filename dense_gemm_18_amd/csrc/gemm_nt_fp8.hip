@@ -67,7 +67,9 @@ int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, in
 {
     if (!sizes_ok(M, N, K) || !bm || !bn)
         return GEMM_EINVAL;
-    const int lb = K % 16 == 0 && aligned16 ? 16 : (K % 4 == 0 ? 4 : 0);
+    // stand-in addresses with the alignment asked about (4-byte otherwise)
+    const void *p = (const void *)(uintptr_t)(aligned16 ? 0x1000 : 0x1004);
+    const int lb = fp8_load_bytes(p, p, M, N, K);
     tile_dims(fp8_tile(M, N, K, lb), *bm, *bn);
     return GEMM_OK;
 }

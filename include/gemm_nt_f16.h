@@ -137,10 +137,12 @@ int gemm_nt_f16_acc16_kernel(const void *A, const void *B, int64_t M, int64_t N,
  *   Products are exact and summed in fp32; the sum is multiplied by scale in
  *   fp32 and rounded once to fp16 (round to nearest even).  K == 0 gives
  *   scale * (+0).
- * Load paths: K % 16 == 0 with A and B 16-byte aligned loads straight into
- *   LDS (then K % 4 == 0 with 4-byte alignment, 4 bytes per lane); anything
- *   else loads 16-byte chunks into registers at any alignment and writes
- *   them to LDS (128 x 128 or 64 x 64 tiles), all on the FP8 MFMA.
+ * Load paths: 16-byte loads straight into LDS when K % 16 == 0 with A and
+ *   B 16-byte aligned, and when K is even (K >= 16) with A and B 2-byte
+ *   aligned and M, N > 64; then 4 bytes per lane when K % 4 == 0 with
+ *   4-byte alignment; anything else loads 16-byte chunks into registers at
+ *   any alignment and writes them to LDS (128 x 128 or 64 x 64 tiles), all
+ *   on the FP8 MFMA.
  *
  * Returns as gemm_nt_f16 (sizes M, N, K in [0, 2^31 - 1], K <= GEMM_MAX_K),
  * and GEMM_EINVAL also for an unknown format or D overlapping A or B.
@@ -174,7 +176,7 @@ int gemm_nt_fp8_cs(const void *A, const void *B, void *D, int64_t M, int64_t N, 
 /*
  * Host-only: the output tile gemm_nt_fp8 uses for these sizes (aligned16:
  * whether A and B are 16-byte aligned; 4-byte alignment is assumed
- * otherwise; with K % 4 != 0 the tile of the register-staged loads).
+ * otherwise), following the load paths above.
  * GEMM_EINVAL for sizes out of the entry points' range or NULL outputs.
  */
 int gemm_nt_fp8_tile(int64_t M, int64_t N, int64_t K, int aligned16, int *bm, int *bn);

@@ -254,10 +254,12 @@ def test_fp8_cs_empty_output_needs_no_scales():
     (8192, 8192, 8192, True, (256, 256)),
     (2048, 2048, 4096, True, (128, 128)),
     (64, 4096, 4096, True, (64, 64)),
-    (8192, 8192, 8196, True, (128, 128)),    # K % 16 != 0: 4-byte loads, no 256 x 256 tile
-    (8192, 8192, 8192, False, (128, 128)),   # operands only 4-byte aligned
-    (40, 8192, 8196, True, (64, 64)),
-    (300, 200, 130, True, (128, 128)),       # K % 4 != 0: register staging
+    (8192, 8192, 8196, True, (256, 256)),    # K % 16 != 0: 16-byte loads at 4-byte aligned rows
+    (8192, 8192, 8194, True, (256, 256)),    # K % 4 != 0, K even: the same
+    (8192, 8192, 8192, False, (256, 256)),   # operands only 4-byte aligned
+    (40, 8192, 8196, True, (64, 64)),        # skinny: 4-byte loads
+    (300, 200, 130, True, (128, 128)),
+    (1100, 1100, 1031, True, (128, 128)),    # odd K: register staging
     (50, 300, 131, True, (64, 64)),
 ])
 def test_fp8_tile_choice(M, N, K, aligned, tile):

@@ -30,12 +30,14 @@ pytestmark = pytest.mark.gpu
 
 E4, E5 = binding.GEMM_FP8_E4M3, binding.GEMM_FP8_E5M2
 
-# 256x256 (K tail inside a step), 128x128, 64x64, 128x128 with 4-byte loads,
-# 64x64 with 4-byte loads, register staging (K % 4 == 2, K odd), one step,
-# two-stage 128x128 (more tiles than CUs, K tail inside a step)
+# 256x256 (K tail inside a step), 128x128, 64x64, 16-byte loads at rows that
+# start 4- or 2-byte aligned (K % 16 == 4 and 2: 700 x 900 x 4100, 300 x 200
+# x 130, 2900 x 4100 x 1026), 64x64 with 4-byte loads (skinny), register
+# staging (K odd), one step, two-stage 128x128 (more tiles than CUs, K tail
+# inside a step)
 SHAPES = [(2900, 4100, 400), (1100, 1100, 1024), (64, 300, 512), (700, 900, 4100),
           (50, 300, 260), (300, 200, 130), (150, 97, 37), (256, 256, 128),
-          (2100, 2200, 528)]
+          (2100, 2200, 528), (2900, 4100, 1026)]
 
 
 def _ref(A, B, scale, fa, fb):
@@ -71,7 +73,7 @@ def test_fp8_format_pairs(fa, fb, M, N, K):
                     f"fp8 integer {fa},{fb} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("a_off,b_off", [(4, 0), (0, 12), (1, 0), (0, 3)])
+@pytest.mark.parametrize("a_off,b_off", [(4, 0), (0, 12), (2, 6), (1, 0), (0, 3)])
 def test_fp8_misaligned_operands(a_off, b_off):
     M, N, K = 500, 600, 1024
     A, B = wl.fp8_integers(12400 + a_off, M, N, K)

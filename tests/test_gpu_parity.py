@@ -84,6 +84,28 @@ def test_headline_8192_sampled(variant):
         assert_tolerance(got, ref, w.K, f"{w.name} random sampled")
 
 
+@pytest.mark.parametrize("K,a_off", [(8191, 0), (8194, 0), (8192, 1)])
+def test_large_unaligned_rows_sampled(K, a_off):
+    # 8192 x 8192 with rows that do not start 16-byte aligned (odd K, K % 8
+    # == 2, A offset by one element): the 256 x 256 direct-load kernel with
+    # the first-step fix-up and three B stages; integer inputs, 4096 sampled
+    # entries plus full rows and columns at tile edges, bit-exact
+    M = N = 8192
+    assert binding.gemm_nt_f16_kernel((1 << 20) + 2 * a_off, 2 << 20, 3 << 20, M, N, K)[:3] == \
+        (256, 256, 16)
+    A, B = wl.integer_free(8300 + K + a_off, M, N, K)
+    note(f"large unaligned rows {M}x{N}x{K} a+{a_off}")
+    d = run_gemm(A, B, a_off=a_off)
+    rng = np.random.default_rng(8400 + K)
+    idx = rng.choice(M * N, 4096, replace=False)
+    er, ec = wl.edge_lines(M, 256), wl.edge_lines(N, 256)
+    rows = np.concatenate([idx // N, np.repeat(er, N), np.tile(np.arange(M), ec.size)])
+    cols = np.concatenate([idx % N, np.tile(np.arange(N), er.size), np.repeat(ec, M)])
+    ref = oracle.gemm_nt_f16_entries(A, B, rows, cols)
+    assert np.abs(oracle.decode(ref)).max() <= 2048
+    assert_bitexact(d[rows, cols], ref, f"{M}x{N}x{K} a+{a_off} sampled")
+
+
 def test_permutation_lane_maps():
     # Permutation operands make any row/column mis-map of the MFMA lanes or
     # the epilogue visible bit for bit (128 x 128 x 64, one tile).

@@ -24,7 +24,8 @@ SHAPES = [
     (1024, 1024, 12288),     # 64 tiles, 3 contributors each
     (768, 768, 12288),       # 36 tiles, pieces cross tile boundaries
     (512, 640, 16384),       # 20 tiles, up to 12 contributors each
-    (900, 1000, 12290),      # ragged M, N; 4-byte loads and a K tail
+    (900, 1000, 12290),      # ragged M, N; rows 4-byte aligned, a K tail
+    (512, 640, 12351),       # odd K: rows 2-byte aligned, first-step fix-up
     (768, 1024, 12296),      # 16-byte loads and a K tail (only step 0 masked)
     (100, 8192, 32768),      # one tile row, K = 32768
 ]

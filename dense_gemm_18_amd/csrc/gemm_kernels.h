@@ -140,7 +140,10 @@ __device__ __forceinline__ f32x4 mfma_f8(i32x8 b, i32x8 a, f32x4 c)
 // six, and with one wave per SIMD already issuing the MFMAs the VALU issue
 // slots are what bounds this kernel.  b and a hold the lane's two 8-element
 // K groups of the step (the first for the step's first 32 K).
-__device__ __forceinline__ f16x4 mma_acc16(i32x8 b, i32x8 a, f16x4 s)
+// The kernel issues the two halves separately (mma_chunk16, then
+// acc16_add one block later), so that a block's conversions and adds run
+// under the next block's MFMAs instead of waiting for its own.
+__device__ __forceinline__ f32x4 mma_chunk16(i32x8 b, i32x8 a)
 {
     const f16x8 b0 = __builtin_bit_cast(f16x8, __builtin_shufflevector(b, b, 0, 1, 2, 3));
     const f16x8 b1 = __builtin_bit_cast(f16x8, __builtin_shufflevector(b, b, 4, 5, 6, 7));
@@ -148,8 +151,17 @@ __device__ __forceinline__ f16x4 mma_acc16(i32x8 b, i32x8 a, f16x4 s)
     const f16x8 a1 = __builtin_bit_cast(f16x8, __builtin_shufflevector(a, a, 4, 5, 6, 7));
     f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(b0, a0, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
                                                      0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, a1, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b1, a1, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x4 acc16_add(f16x4 s, f32x4 c)
+{
     return s + __builtin_convertvector(c, f16x4);
+}
+
+__device__ __forceinline__ f16x4 mma_acc16(i32x8 b, i32x8 a, f16x4 s)
+{
+    return acc16_add(s, mma_chunk16(b, a));
 }
 
 constexpr int kBK = 64;            // K elements per LDS row: 128 B, 8 chunks
@@ -1070,6 +1082,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // h: (whole-step fragments) which half of the block rows this slice
     // multiplies.
     // cur, nxt: fragment sets (integral constants) multiplied and read.
+    f32x4 pend;     // (H16) the chunk sum of the block multiplied last
     auto slice = [&](auto cur, auto nxt,
                      auto do_read, auto rs, auto rt, auto do_load, int lstep, auto ls,
                      auto l0, auto hc) G18_INLINE {
@@ -1081,8 +1094,19 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             using QB = std::integral_constant<int, C::TM + j>;
             if constexpr (F8 != 0)
                 acc[i][j] = mfma_f8<F8>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
-            else if constexpr (H16)
-                acc[i][j] = mma_acc16(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
+            else if constexpr (H16) {
+                // this block's chunk sum; the previous block's fp16 update
+                // now, under these MFMAs; the slice's last block at its end
+                const f32x4 c = mma_chunk16(frag(cur, QB{}), frag(cur, QA{}));
+                __builtin_amdgcn_sched_barrier(0);     // both MFMAs first
+                if constexpr (p > 0) {
+                    constexpr int qp = q - 1;
+                    acc[qp / C::TN][qp % C::TN] = acc16_add(acc[qp / C::TN][qp % C::TN], pend);
+                }
+                pend = c;
+                if constexpr (p == NMS - 1)
+                    acc[i][j] = acc16_add(acc[i][j], pend);
+            }
             else if constexpr (C::MF == 32)
                 acc[i][j] = mfma32<BF>(frag(cur, QB{}), frag(cur, QA{}), acc[i][j]);
             else

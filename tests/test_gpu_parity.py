@@ -106,6 +106,49 @@ def test_large_unaligned_rows_sampled(K, a_off):
     assert_bitexact(d[rows, cols], ref, f"{M}x{N}x{K} a+{a_off} sampled")
 
 
+def test_max_k():
+    # K = GEMM_MAX_K (4194303, odd: rows 2-byte aligned, the first K-step's
+    # fix-up; 65536 K-steps) at 300 x 300, through the plain entry point
+    # (64 x 64 tiles) and the stream-K form (128 x 128 tiles split by
+    # K-steps); integer inputs in {-1, 0, 1}, whose fp32 sums stay exact,
+    # checked bit for bit at 256 sampled entries and the corners.  (Operand
+    # offsets near 2^31 bytes need 256-row tiles, which this library picks
+    # only for shapes of tens of GB at this K.)
+    import torch
+    M = N = 300
+    K = binding.GEMM_MAX_K
+    rng = np.random.default_rng(8700)
+    A = rng.integers(-1, 2, size=(M, K), dtype=np.int8).astype(np.float16)
+    B = rng.integers(-1, 2, size=(N, K), dtype=np.int8).astype(np.float16)
+    idx = rng.choice(M * N, 256, replace=False)
+    rows = np.concatenate([idx // N, [0, 0, M - 1, M - 1, 63, 64]])
+    cols = np.concatenate([idx % N, [0, N - 1, 0, N - 1, 64, 63]])
+    ref = oracle.gemm_nt_f16_entries(A, B, rows, cols)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    del A, B
+    dD = torch.empty((M, N), dtype=torch.float16, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    note(f"max K {M}x{N}x{K} plain")
+    assert binding.gemm_nt_f16(dA.data_ptr(), dB.data_ptr(), dD.data_ptr(), M, N, K, s) == \
+        binding.GEMM_OK
+    torch.cuda.synchronize(dev)
+    got = dD.cpu().numpy().view(np.uint16)
+    assert_bitexact(got[rows, cols], ref, "max K plain")
+    need = binding.gemm_nt_f16_ws_size(M, N, K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    dD.fill_(0)
+    note(f"max K {M}x{N}x{K} stream-K")
+    assert binding.gemm_nt_f16_ws(dA.data_ptr(), dB.data_ptr(), dD.data_ptr(), M, N, K,
+                                  ws.data_ptr(), need, s) == binding.GEMM_OK
+    torch.cuda.synchronize(dev)
+    got = dD.cpu().numpy().view(np.uint16)
+    assert_bitexact(got[rows, cols], ref, "max K stream-K")
+    assert ws[:256].view(torch.int32)[2].item() == 0, "a stream-K wait timed out"
+
+
 def test_permutation_lane_maps():
     # Permutation operands make any row/column mis-map of the MFMA lanes or
     # the epilogue visible bit for bit (128 x 128 x 64, one tile).

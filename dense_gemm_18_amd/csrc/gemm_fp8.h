@@ -48,7 +48,7 @@ void launch_fp8_dma(const void *A, const void *B, void *D, int M, int N, int Kp,
     auto go = [&](auto ktail, auto ntc) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<C, decltype(ktail)::value, false, true, false, F8, 2,
                                                decltype(ntc)::value>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           tile_grid((int64_t)tm * tn), dim3(C::THREADS), 0, s, (const T *)A,
                            (const T *)B, (T *)D, M, N, Kp, tm, tn, vec, none, epi);
     };
     // As for 16-bit operands: an operand read once per call (one tile row:
@@ -83,11 +83,11 @@ void launch_fp8_reg(const void *A, const void *B, void *D, int M, int N, int K, 
     const SkPlan none{};
     if (K % C::ROW_BYTES == 0)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<C, false, false, true, false, F8, 1>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           tile_grid((int64_t)tm * tn), dim3(C::THREADS), 0, s, (const T *)A,
                            (const T *)B, (T *)D, M, N, K, tm, tn, vec, none, epi);
     else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<C, true, false, true, false, F8, 1>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           tile_grid((int64_t)tm * tn), dim3(C::THREADS), 0, s, (const T *)A,
                            (const T *)B, (T *)D, M, N, K, tm, tn, vec, none, epi);
 }
 

@@ -839,7 +839,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void *)A, (short)0, 0, kRsrcFlags);
     const int nk = (K + BKU - 1) / BKU;
-    auto set_item = [&](int tile, int s0, int s1) G18_INLINE {
+    auto set_item = [&](int64_t tile, int s0, int s1) G18_INLINE {
         int64_t tm64, tn64;
         tile_coord(tile, tiles_m, tiles_n, tm64, tn64);
         m0 = (int)tm64 * C::BM;
@@ -1387,7 +1387,13 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             lds_barrier();             // every wave is done with the LDS stages
             set_item(it.tile, it.s0, it.s1);
         } else {
-            set_item(blockIdx.x, 0, nk);
+            // one tile per workgroup; a grid of more tiles than one grid
+            // dimension holds spreads over y, and workgroups past the last
+            // tile end here, before any barrier
+            const int64_t tile = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+            if (tile >= (int64_t)tiles_m * tiles_n)
+                return;
+            set_item(tile, 0, nk);
         }
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -1746,18 +1752,29 @@ EpiArg<EPI> epi_arg(const Epi &e)
         return NoEpi{};
 }
 
+// Grid of a one-tile-per-workgroup launch: at least `tiles` workgroups.  A
+// grid dimension holds at most 2^32 - 1 work-items, so tile counts above
+// 2^22 (workgroups of up to 512 lanes) spread over y; the kernel numbers its
+// tile blockIdx.x + blockIdx.y * gridDim.x and skips those past the last.
+inline dim3 tile_grid(int64_t tiles)
+{
+    constexpr int64_t kMaxX = int64_t(1) << 22;
+    if (tiles <= kMaxX)
+        return dim3((unsigned)tiles);
+    return dim3((unsigned)kMaxX, (unsigned)cdiv(tiles, kMaxX));
+}
+
 template <class C, bool SK, bool EPI, bool BF>
 void launch_dma(const void *A, const void *B, void *D, int M, int N, int K, int vec, hipStream_t s,
                 const SkPlan &sk, int grid, const Epi &epi)
 {
     using T = typename Elem<BF>::T;
     const int tm = (int)cdiv(M, C::BM), tn = (int)cdiv(N, C::BN);
-    if (!SK)
-        grid = tm * tn;
+    const dim3 g = SK ? dim3((unsigned)grid) : tile_grid((int64_t)tm * tn);
     auto go = [&](auto ktail, auto ntc) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<C, decltype(ktail)::value, SK, EPI, BF, 0, 2,
                                                decltype(ntc)::value>),
-                           dim3((unsigned)grid), dim3(C::THREADS), 0, s, (const T *)A,
+                           g, dim3(C::THREADS), 0, s, (const T *)A,
                            (const T *)B, (T *)D, M, N, K, tm, tn, vec, sk, epi_arg<EPI>(epi));
     };
     auto go_nt = [&](auto ktail) {

@@ -62,7 +62,7 @@ void launch_acc16(const void *A, const void *B, void *D, int M, int N, int K, hi
     auto go = [&](auto ktail, auto ntc) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<C, decltype(ktail)::value, false, false, false, 0, 2,
                                                decltype(ntc)::value, true>),
-                           dim3((unsigned)(tm * tn)), dim3(C::THREADS), 0, s, (const T *)A,
+                           tile_grid((int64_t)tm * tn), dim3(C::THREADS), 0, s, (const T *)A,
                            (const T *)B, (T *)D, M, N, K, tm, tn, vec, none, NoEpi{});
     };
     // An operand read once per call (one tile row: B; one tile column: A)

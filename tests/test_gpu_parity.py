@@ -149,6 +149,49 @@ def test_max_k():
     assert ws[:256].view(torch.int32)[2].item() == 0, "a stream-K wait timed out"
 
 
+@pytest.mark.parametrize("path", ["f16", "acc16", "fp8"])
+def test_max_m(path):
+    # M = 2^31 - 1 rows (33.5 million 64 x 64 tiles, more workgroups than one
+    # grid dimension holds; D 8 GB, so its byte offsets pass 2^32):
+    # A[m, 0] = (m mod 7) - 3 and B[n, 0] = n + 1 with K = 1, so
+    # D[m, n] = ((m mod 7) - 3) (n + 1) exactly (page "构建 Tiled GEMM",
+    # section "GEMM": a sum of one product), on the fp16, fp16-accumulating
+    # and FP8 (E4M3, scale 1) entry points.  Checked at 4096 sampled rows and
+    # the last rows, read back from the device.
+    import torch
+    M, N, K = 2 ** 31 - 1, 2, 1
+    dev = torch.device("cuda:0")
+    r7 = (torch.arange(M, dtype=torch.int64, device=dev) % 7).to(torch.uint8)
+    if path == "fp8":
+        # E4M3 codes of -3 .. 3 (sign, 4 exponent bits with bias 7, 3 mantissa bits)
+        codes = torch.tensor([0xC4, 0xC0, 0xB8, 0x00, 0x38, 0x40, 0x44], dtype=torch.uint8,
+                             device=dev)
+        dA = codes.index_select(0, r7.int()).view(M, K)
+        dB = torch.tensor([[0x38], [0x40]], dtype=torch.uint8, device=dev)
+    else:
+        dA = (r7.to(torch.float16) - 3).view(M, K)
+        dB = torch.tensor([[1.0], [2.0]], dtype=torch.float16, device=dev)
+    del r7
+    dD = torch.full((M, N), 7.0, dtype=torch.float16, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    a, b, d = dA.data_ptr(), dB.data_ptr(), dD.data_ptr()
+    note(f"max M {M}x{N}x{K} {path}")
+    if path == "fp8":
+        rc = binding.gemm_nt_fp8(a, b, d, M, N, K, 1.0, binding.GEMM_FP8_E4M3,
+                                 binding.GEMM_FP8_E4M3, s)
+    elif path == "acc16":
+        rc = binding.gemm_nt_f16_acc16(a, b, d, M, N, K, s)
+    else:
+        rc = binding.gemm_nt_f16(a, b, d, M, N, K, s)
+    assert rc == binding.GEMM_OK
+    torch.cuda.synchronize(dev)
+    rng = np.random.default_rng(8800)
+    rows = np.concatenate([rng.integers(0, M, 4096), np.arange(M - 130, M)])
+    got = dD[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    want = ((rows % 7) - 3)[:, None] * np.array([[1.0, 2.0]])
+    assert np.array_equal(got, want), f"max M {path}: entries differ from the closed form"
+
+
 def test_permutation_lane_maps():
     # Permutation operands make any row/column mis-map of the MFMA lanes or
     # the epilogue visible bit for bit (128 x 128 x 64, one tile).

@@ -871,6 +871,22 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     // loop's epilogues, where the 256 accumulators leave no registers free.
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
     int a_k[C::A_LOADS], b_k[C::B_LOADS];
+    // Offset and first k of load q (A's loads first, then B's); only the
+    // operand's own array is indexed, since the two have their own lengths.
+    auto off_of = [&](auto qc) G18_INLINE {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q < C::A_LOADS)
+            return a_off[q];
+        else
+            return b_off[q - C::A_LOADS];
+    };
+    auto k_of = [&](auto qc) G18_INLINE {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q < C::A_LOADS)
+            return a_k[q];
+        else
+            return b_k[q - C::A_LOADS];
+    };
     auto setup_loads = [&](int ln) G18_INLINE {
         const int slot_row = ln / C::LPR;
         const int slot_byte = (ln % C::LPR) * C::LB;
@@ -908,10 +924,9 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     auto reg_load = [&](int step, auto qc, auto firstc) G18_INLINE {
         constexpr int q = decltype(qc)::value;
         constexpr bool isa = q < C::A_LOADS;
-        constexpr int i = isa ? q : q - C::A_LOADS;
         const int k0 = kb + step * BKU;
         const __amdgpu_buffer_rsrc_t rs = step < n ? (isa ? ra : rb) : rz;
-        const uint32_t off = isa ? a_off[i] : b_off[i];
+        const uint32_t off = off_of(qc);
         const uint32_t soff = (uint32_t)k0 * (uint32_t)UB;
         if constexpr (KTAIL && decltype(firstc)::value) {
             if (k0 < 0) {
@@ -919,7 +934,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
                 // first k is negative reads element by element, k < 0 as
                 // zero (such a chunk may start in the row before, or before
                 // the buffer).  Offsets wrap modulo 2^32, as soff does.
-                const int kk = k0 + (isa ? a_k[i] : b_k[i]);
+                const int kk = k0 + k_of(qc);
                 if (kk >= 0) {
                     rst[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + soff, 0, 0);
                 } else {
@@ -973,11 +988,11 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
         // S: the ring position of `step`
         char *stage = smem + (isa ? C::a_base(S % C::NSTAGE) : C::b_base(S % C::NSB));
         constexpr int i = isa ? q : q - C::A_LOADS;
-        uint32_t off = isa ? a_off[i] : b_off[i];
+        uint32_t off = off_of(qc);
         uint32_t soff = (uint32_t)k0 * 2u;
         if constexpr (KTAIL && decltype(firstc)::value) {
             if (k0 < 0) {
-                const int kk = isa ? a_k[i] : b_k[i];
+                const int kk = k_of(qc);
                 off = k0 + kk >= 0 ? off + soff : kOob;
                 soff = 0;
             }
@@ -1443,10 +1458,7 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
     const int fe = FIX && kb < 0 ? (kb & 7) : 0;       // uniform: K mod 8, or 0
     u32x4 fixv[FIX ? C::LPS : 1];
     auto fix_chunk = [&](auto qc) G18_INLINE -> bool {
-        constexpr int q = decltype(qc)::value;
-        constexpr bool isa = q < C::A_LOADS;
-        constexpr int i = isa ? q : q - C::A_LOADS;
-        const int kk = kb + (isa ? a_k[i] : b_k[i]);
+        const int kk = kb + k_of(qc);
         return kk < 0 && kk > -8;
     };
     if constexpr (FIX) {
@@ -1454,10 +1466,8 @@ gemm_nt_dma_kernel(const typename Elem<BF>::T *__restrict__ A,
             static_for<0, C::LPS>([&](auto qc) G18_INLINE {
                 constexpr int q = decltype(qc)::value;
                 constexpr bool isa = q < C::A_LOADS;
-                constexpr int i = isa ? q : q - C::A_LOADS;
                 if (fix_chunk(qc)) {
-                    const uint32_t row0 = (isa ? a_off[i] : b_off[i]) -
-                                          (uint32_t)((isa ? a_k[i] : b_k[i]) * 2);
+                    const uint32_t row0 = off_of(qc) - (uint32_t)(k_of(qc) * 2);
                     fixv[q] = __builtin_amdgcn_raw_buffer_load_b128(n > 0 ? (isa ? ra : rb) : rz,
                                                                     row0, 0, 0);
                 }
@@ -1910,13 +1920,55 @@ inline SkPlan sk_split(int64_t tiles, int64_t steps, int P)
 
 constexpr int64_t kSkMinSteps = 192;
 
+// Skinny shapes (M or N <= 64; 16-byte loads, so K % 8 == 0): the plain grid
+// runs one 64 x 32 (or 32 x 64) tile per workgroup, which leaves CUs idle
+// when there are fewer tiles than CUs, and every tile re-reads the whole
+// short operand.  Stream-K then runs on the 64 x 64 tile (half the re-reads)
+// when there are P/4 to P/2 of those tiles and either CUs idle or the K-loop
+// is long (>= 128 steps), else on the plain tile when it fills at most half
+// the CUs and every workgroup gets >= 8 K-steps.  Measured on MI355X, kernel
+// us, plain / stream-K on 64 x 32 / stream-K on 64 x 64: 64x2048x8192
+// 24.0/13.2/12.8, 64x1024x8192 26.1/13.9/16.3, 64x512x8192 25.9/16.8/25.6,
+// 64x256x16384 48.7/24.9/42.0, 64x2048x4096 14.7/11.1/12.7, 64x4096x4096
+// 15.1/12.3/10.9, 64x6144x8192 29.7/22.5/21.5, 64x8192x8192 31.4/26.2/25.2,
+// 8192x64x8192 30.9/26.3/25.5, 32x8192x4096 14.3/16.1/16.4; fewer K-steps or
+// per-workgroup steps lose to the plain grid (64x2048x2048 8.8/10.1,
+// 64x512x4096 13.9/16.4, one 64 x 64 tile at K = 8192 36/75).
+inline bool plan_skinny(Plan &pl, int64_t M, int64_t N, int64_t K, int P)
+{
+    const int64_t steps = cdiv(K, 64);
+    if (K % 8 != 0 || steps < 64)
+        return false;
+    int bm, bn;
+    tile_dims(pl.tile, bm, bn);
+    const int64_t plain = cdiv(M, bm) * cdiv(N, bn);
+    const int64_t t64 = cdiv(M, 64) * cdiv(N, 64);
+    int64_t tiles;
+    if (4 * t64 >= P && 2 * t64 <= P && (plain < P || steps >= 128)) {
+        pl.tile = Tile::kThin;
+        tiles = t64;
+    } else if (2 * plain <= P && plain * steps >= 8 * (int64_t)P) {
+        tiles = plain;
+    } else {
+        return false;
+    }
+    pl.sk = true;
+    pl.grid = P;
+    pl.split = sk_split(tiles, steps, P);
+    return true;
+}
+
 // lb: 16 (0: the register-staged path, no stream-K).
 inline Plan make_plan(int64_t M, int64_t N, int64_t K, int lb, int P)
 {
     Plan pl;
     pl.tile = choose_tile(M, N, K);
-    if (lb == 0 || M <= 64 || N <= 64 || K == 0)
+    if (lb == 0 || K == 0)
         return pl;
+    if (M <= 64 || N <= 64) {
+        plan_skinny(pl, M, N, K, P);
+        return pl;
+    }
     const int64_t steps = cdiv(K, 64);
     const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
     if (4 * tiles <= P && steps >= kSkMinSteps) {
@@ -1933,15 +1985,32 @@ constexpr int64_t kSkHdrBytes = kSkHdrWords * 4;
 
 inline int64_t workspace_bytes(const Plan &pl)
 {
-    return pl.sk ? kSkHdrBytes + flag_bytes(pl.grid) + (int64_t)pl.grid * 128 * 128 * 4 : 0;
+    if (!pl.sk)
+        return 0;
+    int bm, bn;
+    tile_dims(pl.tile, bm, bn);
+    return kSkHdrBytes + flag_bytes(pl.grid) + (int64_t)pl.grid * bm * bn * 4;
 }
 
-// The persistent stream-K grid (128 x 128 tiles, direct-to-LDS paths).
+// The persistent stream-K grid on the plan's tile (direct-to-LDS paths).
 inline void launch_sk(const void *A, const void *B, void *D, int M, int N, int K, hipStream_t s,
-                      const SkPlan &sk, int grid)
+                      const SkPlan &sk, int grid, Tile t)
 {
     const int vec = (((uintptr_t)D & 7u) == 0 && N % 4 == 0) ? 1 : 0;
-    launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+    switch (t) {
+    case Tile::kThin:
+        launch_dma<ThinDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        break;
+    case Tile::kThinN:
+        launch_dma<ThinNDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        break;
+    case Tile::kThinM:
+        launch_dma<ThinMDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        break;
+    default:
+        launch_dma<MidDma, true, false, false>(A, B, D, M, N, K, vec, s, sk, grid, Epi{});
+        break;
+    }
 }
 
 // Header, flags and slots of a stream-K plan inside workspace `ws`.

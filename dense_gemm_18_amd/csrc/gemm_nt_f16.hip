@@ -101,7 +101,7 @@ int gemm_nt_f16_ws(const void *A, const void *B, void *D, int64_t M, int64_t N, 
         return gemm_nt_f16(A, B, D, M, N, K, stream);
     SkPlan sp = pl.split;
     bind_workspace(sp, workspace, pl.grid);
-    launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
+    launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid, pl.tile);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }
 

@@ -6,8 +6,8 @@
 #include "gemm_kernels.h"
 
 // The workspace: stream-K header, flags and fp32 partial sums for a grid of
-// up to 256 workgroups (16 MiB + 1.25 KiB), one copy per GPU, held until the
-// process ends.  In host code this name is only a stand-in for the device
+// up to 256 workgroups on the largest stream-K tile, 128 x 128 (16 MiB +
+// 1.25 KiB), one copy per GPU, held until the process ends.  In host code this name is only a stand-in for the device
 // symbol, never an address: kernels get the pointer hipGetSymbolAddress
 // returns for the current device.
 static __device__ __align__(256) unsigned char
@@ -75,7 +75,7 @@ int gemm_nt_f16_ws_noalloc(const void *A, const void *B, void *D, int64_t M, int
         return GEMM_ELAUNCH;
     SkPlan sp = pl.split;
     bind_workspace(sp, ws, pl.grid);
-    launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid);
+    launch_sk(A, B, D, (int)M, (int)N, (int)K, stream, sp, pl.grid, pl.tile);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ELAUNCH;
 }
 

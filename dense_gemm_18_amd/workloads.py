@@ -54,6 +54,12 @@ WORKLOADS = {
         # few output tiles, long K: the stream-K form's case
         Workload("deep_1024x1024x16384", 1024, 1024, 16384, "uniform", "uniform",
                  (6001, 6002), (6011, 6012)),
+        # one GPU's share when 8192^3 and the skinny shape are split over
+        # B's rows (N) on eight GPUs
+        Workload("shard_8192x1024x8192", 8192, 1024, 8192, "uniform", "uniform",
+                 (7001, 7002), (7011, 7012), sample_seed=7003),
+        Workload("shard_64x2048x8192", 64, 2048, 8192, "uniform", "normal_0.02",
+                 (8001, 8002), (8011, 8012)),
     )
 }
 

@@ -217,12 +217,19 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
  * the fp32 additions differs, and it is fixed for a given shape, so repeated
  * calls are bitwise identical.
  *
- * When the problem's 128 x 128 output tiles fill at most a quarter of the
- * GPU's CUs and K spans at least 192 steps of 64 (K > 12224), a persistent
- * grid of one workgroup per CU (at most 256) splits the K-steps of the
- * tiles evenly over all workgroups; a tile split over several workgroups
- * is summed in fp32 through `workspace` and rounded to fp16 once.  Other
- * shapes run exactly as gemm_nt_f16.
+ * A persistent grid of one workgroup per CU (at most 256) splits the
+ * K-steps of the tiles evenly over all workgroups; a tile split over several
+ * workgroups is summed in fp32 through `workspace` and rounded to fp16 once.
+ * It is used (P = the GPU's CUs, K-steps of 64):
+ *   - M and N > 64: on 128 x 128 tiles when those fill at most P/4 and K
+ *     spans at least 192 steps (K > 12224);
+ *   - M or N <= 64 with K % 8 == 0 (16-byte aligned rows): on 64 x 64 tiles
+ *     when there are P/4 to P/2 of them and either the plain grid's 64 x 32
+ *     (or 32 x 64) tiles number fewer than P or K spans at least 128 steps;
+ *     else on the plain grid's tile when those fill at most P/2 and the
+ *     workgroups get at least 8 steps each; in both cases K spans at least
+ *     64 steps (K > 4032).
+ * Other shapes run exactly as gemm_nt_f16.
  *
  * workspace: device memory of at least gemm_nt_f16_ws_size(M, N, K) bytes,
  *   256-byte aligned, not overlapping A, B or D, owned by the caller.  It

@@ -18,7 +18,8 @@ from tests.gpu_util import assert_bitexact, assert_tolerance, note, run_gemm
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tile_128x128x64", "square_1024", "ragged_3000x5000x2050", "skinny_64x16384x8192"]
+SMALL = ["tile_128x128x64", "square_1024", "ragged_3000x5000x2050", "skinny_64x16384x8192",
+         "shard_64x2048x8192"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -56,9 +57,10 @@ def _headline_positions(w):
     return rows, cols, er, ec
 
 
+@pytest.mark.parametrize("name", [wl.HEADLINE, "shard_8192x1024x8192"])
 @pytest.mark.parametrize("variant", ["random", "integer"])
-def test_headline_8192_sampled(variant):
-    w = wl.WORKLOADS[wl.HEADLINE]
+def test_large_workload_sampled(name, variant):
+    w = wl.WORKLOADS[name]
     A, B = wl.random_inputs(w) if variant == "random" else wl.integer_inputs(w)
     note(f"{w.name} {variant} (sampled + tile-edge rows/cols)")
     d = run_gemm(A, B, check_canary=True)

@@ -1,8 +1,9 @@
 """GPU parity of the stream-K entry point gemm_nt_f16_ws against the oracle.
 
-Shapes are chosen so that the persistent kernel runs with 3 to 12
+Shapes are chosen so that the persistent kernel runs with 3 to 32
 contributors per tile, pieces that cross tile boundaries, a single tile
-row, and 4-byte loads with a K tail.  The
+row, rows not 16-byte aligned with a K tail, and the skinny shapes' 64 x 32,
+32 x 64 and 64 x 64 tiles.  The
 bar is the one of the plain entry point: integer inputs bit-exact, random
 inputs within 2^-10 |D_ref| + 1e-3 sqrt(K).  The summation order is fixed
 per shape, so repeated calls must agree bit for bit, and the workspace must
@@ -28,6 +29,15 @@ SHAPES = [
     (512, 640, 12351),       # odd K: rows 2-byte aligned, first-step fix-up
     (768, 1024, 12296),      # 16-byte loads and a K tail (only step 0 masked)
     (100, 8192, 32768),      # one tile row, K = 32768
+    # skinny shapes (M or N <= 64)
+    (64, 2048, 8192),        # 64 x 32 tiles, 4 contributors each
+    (2048, 64, 8192),        # 32 x 64 tiles
+    (64, 4096, 4096),        # 64 x 64 tiles
+    (8192, 64, 8192),        # 64 x 64 tiles where the plain grid fills the CUs
+    (64, 2000, 8200),        # ragged N, a K tail
+    (1, 4096, 4096),         # one row
+    (48, 3000, 4096),        # ragged M and N
+    (64, 256, 16384),        # 32 contributors per tile
 ]
 
 

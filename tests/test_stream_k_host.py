@@ -25,6 +25,14 @@ SK_SHAPES = [
     (100, 8192, 32768),      # one tile row
     (65, 300, 12288),        # one tile row of 3 tiles, ragged
     (64 * 128, 65, 12288),   # a tall single column of tiles
+    # skinny shapes: stream-K on the 64 x 32 / 32 x 64 or the 64 x 64 tile
+    (64, 2048, 8192),        # 64 tiles of 64 x 32, 4 pieces each
+    (64, 4096, 4096),        # 64 tiles of 64 x 64
+    (8192, 64, 8192),        # 128 tiles of 64 x 64 (the plain grid fills the CUs)
+    (2048, 64, 8192),        # 64 tiles of 32 x 64
+    (64, 2000, 8200),        # ragged N, a K tail
+    (1, 4096, 4096),         # one row
+    (64, 256, 16384),        # 8 tiles, 32 pieces each
 ]
 
 
@@ -88,14 +96,24 @@ def test_schedule_covers_each_step_once(M, N, K):
     (900, 1000, 12290, 128, 64),     # K % 8 != 0: the same 16-byte loads
     (64, 16384, 8192, 64, 0),        # thin tiles never split
     (1024, 1024, 16383, 128, 64),    # odd K as well
+    (64, 2048, 8192, 64, 64),        # skinny: 64 x 32 tiles fill a quarter of the CUs
+    (2048, 64, 8192, 32, 64),        # the same on 32 x 64 tiles
+    (64, 256, 16384, 64, 8),         # 8 tiles, 256 K-steps
+    (64, 4096, 4096, 64, 64),        # 64 tiles of 64 x 64
+    (64, 8192, 8192, 64, 128),       # 64 x 64 tiles: half the re-reads of A
+    (64, 8192, 4096, 64, 0),         # 64 K-steps and the plain grid fills the CUs
+    (64, 512, 4096, 64, 0),          # 4 K-steps per workgroup: too few
+    (64, 2048, 2048, 64, 0),         # 32 K-steps
+    (64, 64, 8192, 64, 0),           # one tile
+    (64, 2048, 8196, 64, 0),         # K % 8 != 0: skinny rows only on 16-byte loads
 ])
 def test_plan_choice(M, N, K, bm, sk):
     got = binding.gemm_nt_f16_ws_tile(M, N, K)
     assert (got[0], got[3]) == (bm, sk)
     need = binding.gemm_nt_f16_ws_size(M, N, K)
     if sk:
-        # a 256-byte header, 256 flag words, 256 fp32 128x128 slots
-        assert need == 256 + 1024 + 256 * 128 * 128 * 4
+        # a 256-byte header, 256 flag words, 256 fp32 slots of one tile
+        assert need == 256 + 1024 + 256 * got[0] * got[1] * 4
     else:
         assert need == 0 and binding.gemm_nt_f16_ws_items(M, N, K, 0) == []
 

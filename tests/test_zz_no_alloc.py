@@ -61,6 +61,18 @@ def test_noalloc_integer_against_oracle_two_calls():
         assert_bitexact(got, run_gemm_ws(A, B), f"noalloc vs workspace integer {M}x{N}x{K}")
 
 
+def test_noalloc_skinny_plans_two_calls():
+    # skinny stream-K plans on 64 x 64 and 64 x 32 tiles (smaller slots in
+    # the same static array), the second call smaller than the first
+    for i, (M, N, K) in enumerate([(8192, 64, 8192), (64, 2048, 4096)]):
+        assert binding.gemm_nt_f16_ws_tile(M, N, K)[3] > 0, "shape must take stream-K"
+        A, B = wl.integer_free(17300 + i, M, N, K)
+        note(f"noalloc skinny call {i}: {M}x{N}x{K}")
+        got = _run_noalloc(A, B)
+        assert_bitexact(got, run_gemm_ws(A, B), f"noalloc vs workspace {M}x{N}x{K}")
+        assert_bitexact(got, oracle.gemm_nt_f16(A, B), f"noalloc skinny integer {M}x{N}x{K}")
+
+
 def test_noalloc_plain_shape_falls_through():
     M, N, K = 300, 200, 96           # not a stream-K plan: runs as gemm_nt_f16
     assert binding.gemm_nt_f16_ws_tile(M, N, K)[3] == 0

@@ -94,7 +94,7 @@ def test_tile_introspection():
     (3000, 5000, 2050, 256),    # the same with 4-byte loads
     (3072, 3072, 3072, 256),    # 144 big tiles (1 wave) vs 576 mid tiles (3 waves)
     (2048, 2048, 8192, 128),    # 64 big tiles would leave 3/4 of the CUs idle
-    (2560, 2560, 4096, 128),    # 100 big tiles vs 400 mid tiles (2 waves)
+    (2560, 2560, 4096, 256),    # 200 tiles of 256 x 128 (1 wave) vs 400 mid tiles (2 waves)
     (2048, 2048, 8194, 128),
     (1024, 1024, 1024, 64),     # 256 thin tiles (1 wave) beat 64 mid tiles
     (2048, 1024, 1024, 128),    # 128 mid tiles (1 wave) beat 512 thin tiles (2 waves)
@@ -109,6 +109,24 @@ def test_tile_introspection():
 def test_tile_choice(M, N, K, bm):
     # The choice minimises (waves of workgroups on 256 CUs) x (tile time).
     assert binding.gemm_nt_f16_tile(M, N, K)[0] == bm
+
+
+@pytest.mark.parametrize("M,N,K,tile", [
+    (2560, 2560, 4096, (256, 128)),   # 200 tiles of 256 x 128 vs 400 of 128 x 128
+    (8192, 1024, 8192, (256, 128)),   # 256 tiles: one per CU
+    (1024, 8192, 8192, (256, 128)),
+    (2048, 4096, 256, (256, 128)),
+    (1536, 6144, 4096, (256, 256)),   # 144 big tiles: one wave
+    (2048, 2048, 8192, (128, 128)),   # 256 mid tiles: one wave
+    (4300, 4400, 200, (128, 128)),    # 1190 mid tiles (5 waves) vs 595 (3 waves)
+    (2560, 2560, 7, (128, 128)),      # K < 8: register staging, the 128 x 128 kernel
+])
+def test_rect_tile_choice(M, N, K, tile):
+    # The 256 x 128 tile takes the shapes whose 128 x 128 tiles fill the CUs
+    # twice; the introspection of the kernel agrees with the tile.
+    assert binding.gemm_nt_f16_tile(M, N, K)[:2] == tile
+    assert binding.gemm_nt_f16_kernel(1 << 20, 2 << 20, 3 << 20, M, N, K)[:2] == tile
+    assert binding.gemm_nt_f16_ws_tile(M, N, K)[:2] == tile
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (1, 7), (7, 1), (3, 5), (8, 8), (32, 32),

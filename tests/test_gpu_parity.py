@@ -357,8 +357,27 @@ def test_big_tile_b_rings(M, N, K):
     assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")
 
 
-@pytest.mark.parametrize("M,N,K", [(2100, 2200, 200), (2100, 2200, 136), (2048, 4096, 256),
-                                   (1300, 4100, 72)])
+@pytest.mark.parametrize("M,N,K,a_off", [(2100, 2200, 200, 0), (2100, 2200, 136, 0),
+                                         (2048, 4096, 256, 0), (1300, 4100, 72, 0),
+                                         (3000, 2000, 333, 0), (3000, 2000, 520, 1)])
+def test_rect_tiles(M, N, K, a_off):
+    # 256 x 128 tiles (three 48 KB stages, refills split over two slices):
+    # K tails, odd K (the first-step fix-up with A and B loads of different
+    # counts), A offset by one element, staged and direct stores; integer
+    # inputs bit-exact, random inputs in tolerance
+    bm, bn, lb, _ = binding.gemm_nt_f16_kernel((1 << 20) + 2 * a_off, 2 << 20, 3 << 20, M, N, K)
+    assert (bm, bn, lb) == (256, 128, 16)
+    A, B = wl.integer_free(7800 + M + K, M, N, K)
+    ref = oracle.gemm_nt_f16(A, B)
+    note(f"256x128 {M}x{N}x{K} a+{a_off}")
+    assert_bitexact(run_gemm(A, B, a_off=a_off), ref, f"{M}x{N}x{K}")
+    assert_bitexact(run_gemm(A, B, a_off=a_off, d_off=4), ref, f"{M}x{N}x{K} direct stores")
+    Ar, Br = wl.uniform_inputs(7850 + K, M, N, K)
+    assert_tolerance(run_gemm(Ar, Br, a_off=a_off), oracle.gemm_nt_f16(Ar, Br), K,
+                     f"{M}x{N}x{K} random")
+
+
+@pytest.mark.parametrize("M,N,K", [(4300, 4400, 200), (4352, 4352, 136), (4300, 4400, 72)])
 def test_mid_two_stage_tiles(M, N, K):
     # more 128 x 128 tiles than CUs: the two-stage 128 x 128 kernel (two
     # workgroups per CU); K tails, staged and direct stores, integer inputs

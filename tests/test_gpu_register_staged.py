@@ -44,14 +44,15 @@ def _kernel(M, N, K, a_off=0, b_off=0, d_off=0):
 # (M, N, K, a_off, b_off, tile, load): rows not 16-byte aligned on the
 # direct loads (odd K, K % 8 != 0, 2- or 4-byte aligned operands; K = 8 and
 # 9, the shortest rows that take them) on the 256 x 256 (both B rings),
-# 128 x 128 (four and two stages) and 64 x 64 tiles, then the register-
+# 256 x 128, 128 x 128 (four and two stages) and 64 x 64 tiles, then the register-
 # staged kernels: K < 8 on every tile and skinny shapes
 CASES = [(2900, 4100, 97, 0, 0, 256, 16), (3000, 5000, 2049, 0, 0, 256, 16),
          (2900, 4100, 64, 1, 0, 256, 16), (2900, 4100, 64, 0, 1, 256, 16),
          (2900, 4100, 2050, 0, 0, 256, 16), (2900, 4100, 2054, 2, 0, 256, 16),
          (2900, 4100, 9, 0, 0, 256, 16), (1100, 1100, 99, 0, 0, 128, 16),
          (1100, 1100, 64, 1, 3, 128, 16), (1000, 1100, 9, 0, 0, 128, 16),
-         (1000, 1100, 8, 1, 0, 128, 16), (2100, 2200, 201, 0, 0, 128, 16),
+         (1000, 1100, 8, 1, 0, 128, 16), (2100, 2200, 201, 0, 0, 256, 16),
+         (4300, 4400, 201, 0, 0, 128, 16),
          (300, 200, 130, 0, 0, 64, 16), (700, 900, 202, 0, 0, 64, 16),
          (2900, 4100, 7, 0, 0, 256, 1), (1100, 1100, 5, 0, 0, 128, 1),
          (300, 200, 3, 0, 0, 64, 1), (64, 300, 37, 0, 0, 64, 1), (300, 64, 64, 0, 1, 64, 1),

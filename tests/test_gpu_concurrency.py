@@ -5,13 +5,13 @@ them have finished, each output must equal, bit for bit, the same call made
 alone, and that in turn equals the oracle (integer inputs, so the fp32 sums
 are exact and both sides round the same value once).
 
-The cases cover the 256 x 256, 128 x 128 and 64 x 64 direct-to-LDS tiles,
+The cases cover the 256 x 256, 256 x 128, 128 x 128 and 64 x 64 direct-to-LDS tiles,
 rows that are not 16-byte aligned on the direct loads and on the register-
 staged ones, the fp16-accumulating and FP8 entry points, and
-the stream-K form.  The stream-K calls overlap the others but never each
-other: they share one workspace, and each grid expects to get every CU once
-the kernels around it finish, so all of them go on one stream, as the
-header asks.
+the stream-K form (128 x 128 and skinny 64 x 32 plans).  The stream-K
+calls overlap the others but never each other: each grid expects to get
+every CU once the kernels around it finish, so all of them go on one
+stream, as the header asks.
 """
 from __future__ import annotations
 
@@ -96,7 +96,9 @@ def cases():
             Case("register-staged", 64, 3000, 201, 24008, "reg"),
             Case("fp16 accumulation", 1000, 1100, 320, 24005, "acc16"),
             Case("fp8", 1000, 1100, 1024, 24006, "fp8"),
-            Case("stream-K", 512, 640, 12352, 24007, "ws")]
+            Case("stream-K", 512, 640, 12352, 24007, "ws"),
+            Case("256x128 tile", 2100, 2200, 200, 24009),
+            Case("skinny stream-K", 64, 2048, 8192, 24010, "ws")]
 
 
 def test_calls_on_overlapping_streams(cases):
@@ -120,27 +122,31 @@ def test_calls_on_overlapping_streams(cases):
 
 
 def test_calls_from_threads(cases):
+    # one host thread per case, except that the stream-K cases share one
+    # thread (and its stream), as they share the GPU's CUs
     import torch
     for c in cases:
         c.reset()
     torch.cuda.synchronize()
+    groups = [[c] for c in cases if c.kind != "ws"] + [[c for c in cases if c.kind == "ws"]]
     errors = []
-    start = threading.Barrier(len(cases))
+    start = threading.Barrier(len(groups))
 
-    def worker(c):
+    def worker(group):
         try:
             s = torch.cuda.Stream()
             start.wait()
             for r in range(ROUNDS):
-                rc = c.call(r, s.cuda_stream)
-                if rc != binding.GEMM_OK:
-                    errors.append(f"{c.name}: rc {rc}")
+                for c in group:
+                    rc = c.call(r, s.cuda_stream)
+                    if rc != binding.GEMM_OK:
+                        errors.append(f"{c.name}: rc {rc}")
             s.synchronize()
         except Exception as e:           # reported below, on the main thread
-            errors.append(f"{c.name}: {e!r}")
+            errors.append(f"{group[0].name}: {e!r}")
 
-    note(f"concurrency: {len(cases)} host threads, {ROUNDS} calls each")
-    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    note(f"concurrency: {len(groups)} host threads, {ROUNDS} rounds each")
+    threads = [threading.Thread(target=worker, args=(g,)) for g in groups]
     for t in threads:
         t.start()
     for t in threads:

@@ -246,7 +246,9 @@ int gemm_nt_f16_ex(const void *A, const void *B, const void *C, const void *bias
  *   as gemm_nt_f16 (workspace unused; it may then be NULL with ws_bytes 0).
  *
  * All workgroups of the grid must be resident at once: the call expects the
- * GPU's CUs not to be held by other long-running work.  A workgroup that
+ * GPU's CUs not to be held by other long-running work, which includes
+ * another stream-K call (of this entry point or gemm_nt_f16_ws_noalloc),
+ * even with its own workspace: order stream-K calls on one stream.  A workgroup that
  * waits more than ~5 s for another writes its tile as NaN (0x7E00), sets the
  * header's error word and ends, so the kernel always terminates; the
  * workspace stays valid for later calls.

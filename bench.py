@@ -95,11 +95,9 @@ def recorded_traffic(path: str, workload: str):
     return float(b.group(1))
 
 
-def cpu_baseline(rows_fn, M, N, K, budget_s: float = 12.0) -> dict:
-    """The oracle (untuned) on whole rows of D until ~budget_s of CPU work;
-    rows_fn(r0, r1, threads) computes rows r0 .. r1-1."""
-    import oracle
-    threads = oracle.threads_available()
+def _oracle_rows(rows_fn, M, N, K, threads: int, budget_s: float):
+    """Whole rows of D through the oracle until all M rows or ~budget_s;
+    returns (rows, seconds)."""
     chunk = 64
     rows = 0
     t0 = time.perf_counter()
@@ -107,8 +105,18 @@ def cpu_baseline(rows_fn, M, N, K, budget_s: float = 12.0) -> dict:
         r1 = min(M, rows + chunk)
         rows_fn(rows, r1, threads)
         rows = r1
-    dt = time.perf_counter() - t0
-    return {
+    return rows, time.perf_counter() - t0
+
+
+def cpu_baseline(rows_fn, M, N, K, budget_s: float = 12.0, single_thread: bool = False) -> dict:
+    """The oracle (untuned) on whole rows of D until ~budget_s of CPU work;
+    rows_fn(r0, r1, threads) computes rows r0 .. r1-1.  single_thread: also
+    time it on one thread (the small workloads, whose whole D a single core
+    computes within the budget)."""
+    import oracle
+    threads = oracle.threads_available()
+    rows, dt = _oracle_rows(rows_fn, M, N, K, threads, budget_s)
+    out = {
         "value": tflops(rows, N, K, dt),
         "unit": "TFLOPS",
         "cores": threads,
@@ -116,6 +124,15 @@ def cpu_baseline(rows_fn, M, N, K, budget_s: float = 12.0) -> dict:
         "sample": f"{rows} full rows of D ({rows}x{N}x{K}, {rows * N * K:.3e} MACs) in {dt:.1f} s",
         "host": host_cpu(),
     }
+    if single_thread:
+        rows1, dt1 = _oracle_rows(rows_fn, M, N, K, 1, budget_s)
+        out["single_thread"] = {
+            "value": tflops(rows1, N, K, dt1),
+            "unit": "TFLOPS",
+            "cores": 1,
+            "sample": f"{rows1} full rows of D ({rows1 * N * K:.3e} MACs) in {dt1:.2f} s",
+        }
+    return out
 
 
 def host_cpu() -> dict:
@@ -650,7 +667,8 @@ def run(args, sampler) -> int:
         # GPU work; amd-smi reports each sample averaged over its interval
         out["clock"] = sampler.report(t_load + 1.0, t_unload + 1.0, peak, value)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(P["cpu_rows"], M, N, K)
+        out["cpu_baseline"] = cpu_baseline(P["cpu_rows"], M, N, K,
+                                           single_thread=M * N * K <= 1024 ** 3)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -55,3 +55,17 @@ def test_recorded_traffic_is_plausible(path, workload, M, N, K, elem):
     assert "rocprofv3 --pmc FETCH_SIZE" in summary.read_text()
     if t is not None:
         assert t >= 0.95 * bench.algorithmic_bytes(M, N, K, elem=elem)
+
+
+def test_cpu_baseline_single_thread_leg():
+    # the oracle leg on a small workload: all threads, then one thread, each
+    # over the whole D (the small workloads' oracle timing)
+    import oracle
+    from dense_gemm_18_amd import workloads as wl
+    w = wl.WORKLOADS["tile_128x128x64"]
+    A, B = wl.random_inputs(w)
+    r = bench.cpu_baseline(lambda r0, r1, t: oracle.gemm_nt_f16(A[r0:r1], B, threads=t),
+                           w.M, w.N, w.K, budget_s=5.0, single_thread=True)
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    st = r["single_thread"]
+    assert st["cores"] == 1 and st["value"] > 0 and st["sample"].startswith("128 full rows")

@@ -54,7 +54,8 @@ def _check_graph(call, out):
     del g
 
 
-@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (2900, 4100, 97), (64, 3000, 448)])
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (2900, 4100, 97), (64, 3000, 448),
+                                   (2100, 2200, 200)])
 def test_graph_plain(M, N, K):
     import torch
     A, B = wl.uniform_inputs(21000 + K, M, N, K)
@@ -105,11 +106,12 @@ def test_graph_fp8_and_epilogue():
                                                   -1.0, s), dD)
 
 
-def test_graph_stream_k():
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 12288), (64, 2048, 8192)])
+def test_graph_stream_k(M, N, K):
     # the workspace's epochs carry over from call to call and from replay to
-    # replay; its header must show no timeout afterwards
+    # replay; its header must show no timeout afterwards (128 x 128 and
+    # skinny 64 x 32 plans)
     import torch
-    M, N, K = 1024, 1024, 12288
     A, B = wl.uniform_inputs(21800, M, N, K)
     dA, dB = _dev(A), _dev(B)
     dD = torch.empty((M, N), dtype=torch.float16, device="cuda:0")

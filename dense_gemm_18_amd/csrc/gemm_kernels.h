@@ -1715,8 +1715,13 @@ inline Tile choose_tile(int64_t M, int64_t N, int64_t K, bool thin_ok = true)
     if (!thin_ok)
         return big <= mid ? Tile::kBig : Tile::kMid;
     // the 256 x 128 tile only on direct loads (register staging would run
-    // the 128 x 128 kernel)
-    const double rect = wide ? cdiv(cdiv(M, 256) * cdiv(N, 128), kCUs) * rect_tile : 1e30;
+    // the 128 x 128 kernel) and with K >= 1024: below that, two 128 x 128
+    // workgroups per CU hide each other's prologue and epilogue (TFLOP/s,
+    // 256 x 128 / two-stage 128 x 128: 4096x2048x256 447/484, x512 729/744,
+    // 8192x1024x1024 1012/978, 2560^2x2048 1019/969, 2560^2x2050 792/671)
+    const double rect = wide && K >= 1024
+                            ? cdiv(cdiv(M, 256) * cdiv(N, 128), kCUs) * rect_tile
+                            : 1e30;
     if (big <= mid && big <= thin && big <= rect)
         return Tile::kBig;
     if (rect < mid && rect <= thin)

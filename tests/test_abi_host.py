@@ -115,7 +115,8 @@ def test_tile_choice(M, N, K, bm):
     (2560, 2560, 4096, (256, 128)),   # 200 tiles of 256 x 128 vs 400 of 128 x 128
     (8192, 1024, 8192, (256, 128)),   # 256 tiles: one per CU
     (1024, 8192, 8192, (256, 128)),
-    (2048, 4096, 256, (256, 128)),
+    (2048, 4096, 1024, (256, 128)),
+    (2048, 4096, 512, (128, 128)),    # K < 1024: two 128 x 128 workgroups per CU
     (1536, 6144, 4096, (256, 256)),   # 144 big tiles: one wave
     (2048, 2048, 8192, (128, 128)),   # 256 mid tiles: one wave
     (4300, 4400, 200, (128, 128)),    # 1190 mid tiles (5 waves) vs 595 (3 waves)

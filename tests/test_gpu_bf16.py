@@ -21,7 +21,7 @@ from tests.gpu_util import note, run_gemm_bf16
 pytestmark = pytest.mark.gpu
 
 # 256x256 (both B rings), 128x128, 64x64, rows not 16-byte aligned (K = 130, 37)
-SHAPES = [(2900, 4100, 136), (2900, 4100, 512), (1100, 1100, 96), (64, 300, 128), (300, 200, 130), (150, 97, 37),
+SHAPES = [(2900, 4100, 136), (2900, 4100, 512), (2100, 2200, 1032), (1100, 1100, 96), (64, 300, 128), (300, 200, 130), (150, 97, 37),
           (1024, 1024, 1024), (64, 3000, 136), (3000, 40, 200), (2100, 2200, 200)]
 
 

@@ -97,7 +97,7 @@ def cases():
             Case("fp16 accumulation", 1000, 1100, 320, 24005, "acc16"),
             Case("fp8", 1000, 1100, 1024, 24006, "fp8"),
             Case("stream-K", 512, 640, 12352, 24007, "ws"),
-            Case("256x128 tile", 2100, 2200, 200, 24009),
+            Case("256x128 tile", 2100, 2200, 1032, 24009),
             Case("skinny stream-K", 64, 2048, 8192, 24010, "ws")]
 
 

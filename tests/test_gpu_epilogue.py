@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 # (M, N, K, tile the plain path picks): 256x256 16-byte loads, 128x128,
 # 64x64 (thin), rows not 16-byte aligned (K = 130, 37, 98)
-SHAPES = [(2900, 4100, 136), (2900, 4100, 512), (1100, 1100, 96), (64, 300, 128), (300, 200, 130), (150, 97, 37),
+SHAPES = [(2900, 4100, 136), (2900, 4100, 512), (2100, 2200, 1032), (1100, 1100, 96), (64, 300, 128), (300, 200, 130), (150, 97, 37),
           (3000, 4999, 98), (64, 3000, 136), (3000, 40, 200), (2100, 2200, 200)]
 SCALARS = [(2.0, -1.0), (-0.5, 3.0), (1.0, 0.25)]
 

@@ -357,9 +357,9 @@ def test_big_tile_b_rings(M, N, K):
     assert_tolerance(run_gemm(Ar, Br), oracle.gemm_nt_f16(Ar, Br), K, f"{M}x{N}x{K} random")
 
 
-@pytest.mark.parametrize("M,N,K,a_off", [(2100, 2200, 200, 0), (2100, 2200, 136, 0),
-                                         (2048, 4096, 256, 0), (1300, 4100, 72, 0),
-                                         (3000, 2000, 333, 0), (3000, 2000, 520, 1)])
+@pytest.mark.parametrize("M,N,K,a_off", [(2100, 2200, 1032, 0), (2100, 2200, 1024, 0),
+                                         (2048, 4096, 1024, 0), (1300, 4100, 1096, 0),
+                                         (3000, 2000, 1025, 0), (3000, 2000, 1088, 1)])
 def test_rect_tiles(M, N, K, a_off):
     # 256 x 128 tiles (three 48 KB stages, refills split over two slices):
     # K tails, odd K (the first-step fix-up with A and B loads of different

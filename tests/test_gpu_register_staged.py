@@ -51,7 +51,7 @@ CASES = [(2900, 4100, 97, 0, 0, 256, 16), (3000, 5000, 2049, 0, 0, 256, 16),
          (2900, 4100, 2050, 0, 0, 256, 16), (2900, 4100, 2054, 2, 0, 256, 16),
          (2900, 4100, 9, 0, 0, 256, 16), (1100, 1100, 99, 0, 0, 128, 16),
          (1100, 1100, 64, 1, 3, 128, 16), (1000, 1100, 9, 0, 0, 128, 16),
-         (1000, 1100, 8, 1, 0, 128, 16), (2100, 2200, 201, 0, 0, 256, 16),
+         (1000, 1100, 8, 1, 0, 128, 16), (2100, 2200, 1033, 0, 0, 256, 16),
          (4300, 4400, 201, 0, 0, 128, 16),
          (300, 200, 130, 0, 0, 64, 16), (700, 900, 202, 0, 0, 64, 16),
          (2900, 4100, 7, 0, 0, 256, 1), (1100, 1100, 5, 0, 0, 128, 1),

@@ -194,6 +194,46 @@ def test_max_m(path):
     assert np.array_equal(got, want), f"max M {path}: entries differ from the closed form"
 
 
+@pytest.mark.parametrize("path", ["f16", "fp8"])
+def test_max_n(path):
+    # N = 2^31 - 1 columns (2^25 tiles of 64 x 64 on a two-dimensional grid;
+    # B 4 GB, and a row of D spans 4 GiB): A = [[1], [2]] and
+    # B[n, 0] = (n mod 7) - 3 with K = 1, so D[m, n] = (m + 1) ((n mod 7) - 3)
+    # exactly (page "构建 Tiled GEMM", section "GEMM": a sum of one product),
+    # on the fp16 and FP8 (E4M3, scale 1) entry points; 4096 sampled columns
+    # and the last ones, read back from the device.
+    import torch
+    M, N, K = 2, 2 ** 31 - 1, 1
+    dev = torch.device("cuda:0")
+    r7 = (torch.arange(N, dtype=torch.int64, device=dev) % 7).to(torch.uint8)
+    if path == "fp8":
+        # E4M3 codes of -3 .. 3, and of 1 and 2
+        codes = torch.tensor([0xC4, 0xC0, 0xB8, 0x00, 0x38, 0x40, 0x44], dtype=torch.uint8,
+                             device=dev)
+        dB = codes.index_select(0, r7.int()).view(N, K)
+        dA = torch.tensor([[0x38], [0x40]], dtype=torch.uint8, device=dev)
+    else:
+        dB = (r7.to(torch.float16) - 3).view(N, K)
+        dA = torch.tensor([[1.0], [2.0]], dtype=torch.float16, device=dev)
+    del r7
+    dD = torch.full((M, N), 7.0, dtype=torch.float16, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    a, b, d = dA.data_ptr(), dB.data_ptr(), dD.data_ptr()
+    note(f"max N {M}x{N}x{K} {path}")
+    if path == "fp8":
+        rc = binding.gemm_nt_fp8(a, b, d, M, N, K, 1.0, binding.GEMM_FP8_E4M3,
+                                 binding.GEMM_FP8_E4M3, s)
+    else:
+        rc = binding.gemm_nt_f16(a, b, d, M, N, K, s)
+    assert rc == binding.GEMM_OK
+    torch.cuda.synchronize(dev)
+    rng = np.random.default_rng(8900)
+    cols = np.concatenate([rng.integers(0, N, 4096), np.arange(N - 130, N)])
+    got = dD[:, torch.from_numpy(cols).to(dev)].float().cpu().numpy()
+    want = np.array([[1.0], [2.0]]) * ((cols % 7) - 3)[None, :]
+    assert np.array_equal(got, want), f"max N {path}: entries differ from the closed form"
+
+
 def test_permutation_lane_maps():
     # Permutation operands make any row/column mis-map of the MFMA lanes or
     # the epilogue visible bit for bit (128 x 128 x 64, one tile).

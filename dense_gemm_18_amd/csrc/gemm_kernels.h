@@ -13,7 +13,10 @@
 // alpha/beta/bias epilogue.  The kernel design is gfx950's own; what it keeps
 // from the pages is listed next to each part.
 //
-// One workgroup computes one BM x BN output tile:
+// One workgroup computes one BM x BN output tile (256 x 256, 256 x 128,
+// 128 x 128, 64 x 64, 64 x 32 or 32 x 64, by choose_tile); the stream-K form
+// instead runs one workgroup per CU over K-step ranges of tile-starved
+// shapes and sums split tiles through a workspace (make_plan, sk_next):
 //   * Tile -> workgroup map: an XCD-aware remap (consecutive workgroup ids
 //     land on different XCDs, each with its own L2) followed by grouped
 //     rasterisation, so tiles that share A rows or B rows run on one XCD.

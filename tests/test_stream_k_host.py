@@ -40,7 +40,26 @@ def _steps(K):
     return -(-K // 64)
 
 
-@pytest.mark.parametrize("M,N,K", SK_SHAPES)
+def _random_planned_shapes(count=40, seed=4242):
+    """Seeded shapes (skinny and not) that take a stream-K plan."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        if rng.random() < 0.6:                  # skinny: M or N <= 64
+            short = int(rng.integers(1, 65))
+            long_ = int(rng.integers(65, 12000))
+            M, N = (short, long_) if rng.random() < 0.5 else (long_, short)
+            K = 8 * int(rng.integers(512, 4096))
+        else:
+            M, N = int(rng.integers(65, 1500)), int(rng.integers(65, 1500))
+            K = int(rng.integers(12225, 40000))
+        if binding.gemm_nt_f16_ws_tile(M, N, K)[3] > 0:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", SK_SHAPES + _random_planned_shapes())
 def test_schedule_covers_each_step_once(M, N, K):
     bm, bn, grid, sk_tiles = binding.gemm_nt_f16_ws_tile(M, N, K)
     assert sk_tiles > 0 and 0 < grid <= 256
